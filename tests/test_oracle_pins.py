@@ -1,0 +1,344 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties an oracle function to something other than itself: a library
+routine (torch's fp8 / e8m0 / bf16 casts, numpy float64 matmul), a closed
+form, an exact-arithmetic case where every summation order gives the same
+answer, or an error bound.  A mistake anywhere in the oracle -- a dropped
+scale, a transposed operand, a wrong scale index, a wrong rounding -- fails
+at least one of them; ``test_oracle_mutants.py`` checks that claim.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from dense_matmul_amd import inputs
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+# ------------------------------------------------------------ helpers
+def t_dec_e4m3(q):
+    """Library decode: torch's float8_e4m3fn -> float32."""
+    return torch.from_numpy(np.ascontiguousarray(q, np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+
+
+def t_enc_e4m3(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def t_bf16(x):
+    """Library round: torch's float32 -> bfloat16, returned as bit patterns."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def t_dec_e8m0(b):
+    return torch.from_numpy(np.ascontiguousarray(b, np.uint8)).view(torch.float8_e8m0fnu).float().numpy()
+
+
+def bf16_to_f64(h):
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def exact_codes(shape, seed, orc):
+    """Codes of values {0, +-0.5, +-1, +-2}: every product and partial sum of
+    a K <= 8192 dot product is then exact in fp32."""
+    vals = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0], np.float32)
+    return inputs.choice(shape, orc.enc_e4m3(vals), seed)
+
+
+POW2 = np.array([0.25, 0.5, 1.0, 2.0, 4.0], np.float32)
+
+
+def full_scales(mode, sa, sb, M, N, K):
+    """Per-element scale arrays [M,K] and [N,K] laid out by mode (numpy)."""
+    if mode == "ptpc":
+        return np.repeat(sa[:, None], K, 1).astype(np.float64), np.repeat(sb[:, None], K, 1).astype(np.float64)
+    if mode == "blockscale":
+        fa = np.repeat(sa, 128, axis=0).T  # [K/128, M] -> [K, M] -> [M, K]
+        fb = np.repeat(np.repeat(sb, 128, axis=0)[:N], 128, axis=1)  # [N, K]
+        return fa.astype(np.float64), fb.astype(np.float64)
+    fa = np.repeat(t_dec_e8m0(sa), 32, axis=0).T
+    fb = np.repeat(t_dec_e8m0(sb), 32, axis=0).T
+    return fa.astype(np.float64), fb.astype(np.float64)
+
+
+def run_gemm(orc, mode, qa, qb, sa, sb, **kw):
+    return {"ptpc": orc.gemm_ptpc, "blockscale": orc.gemm_blockscale, "mxfp8": orc.gemm_mxfp8}[mode](qa, qb, sa, sb, **kw)
+
+
+def random_scales(mode, M, N, K, seed, exact):
+    rng = np.random.default_rng(seed)
+    if mode == "mxfp8":
+        lo, hi = (125, 130) if exact else (115, 135)
+        return (rng.integers(lo, hi, size=(K // 32, M)).astype(np.uint8),
+                rng.integers(lo, hi, size=(K // 32, N)).astype(np.uint8))
+    shp = {"ptpc": ((M,), (N,)), "blockscale": ((K // 128, M), ((N + 127) // 128, K // 128))}[mode]
+    if exact:
+        return inputs.choice(shp[0], POW2, seed), inputs.choice(shp[1], POW2, seed + 1)
+    return (rng.uniform(0.001, 0.02, size=shp[0]).astype(np.float32),
+            rng.uniform(0.001, 0.02, size=shp[1]).astype(np.float32))
+
+
+# ------------------------------------------------------------- codecs
+def test_dec_e4m3_matches_torch_on_all_codes(orc):
+    q = np.arange(256, dtype=np.uint8)
+    d, t = orc.dec_e4m3(q), t_dec_e4m3(q)
+    nan = np.isnan(t)
+    assert nan.sum() == 2 and set(q[nan]) == {0x7F, 0xFF}
+    assert np.isnan(d[nan]).all()
+    assert np.array_equal(d[~nan].view(np.uint32), t[~nan].view(np.uint32))  # incl. -0.0
+
+
+def test_dec_e4m3_ocp_closed_forms(orc):
+    # OCP FP8 E4M3: max normal S.1111.110 = 448, min normal 2^-6, max
+    # subnormal 7 * 2^-9, min subnormal 2^-9, 1.0 = 0.0111.000
+    got = orc.dec_e4m3(np.array([0x7E, 0xFE, 0x08, 0x07, 0x01, 0x38, 0x00, 0x80], np.uint8))
+    want = [448.0, -448.0, 2.0**-6, 7 * 2.0**-9, 2.0**-9, 1.0, 0.0, -0.0]
+    assert got.tolist() == want
+
+
+def test_enc_e4m3_round_trips_every_finite_code(orc):
+    q = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(orc.enc_e4m3(orc.dec_e4m3(q)), q)
+
+
+def test_enc_e4m3_ties_go_to_even(orc):
+    q = np.arange(0, 0x7E, dtype=np.uint8)  # adjacent positive pairs (q, q+1)
+    lo, hi = orc.dec_e4m3(q).astype(np.float64), orc.dec_e4m3(q + 1).astype(np.float64)
+    mid = ((lo + hi) / 2).astype(np.float32)
+    assert np.array_equal(mid.astype(np.float64), (lo + hi) / 2)  # midpoints exact in fp32
+    want = np.where(q % 2 == 0, q, q + 1).astype(np.uint8)
+    assert np.array_equal(orc.enc_e4m3(mid), want)
+    assert np.array_equal(orc.enc_e4m3(-mid), want | 0x80)
+    # just off the midpoint goes to the nearer neighbour
+    assert np.array_equal(orc.enc_e4m3(np.nextafter(mid, np.float32(0))), q)
+    assert np.array_equal(orc.enc_e4m3(np.nextafter(mid, np.float32(1e9))), q + 1)
+
+
+def test_enc_e4m3_matches_torch_in_range(orc):
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.uniform(-448, 448, 200000), rng.normal(0, 1, 100000),
+                        rng.uniform(-2.0**-5, 2.0**-5, 100000)]).astype(np.float32)
+    assert np.array_equal(orc.enc_e4m3(x), t_enc_e4m3(x))
+
+
+def test_enc_e4m3_saturates_and_maps_nan(orc):
+    x = np.array([448.0, 449.0, 463.9, 464.0, 500.0, 1e30, np.inf, -449.0, -np.inf, np.nan], np.float32)
+    assert orc.enc_e4m3(x).tolist() == [0x7E] * 7 + [0xFE, 0xFE, 0x7F]
+
+
+def test_dec_e8m0_matches_torch(orc):
+    b = np.arange(256, dtype=np.uint8)
+    d, t = orc.dec_e8m0(b), t_dec_e8m0(b)
+    assert np.isnan(d[255]) and np.isnan(t[255])
+    assert np.array_equal(d[:255], t[:255])
+    assert d[127] == 1.0 and d[128] == 2.0 and d[126] == 0.5
+
+
+def test_bf16_rne_matches_torch(orc):
+    rng = np.random.default_rng(3)
+    u = rng.integers(0, 2**32, size=500000, dtype=np.uint64).astype(np.uint32)
+    u[:1000] = (u[:1000] & 0xFFFF0000) | 0x8000  # exact ties
+    x = u.view(np.float32)
+    x = x[np.isfinite(x)]
+    assert np.array_equal(orc.bf16_rne(x), t_bf16(x))
+    # ties: 257 -> 256, 259 -> 260, 1+2^-8 -> 1, 1+3*2^-8 -> 1+2^-6
+    got = orc.bf16_to_f32(orc.bf16_rne(np.array([257, 259, 1 + 2**-8, 1 + 3 * 2**-8], np.float32)))
+    assert got.tolist() == [256.0, 260.0, 1.0, 1 + 2**-6]
+
+
+# ---------------------------------------------------------- quantisers
+def test_quantize_rows_single_nonzero_and_zero_row(orc):
+    x = np.zeros((3, 256), np.float32)
+    x[0, 17] = 3.5
+    x[1, 200] = -0.01
+    q, s = orc.quantize_rows(x)
+    assert s[0] == np.float32(3.5) / np.float32(448) and s[1] == np.float32(0.01) / np.float32(448)
+    assert s[2] == 1.0 and not q[2].any()
+    assert q[0, 17] == 0x7E and q[1, 200] == 0xFE
+    assert np.count_nonzero(q[0]) == 1 and np.count_nonzero(q[1]) == 1
+
+
+def test_quantize_rows_matches_torch(orc):
+    x = inputs.normal((64, 1792), 5)
+    q, s = orc.quantize_rows(x)
+    tx = torch.from_numpy(x)
+    ts = tx.abs().amax(dim=1) / 448.0
+    assert np.array_equal(s, ts.numpy())
+    assert np.array_equal(q, t_enc_e4m3((tx / ts[:, None]).numpy()))
+    # the row maximum lands on +-448
+    assert set(np.abs(orc.dec_e4m3(q)).max(axis=1).tolist()) == {448.0}
+
+
+def test_quantize_blockscale_a_is_per_row_on_each_k_block(orc):
+    x = inputs.normal((40, 512), 9)
+    q, s = orc.quantize_blockscale_a(x)
+    assert s.shape == (4, 40)
+    for kb in range(4):
+        qr, sr = orc.quantize_rows(x[:, kb * 128:(kb + 1) * 128])
+        assert np.array_equal(q[:, kb * 128:(kb + 1) * 128], qr)
+        assert np.array_equal(s[kb], sr)
+
+
+@pytest.mark.parametrize("n", [256, 272, 144])
+def test_quantize_blockscale_b_block_amax(orc, n):
+    x = inputs.normal((n, 384), 10 + n)
+    q, s = orc.quantize_blockscale_b(x)
+    assert s.shape == ((n + 127) // 128, 3)
+    tx = torch.from_numpy(x)
+    for nb in range(s.shape[0]):
+        for kb in range(3):
+            blk = tx[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128]
+            sc = blk.abs().amax() / 448.0
+            assert s[nb, kb] == sc.item()
+            assert np.array_equal(q[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128], t_enc_e4m3((blk / sc).numpy()))
+
+
+def test_quantize_mxfp8_exponent_and_codes(orc):
+    x = inputs.normal((24, 512), 11)
+    x[3, 32:64] = 0.0
+    x[5, :32] *= 1e-30
+    q, e = orc.quantize_mxfp8(x)
+    assert e.shape == (16, 24)
+    assert e[1, 3] == 127 and not q[3, 32:64].any()
+    g = x.reshape(24, 16, 32)
+    amax = np.abs(g).max(axis=2).T  # [K/32, rows]
+    r = (amax.astype(np.float32) / np.float32(448)).astype(np.float64)
+    ex = e.astype(np.float64) - 127
+    nz = amax > 0
+    # smallest power of two that holds the group: 2^(e-1) < amax/448 <= 2^e
+    assert np.all(r[nz] <= 2.0 ** ex[nz]) and np.all(r[nz] > 2.0 ** (ex[nz] - 1))
+    scale = torch.from_numpy(np.repeat(2.0 ** (-ex), 32, axis=0).T.astype(np.float32))
+    assert np.array_equal(q, t_enc_e4m3((torch.from_numpy(x) * scale).numpy()))
+
+
+# ---------------------------------------------------------------- GEMM
+@pytest.mark.parametrize("mode", ["ptpc", "blockscale", "mxfp8"])
+@pytest.mark.parametrize("M,N,K", [(17, 48, 256), (40, 144, 384), (3, 16, 128)])
+def test_gemm_exact_regime_equals_float64(orc, mode, M, N, K):
+    """Small integer codes and power-of-two scales: every partial sum is exact
+    in fp32, so the one correct answer is bf16(float64 matmul)."""
+    qa, qb = exact_codes((M, K), 100 + M, orc), exact_codes((N, K), 200 + N, orc)
+    sa, sb = random_scales(mode, M, N, K, 300 + K, exact=True)
+    fa, fb = full_scales(mode, sa, sb, M, N, K)
+    ref = (t_dec_e4m3(qa).astype(np.float64) * fa) @ (t_dec_e4m3(qb).astype(np.float64) * fb).T
+    got, got32 = run_gemm(orc, mode, qa, qb, sa, sb, want_f32=True)
+    assert np.array_equal(got32.astype(np.float64), ref)
+    assert np.array_equal(got, t_bf16(ref.astype(np.float32)))
+
+
+@pytest.mark.parametrize("mode", ["ptpc", "blockscale", "mxfp8"])
+def test_gemm_general_values_within_dot_product_bound(orc, mode):
+    """N(0,1)-quantised operands with arbitrary scales: the fp32 result lies
+    within gamma_K * sum|a'b'| of the float64 value of the same dot product,
+    and the bf16 output is that fp32 value rounded."""
+    M, N, K = 48, 48, 512
+    qa, _ = orc.quantize_rows(inputs.normal((M, K), 1))
+    qb, _ = orc.quantize_rows(inputs.normal((N, K), 2))
+    sa, sb = random_scales(mode, M, N, K, 5, exact=False)
+    fa, fb = full_scales(mode, sa, sb, M, N, K)
+    ap = (t_dec_e4m3(qa) * fa.astype(np.float32)).astype(np.float64)  # a' = fl32(dec * s)
+    bp = (t_dec_e4m3(qb) * fb.astype(np.float32)).astype(np.float64)
+    exact = ap @ bp.T
+    u = 2.0**-24
+    gamma = K * u / (1 - K * u)
+    bound = gamma * (np.abs(ap) @ np.abs(bp).T)
+    got, got32 = run_gemm(orc, mode, qa, qb, sa, sb, want_f32=True)
+    assert np.all(np.abs(got32 - exact) <= bound)
+    assert np.array_equal(got, t_bf16(got32))
+
+
+def test_gemm_identity_b_returns_dequantised_a(orc):
+    M, K = 33, 256
+    qa, sa = orc.quantize_rows(inputs.normal((M, K), 4))
+    qb = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(qb, orc.enc_e4m3(np.float32([1.0]))[0])
+    got = orc.gemm_ptpc(qa, qb, sa, np.ones(K, np.float32))
+    assert np.array_equal(got, t_bf16(t_dec_e4m3(qa) * sa[:, None]))
+
+
+def test_gemm_permutation_b_permutes_columns(orc):
+    M, K = 20, 128
+    qa, sa = orc.quantize_rows(inputs.normal((M, K), 6))
+    perm = np.random.default_rng(0).permutation(K)
+    qb = np.zeros((K, K), np.uint8)
+    qb[np.arange(K), perm] = orc.enc_e4m3(np.float32([1.0]))[0]
+    got = orc.gemm_ptpc(qa, qb, sa, np.ones(K, np.float32))
+    assert np.array_equal(got, t_bf16((t_dec_e4m3(qa) * sa[:, None])[:, perm]))
+
+
+def test_gemm_zero_a_gives_zero(orc):
+    qb, sb = orc.quantize_rows(inputs.normal((64, 256), 8))
+    got = orc.gemm_ptpc(np.zeros((5, 256), np.uint8), qb, np.ones(5, np.float32), sb)
+    assert not got.any()
+
+
+@pytest.mark.parametrize("mode", ["ptpc", "blockscale", "mxfp8"])
+def test_gemm_doubling_a_scale_doubles_output_bitwise(orc, mode):
+    M, N, K = 16, 64, 256
+    qa, _ = orc.quantize_rows(inputs.normal((M, K), 12))
+    qb, _ = orc.quantize_rows(inputs.normal((N, K), 13))
+    sa, sb = random_scales(mode, M, N, K, 14, exact=False)
+    sa2 = sa + 1 if mode == "mxfp8" else sa * 2
+    c1 = run_gemm(orc, mode, qa, qb, sa, sb)
+    c2 = run_gemm(orc, mode, qa, qb, sa2, sb)
+    assert np.array_equal(orc.bf16_to_f32(c2), 2 * orc.bf16_to_f32(c1))
+
+
+def test_gemm_modes_agree_on_uniform_scales(orc):
+    """mxfp8 with every scale byte 127 is ptpc with unit scales; blockscale
+    with every block of a row sharing one scale is ptpc with that scale."""
+    M, N, K = 24, 160, 512
+    qa, sa = orc.quantize_rows(inputs.normal((M, K), 15))
+    qb, sb = orc.quantize_rows(inputs.normal((N, K), 16))
+    unit_m, unit_n = np.ones(M, np.float32), np.ones(N, np.float32)
+    mx = orc.gemm_mxfp8(qa, qb, np.full((K // 32, M), 127, np.uint8), np.full((K // 32, N), 127, np.uint8))
+    assert np.array_equal(mx, orc.gemm_ptpc(qa, qb, unit_m, unit_n))
+    sbk = np.float32(0.0123)
+    bs = orc.gemm_blockscale(qa, qb, np.tile(sa, (K // 128, 1)), np.full(((N + 127) // 128, K // 128), sbk, np.float32))
+    assert np.array_equal(bs, orc.gemm_ptpc(qa, qb, sa, np.full(N, sbk, np.float32)))
+
+
+def test_gemm_vs_numpy_fp32_blas_at_first_workload(orc):
+    """512x1024x256 ptpc: the oracle and numpy's fp32 BLAS (a different
+    summation order) agree within the acceptance tolerance."""
+    mode, M, N, K, s1, s2 = inputs.WORKLOADS["ptpc_512x1024x256"]
+    qa, sa = orc.quantize_rows(inputs.normal((M, K), s1))
+    qb, sb = orc.quantize_rows(inputs.normal((N, K), s2))
+    got = orc.bf16_to_f32(orc.gemm_ptpc(qa, qb, sa, sb)).astype(np.float64)
+    blas = (t_dec_e4m3(qa) * sa[:, None]) @ (t_dec_e4m3(qb) * sb[:, None]).T
+    ref = bf16_to_f64(t_bf16(blas))
+    err = np.abs(got - ref)
+    assert np.all(err <= 2e-2 * np.abs(ref) + 1e-3)
+    assert np.sqrt((err**2).sum() / (ref**2).sum()) < GOLD["rel_l2_gate"]["value"] / 10
+    # and bf16 output rounding sits at the order the pages call the fp8 floor
+    rl2 = np.sqrt(((got - blas) ** 2).sum() / (blas**2).sum())
+    assert rl2 < GOLD["fp8_floor_rel_l2"]["value"] * 1.5
+
+
+def test_gemm_row_subset_matches_full(orc):
+    qa, sa = orc.quantize_rows(inputs.normal((300, 256), 17))
+    qb, sb = orc.quantize_rows(inputs.normal((272, 256), 18))
+    full = orc.gemm_ptpc(qa, qb, sa, sb, threads=3)
+    rows = np.array([0, 5, 299, 128, 7], np.int64)
+    assert np.array_equal(orc.gemm_ptpc(qa, qb, sa, sb, rows=rows, threads=2), full[rows])
+
+
+def test_gemm_bf16_exact_and_bounded(orc):
+    M, N, K = 40, 48, 1024
+    vals = np.array([0, 1, -1, 2, -2, 3, 0.5], np.float32)
+    a = t_bf16(inputs.choice((M, K), vals, 1))
+    b = t_bf16(inputs.choice((N, K), vals, 2))
+    ref = bf16_to_f64(a) @ bf16_to_f64(b).T
+    assert np.array_equal(orc.gemm_bf16(a, b), t_bf16(ref.astype(np.float32)))
+    a = t_bf16(inputs.normal((M, K), 3))
+    b = t_bf16(inputs.normal((N, K), 4))
+    exact = bf16_to_f64(a) @ bf16_to_f64(b).T
+    got, got32 = orc.gemm_bf16(a, b, want_f32=True)
+    u = 2.0**-24
+    bound = K * u / (1 - K * u) * (np.abs(bf16_to_f64(a)) @ np.abs(bf16_to_f64(b)).T)
+    assert np.all(np.abs(got32 - exact) <= bound)
+    assert np.array_equal(got, t_bf16(got32))

@@ -1,0 +1,198 @@
+"""Benchmark of the fp8 a8w8 GEMM on one MI355X.
+
+Headline: ptpc fp8 e4m3 GEMM, M=32768 N=7168 K=1792, bf16 out (the mori PR 785
+gemm-only table's ptpc row, section Cost).  A step is one GEMM launch over
+operands already resident in HBM: A quantised per token on the GPU
+(quantize_per_token), B quantised per output channel and preshuffled once.
+Inputs are seeded synthetic N(0,1) fp32 (A seed 31, B seed 32).
+
+Prints ONE JSON line.  The roofline object reports the GEMM kernel's
+algorithmic FLOPs per launch over its average launch time (HIP events on the
+launch stream) against the fp8 dense MFMA peak; traffic comes from the
+rocprofv3 FETCH_SIZE / WRITE_SIZE summaries under profiles/ when they were
+taken for the current kernel, else null.  cpu_baseline is the CPU oracle
+timed on a bounded row sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--extra", action="store_true", help="also time the other modes and shapes")
+    p.add_argument("--cpu-rows", type=int, default=1024, help="rows of the headline the oracle computes")
+    return p.parse_args()
+
+
+def timed(fn, steps, warmup):
+    """Average ms per call over ``steps`` back-to-back launches on the current
+    stream (HIP events), after ``warmup`` launches; synchronised both sides."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def headline_operands(dmm, torch, m, n, k, seed_a, seed_b, mode="ptpc"):
+    from dense_matmul_amd import inputs
+
+    a32 = torch.from_numpy(inputs.operand_a(m, k, seed_a)).to("cuda:0")
+    b32 = torch.from_numpy(inputs.normal((n, k), seed_b)).to("cuda:0")
+    if mode == "ptpc":
+        qa, sa = dmm.quantize_per_token(a32)
+        qb, sb = dmm.quantize_per_token(b32)
+    elif mode == "blockscale":
+        qa, sa = dmm.quantize_blockscale_a(a32)
+        qb, sb = dmm.quantize_blockscale_b(b32)
+    else:
+        qa, sa = dmm.quantize_mxfp8(a32)
+        qb, sb = dmm.quantize_mxfp8(b32)
+    bs = dmm.preshuffle_b(qb)
+    del a32, b32
+    torch.cuda.synchronize()
+    return qa, bs, sa, sb
+
+
+def traffic_from_profiles(kernel_tag):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if one
+    exists for the current kernel build (profiles/<tag>_traffic.json)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        return d.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(m, n, k, rows_n):
+    """The oracle, untouched, on ``rows_n`` evenly spaced rows of the headline
+    workload with every host thread; returns TFLOP/s and the sample used."""
+    import numpy as np
+
+    import oracle
+    from dense_matmul_amd import inputs
+
+    a = inputs.normal((m, k), 31)
+    b = inputs.normal((n, k), 32)
+    qa, sa = oracle.quantize_per_token(a)
+    qb, sb = oracle.quantize_per_token(b)
+    rows = np.linspace(0, m - 1, rows_n).astype(np.int64)
+    threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.gemm_ptpc(qa, qb, sa, sb, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows_n * n * k
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_n} evenly spaced rows of {m} (all {n} columns, K={k}), GEMM only, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import dense_matmul_amd as dmm
+
+    dmm.lib()
+    m, n, k = 32768, 7168, 1792
+    qa, bs, sa, sb = headline_operands(dmm, torch, m, n, k, 31, 32)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+    ms = timed(lambda: dmm.gemm_a8w8_ptpc(qa, bs, sa, sb, out=out), args.steps, args.warmup)
+    flops = 2.0 * m * n * k
+    tflops = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "fp8 GEMM TFLOP/s + % of fp8 MFMA peak, ptpc 32768x7168x1792 (1 MI355X)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic N(0,1), seeds 31/32, quantised per token / per channel on the GPU",
+        "config": {"workload": "ptpc fp8 GEMM M=32768 N=7168 K=1792", "mode": "ptpc", "m": m, "n": n, "k": k,
+                   "pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic_from_profiles("gemm_a8w8_ptpc")},
+    }
+    del out
+    if args.extra:
+        rec["extra"] = extra_shapes(dmm, torch, args)
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(m, n, k, args.cpu_rows)
+    print(json.dumps(rec), flush=True)
+
+
+def extra_shapes(dmm, torch, args):
+    """Secondary lines: the other scaling modes, the tail-only and gathered
+    shapes, and the bf16 GEMM (fewer steps each)."""
+    res = {}
+    steps, warm = max(5, args.steps // 5), 3
+    for name, mode, m, n, k, sa_seed, sb_seed in [
+        ("blockscale_16384x7168x2048", "blockscale", 16384, 7168, 2048, 41, 42),
+        ("mxfp8_32768x7168x1792", "mxfp8", 32768, 7168, 1792, 31, 32),
+        ("mxfp8_16384x7168x2048", "mxfp8", 16384, 7168, 2048, 41, 42),
+        ("ptpc_4096x7168x256", "ptpc", 4096, 7168, 256, 11, 12),
+        ("ptpc_16384x7168x512", "ptpc", 16384, 7168, 512, 21, 22),
+        ("ptpc_gathered_32768x6288x7168", "ptpc", 32768, 6288, 7168, tuple(range(500, 508)), 510),
+        ("ptpc_gathered_32768x3648x7168", "ptpc", 32768, 3648, 7168, tuple(range(500, 508)), 511),
+    ]:
+        qa, bs, sa, sb = headline_operands(dmm, torch, m, n, k, sa_seed, sb_seed, mode)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+        fn = {"ptpc": dmm.gemm_a8w8_ptpc, "blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
+        ms = timed(lambda: fn(qa, bs, sa, sb, out=out), steps, warm)
+        tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        hbm = (m * k + n * k + 2 * m * n) / (ms * 1e-3) / 1e9
+        res[name] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1), "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 1),
+                     "alg_GB/s": round(hbm, 0)}
+        del qa, bs, sa, sb, out
+        torch.cuda.empty_cache()
+    from dense_matmul_amd import inputs
+
+    m, k, n = 4096, 1024, 896
+    a32, b_kn = inputs.bf16_operands(m, k, n, 233)
+    a = torch.from_numpy(a32).to(torch.bfloat16).to("cuda:0")
+    b = torch.from_numpy(b_kn.T.copy()).to(torch.bfloat16).to("cuda:0")
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+    ms = timed(lambda: dmm.gemm_bf16(a, b, out=out), 200, 20)
+    tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    res["bf16_4096x1024x896"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+                                 "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
+    return res
+
+
+if __name__ == "__main__":
+    main()

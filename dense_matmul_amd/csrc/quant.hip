@@ -1,0 +1,208 @@
+// quant.hip -- E4M3 quantisers and the B preshuffle for gfx950.
+//
+// Per-token quantisation with scale amax / 448 is the activation path of
+// mori PR 809 ("mori.ops.ag_gemm", section Using it); blockscale (1x128 for
+// A, 128x128 for B) and mxfp8 (E8M0 per 32 K) are the other two modes of
+// mori PR 785 (section Cost).  All kernels are HBM-bound streams: fully
+// coalesced 16-byte loads, wave-level max reductions through lane shuffles,
+// and the quantised bytes written 4 per lane.
+#include "common.h"
+
+namespace dmm {
+
+// fp32 -> OCP E4M3 code, round to nearest even, saturating at +-448; NaN
+// maps to 0x7F.  Bit arithmetic: below 2^-6 the grid is uniform (2^-9), so
+// rint(|v| * 512) is the code; above it, rounding the fp32 significand to 3
+// fraction bits (adding 0x7FFFF plus the kept LSB at bit 20) carries into the
+// exponent exactly like the format does.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t au = u & 0x7FFFFFFFu;
+    if (au > 0x7F800000u) return 0x7Fu;                       // NaN
+    if (au >= 0x43E00000u) return sign | 0x7Eu;               // |v| >= 448 (incl. inf)
+    if (au < 0x3C800000u) {                                   // |v| < 2^-6
+        const float a = __builtin_bit_cast(float, au);
+        return sign | (uint32_t)__builtin_rintf(a * 512.0f); // exact scaling, RNE
+    }
+    const uint32_t r = au + 0x7FFFFu + ((au >> 20) & 1u);
+    const uint32_t e = (r >> 23) - 127u + 7u;                 // 1 .. 15
+    return sign | (e << 3) | ((r >> 20) & 7u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float group_max(float v, int width) {
+    for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float amax_to_scale(float amax) { return amax == 0.0f ? 1.0f : amax / 448.0f; }
+
+__device__ __forceinline__ uint32_t pack4(v4f v, float s) {
+    return e4m3_code(v[0] / s) | (e4m3_code(v[1] / s) << 8) | (e4m3_code(v[2] / s) << 16) | (e4m3_code(v[3] / s) << 24);
+}
+
+// ------------------------------------------------------------- per token
+// One wave per row; 4 rows per workgroup.  cols % 16 == 0.
+__global__ void __launch_bounds__(256) quantize_rows_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
+                                                            float* __restrict__ scale, int rows, int cols) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const v4f* xr = (const v4f*)(x + (size_t)row * cols);
+    uint32_t* qr = (uint32_t*)(q + (size_t)row * cols);
+    const int n4 = cols / 4;
+    float amax = 0.0f;
+    for (int c = lane; c < n4; c += 64) {
+        const v4f v = xr[c];
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
+    const float s = amax_to_scale(wave_max(amax));
+    for (int c = lane; c < n4; c += 64) qr[c] = pack4(xr[c], s);
+    if (lane == 0) scale[row] = s;
+}
+
+// ------------------------------------------------------- blockscale A
+// One wave per row; each pass covers 256 columns, lanes 0-31 one 128-wide
+// block and lanes 32-63 the next.  k % 128 == 0.
+__global__ void __launch_bounds__(256) quantize_blockscale_a_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
+                                                                    float* __restrict__ scale, int m, int k) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= m) return;
+    const v4f* xr = (const v4f*)(x + (size_t)row * k);
+    uint32_t* qr = (uint32_t*)(q + (size_t)row * k);
+    const int n4 = k / 4;
+    for (int base = 0; base < n4; base += 64) {
+        const int c = base + lane;
+        const bool valid = c < n4;  // false only for lanes 32-63 of a last half pass
+        v4f v = valid ? xr[c] : (v4f){0.f, 0.f, 0.f, 0.f};
+        float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        const float s = amax_to_scale(group_max(a, 32));
+        if (valid) {
+            qr[c] = pack4(v, s);
+            if ((lane & 31) == 0) scale[(size_t)(c / 32) * m + row] = s;
+        }
+    }
+}
+
+// ------------------------------------------------------- blockscale B
+// One workgroup per 128 x 128 block (rows past n are skipped).
+__global__ void __launch_bounds__(256) quantize_blockscale_b_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
+                                                                    float* __restrict__ scale, int n, int k) {
+    __shared__ float red[4];
+    const int kb = blockIdx.x, nb = blockIdx.y, kblocks = k / 128;
+    const int t = threadIdx.x;
+    const int col4 = t & 31;  // float4 column within the block
+    const int r0 = t >> 5;    // 8 row lanes
+    const int rows = min(128, n - nb * 128);
+    float amax = 0.0f;
+    for (int r = r0; r < rows; r += 8) {
+        const v4f v = *(const v4f*)(x + (size_t)(nb * 128 + r) * k + kb * 128 + col4 * 4);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
+    amax = wave_max(amax);
+    if ((t & 63) == 0) red[t >> 6] = amax;
+    __syncthreads();
+    const float s = amax_to_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    for (int r = r0; r < rows; r += 8) {
+        const size_t off = (size_t)(nb * 128 + r) * k + kb * 128 + col4 * 4;
+        *(uint32_t*)(q + off) = pack4(*(const v4f*)(x + off), s);
+    }
+    if (t == 0) scale[(size_t)nb * kblocks + kb] = s;
+}
+
+// ------------------------------------------------------------- mxfp8
+// Exponent e = ceil(log2(amax / 448)) read off the fp32 bits of r = amax/448:
+// a power of two keeps its exponent, anything else rounds up by one.
+__device__ __forceinline__ int mx_exp(float amax) {
+    if (amax == 0.0f) return 0;
+    float r = amax / 448.0f;
+    int bias = 0;
+    uint32_t u = __builtin_bit_cast(uint32_t, r);
+    if ((u >> 23) == 0) {  // subnormal: scale up exactly by 2^24 first
+        r = r * 16777216.0f;
+        u = __builtin_bit_cast(uint32_t, r);
+        bias = 24;
+    }
+    int e = (int)(u >> 23) - 127 - bias + ((u & 0x7FFFFFu) ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// One wave per row; each pass covers 256 columns = 8 groups of 32 (8 lanes
+// per group).  k % 128 == 0 so a pass is never split inside a group.
+__global__ void __launch_bounds__(256) quantize_mxfp8_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ scale, int rows, int k) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const v4f* xr = (const v4f*)(x + (size_t)row * k);
+    uint32_t* qr = (uint32_t*)(q + (size_t)row * k);
+    const int n4 = k / 4;
+    for (int base = 0; base < n4; base += 64) {
+        const int c = base + lane;
+        const bool valid = c < n4;
+        v4f v = valid ? xr[c] : (v4f){0.f, 0.f, 0.f, 0.f};
+        float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        const int e = mx_exp(group_max(a, 8));
+        if (valid) {
+            qr[c] = e4m3_code(__builtin_ldexpf(v[0], -e)) | (e4m3_code(__builtin_ldexpf(v[1], -e)) << 8) |
+                    (e4m3_code(__builtin_ldexpf(v[2], -e)) << 16) | (e4m3_code(__builtin_ldexpf(v[3], -e)) << 24);
+            if ((lane & 7) == 0) scale[(size_t)(c / 8) * rows + row] = (uint8_t)(e + 127);
+        }
+    }
+}
+
+// ----------------------------------------------------------- preshuffle
+// Output chunk (block j of 16 rows, K tile kt) = 2 KiB at (j * KI + kt) * 2048.
+// Byte 16 l + t of half h (t < 16) holds B[16 j + l % 16][128 kt + 64 h +
+// 16 (l / 16) + t]: exactly the 32 bytes matrix-core lane l consumes for a
+// 16 x 128 fp8 operand, so each half is one coalesced 1 KiB load.
+__global__ void __launch_bounds__(256) preshuffle_b_kernel(const uint8_t* __restrict__ b, uint8_t* __restrict__ out,
+                                                           int n, int k) {
+    const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;  // one 16-byte piece per thread
+    const int KI = k / 128;
+    const size_t total = (size_t)n * k / 16;
+    if (t >= total) return;
+    const int l = (int)(t & 63);
+    const int h = (int)((t >> 6) & 1);
+    const size_t chunk = t >> 7;
+    const int kt = (int)(chunk % KI);
+    const int j = (int)(chunk / KI);
+    const size_t src = (size_t)(16 * j + (l & 15)) * k + 128 * kt + 64 * h + 16 * (l >> 4);
+    *(v4i*)(out + t * 16) = *(const v4i*)(b + src);
+}
+
+// -------------------------------------------------------------- launch
+hipError_t launch_quantize_rows(const float* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st) {
+    hipLaunchKernelGGL(quantize_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, x, q, s, rows, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_blockscale_a(const float* x, uint8_t* q, float* s, int m, int k, hipStream_t st) {
+    hipLaunchKernelGGL(quantize_blockscale_a_kernel, dim3((m + 3) / 4), dim3(256), 0, st, x, q, s, m, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_blockscale_b(const float* x, uint8_t* q, float* s, int n, int k, hipStream_t st) {
+    hipLaunchKernelGGL(quantize_blockscale_b_kernel, dim3(k / 128, (n + 127) / 128), dim3(256), 0, st, x, q, s, n, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8(const float* x, uint8_t* q, uint8_t* s, int rows, int k, hipStream_t st) {
+    hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, x, q, s, rows, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_preshuffle_b(const uint8_t* b, uint8_t* out, int n, int k, hipStream_t st) {
+    const size_t pieces = (size_t)n * k / 16;
+    hipLaunchKernelGGL(preshuffle_b_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st, b, out, n, k);
+    return hipGetLastError();
+}
+
+}  // namespace dmm

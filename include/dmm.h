@@ -1,0 +1,139 @@
+/*
+ * dmm.h -- C ABI of libdmm, an fp8 a8w8 GEMM library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The user sequence follows mori PR 809 ("mori.ops.ag_gemm"), section Using
+ * it: quantise the activations per token, preshuffle the fp8 weight once,
+ * then call the GEMM with both operands and their scales; the result is a
+ * contiguous bf16 [M, N] tensor.  The GEMM computes
+ *
+ *     C[m, n] = bf16( sum_k (A[m, k] * sa(m, k)) * (B[n, k] * sb(n, k)) )
+ *
+ * with fp32 accumulation, where A [M, K] and B [N, K] hold OCP FP8 E4M3 codes
+ * and sa / sb depend on the scaling mode (ptpc, blockscale, mxfp8) named in
+ * mori PR 785 ("fix(gemm-ar): drain the peeled tail's producers instead of
+ * tightening the loop"), section Cost.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing and keeps no state beyond a per-device arch check.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL is the default stream).  Nothing synchronises the host.
+ *   - Layouts are row-major and contiguous.  e4m3 codes are uint8_t (OCP
+ *     FP8 E4M3, max 448, NaN = S.1111.111); bf16 values are uint16_t bit
+ *     patterns; E8M0 scales are uint8_t (2^(b-127)).
+ *   - Argument errors return DMM_EINVAL before any HIP call is made;
+ *     dmm_last_error() then describes the first violated rule.  A device that
+ *     is not gfx950 returns DMM_ENODEV.  A failed launch returns DMM_ELAUNCH.
+ *   - Every pointer must be 16-byte aligned, and every operand (A, B, C,
+ *     scales) must be smaller than 2^31 bytes: the kernels address operands
+ *     through 32-bit buffer offsets.
+ *   - Calls on one stream are ordered; calls on different streams that write
+ *     the same buffer race, as with any kernel.
+ */
+#ifndef DMM_H
+#define DMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DMM_OK = 0,
+    DMM_EINVAL = 1,  /* an argument breaks a documented rule */
+    DMM_ENODEV = 2,  /* the current device is not gfx950 */
+    DMM_ELAUNCH = 3  /* the HIP runtime reported an error */
+} dmm_status;
+
+/* Name of a status code ("DMM_OK", ...). */
+const char* dmm_status_str(int status);
+
+/* Detail for the last non-OK return on the calling thread ("" if none). */
+const char* dmm_last_error(void);
+
+/* ---------------------------------------------------------------- quantise */
+
+/* Per-row E4M3 quantisation (mori PR 809, Using it: quantize_per_token; the
+ * workloads use scale = amax / 448).  For each row r of x [rows, cols] fp32:
+ *   scale[r] = amax_r / 448 (IEEE fp32 division; 1.0 when the row is zero),
+ *   q[r, c]  = E4M3(x[r, c] / scale[r]), round to nearest even, saturating
+ *              to +-448.
+ * Used per token for A and per output channel for B [N, K].
+ * Rules: rows >= 1, cols >= 16, cols % 16 == 0.  q [rows, cols] u8, scale
+ * [rows] fp32, both written. */
+dmm_status quantize_per_token(const float* x, uint8_t* q, float* scale, int64_t rows, int64_t cols,
+                              void* stream);
+
+/* Blockscale A: one fp32 scale per row per 128-wide K block (mori PR 785,
+ * Cost: blockscale; the A scale is K-block major, mori PR 809, Not done yet).
+ *   scale[kb * m + r] = amax(x[r, 128kb .. 128kb+127]) / 448 (1.0 if zero),
+ *   q[r, c] = E4M3(x[r, c] / scale[c/128 * m + r]).
+ * Rules: m >= 1, k >= 128, k % 128 == 0. */
+dmm_status quantize_blockscale_a(const float* x, uint8_t* q, float* scale, int64_t m, int64_t k, void* stream);
+
+/* Blockscale B [n, k]: one fp32 scale per 128 x 128 block, stored
+ * scale[nb * (k/128) + kb]; a partial last row block uses only the rows it
+ * has.  Rules: n >= 16, n % 16 == 0, k >= 128, k % 128 == 0. */
+dmm_status quantize_blockscale_b(const float* x, uint8_t* q, float* scale, int64_t n, int64_t k, void* stream);
+
+/* mxfp8: one E8M0 scale per 32 consecutive K values of a row (mori PR 785,
+ * Cost: mxfp8).  e = ceil(log2(amax / 448)) clamped to [-127, 127] (0 for a
+ * zero group), stored scale[(c/32) * rows + r] = e + 127;
+ * q[r, c] = E4M3(x[r, c] * 2^-e).  Used for both A [M, K] and B [N, K].
+ * Rules: rows >= 1, k >= 128, k % 128 == 0. */
+dmm_status quantize_mxfp8(const float* x, uint8_t* q, uint8_t* scale, int64_t rows, int64_t k, void* stream);
+
+/* ------------------------------------------------------------- preshuffle */
+
+/* Reorders B [n, k] E4M3 codes (one row per output channel) into the byte
+ * order the GEMM's matrix-core operands use (aiter PR 6539 names the kernels
+ * "bpreshuffle"; mori PR 809, Using it, calls preshuffle_b once per weight).
+ * The layout is library-defined and opaque: b_shuf has the same size as b
+ * (n * k bytes) and is only meant to be passed to the gemm_a8w8_* calls.
+ * b and b_shuf must not overlap.  Rules: n >= 16, n % 16 == 0, k >= 128,
+ * k % 128 == 0. */
+dmm_status preshuffle_b(const uint8_t* b, uint8_t* b_shuf, int64_t n, int64_t k, void* stream);
+
+/* --------------------------------------------------------------- the GEMM */
+
+/* Rules shared by the three fp8 GEMMs:
+ *   m >= 1; n >= 16 and n % 16 == 0 (the last 256-column tile may be
+ *   partial; mori PR 809, Using it); k >= 128 and k % 128 == 0 (k = 256
+ *   runs the peeled tail only; mori PR 785, Why the existing A+B-1 did not
+ *   fix it).  a [m, k] u8 codes; b_shuf from preshuffle_b; c [m, n] bf16 is
+ *   fully overwritten and nothing outside it is written. */
+
+/* ptpc: a_scale [m] fp32 per token, b_scale [n] fp32 per output channel.
+ *   C[m, n] = bf16(a_scale[m] * b_scale[n] * sum_k A[m, k] B[n, k]). */
+dmm_status gemm_a8w8_ptpc(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale, const float* b_scale,
+                          uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream);
+
+/* blockscale: a_scale [k/128][m] fp32 (1x128 blocks, K-block major),
+ * b_scale [ceil(n/128)][k/128] fp32 (128x128 blocks).
+ *   C[m, n] = bf16(sum_kb a_scale[kb][m] b_scale[n/128][kb] sum_{k in kb} A B). */
+dmm_status gemm_a8w8_blockscale(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale,
+                                const float* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k,
+                                void* stream);
+
+/* mxfp8: a_scale [k/32][m] and b_scale [k/32][n] E8M0 bytes, one per 32
+ * consecutive K values.
+ *   C[m, n] = bf16(sum_g 2^(a_scale[g][m]-127) 2^(b_scale[g][n]-127) sum_{k in g} A B).
+ * Scale byte 255 (NaN) is outside the contract. */
+dmm_status gemm_a8w8_mxfp8(const uint8_t* a, const uint8_t* b_shuf, const uint8_t* a_scale,
+                           const uint8_t* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream);
+
+/* bf16 GEMM with fp32 accumulation (DeepGEMM PR 453, "Fix SM120 BF16 GEMM
+ * shared-memory reuse ordering", Reproduction and validation: [4096, 1024]
+ * x [1024, 896]).  a [m, k] bf16, b [n, k] bf16 (the weight given one row
+ * per output column), c [m, n] bf16 = bf16(sum_k a[m, k] b[n, k]).
+ * Rules: m >= 1; n >= 16, n % 16 == 0; k >= 64, k % 64 == 0. */
+dmm_status gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t m, int64_t n, int64_t k,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMM_H */

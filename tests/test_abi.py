@@ -1,0 +1,82 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/dmm.h declares, and rejects invalid arguments with DMM_EINVAL before
+making any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dmm.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)) - {"if"})
+
+
+@pytest.fixture(scope="module")
+def L():
+    import dense_matmul_amd as dmm
+
+    if not os.path.exists(dmm.LIB_PATH):
+        from dense_matmul_amd import build
+
+        build.build()
+    return dmm.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("quantize_per_token", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8",
+              "gemm_bf16", "quantize_blockscale_a", "quantize_blockscale_b", "quantize_mxfp8", "dmm_status_str",
+              "dmm_last_error"):
+        assert f in names, f
+
+
+def test_library_exports_every_declared_function(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"libdmm.so does not export {name}"
+
+
+def test_status_strings(L):
+    assert L.dmm_status_str(0) == b"DMM_OK"
+    assert L.dmm_status_str(1) == b"DMM_EINVAL"
+    assert L.dmm_status_str(99) == b"DMM_UNKNOWN"
+
+
+ALIGNED = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("m,n,k,why", [
+    (0, 256, 256, "m must be"), (64, 24, 256, "n must be"), (64, 8, 256, "n must be"), (64, 256, 200, "k must be"),
+    (64, 256, 0, "k must be"), (1 << 22, 1024, 1024, "too large"), (64, 1 << 22, 1024, "too large"),
+])
+def test_gemm_shape_rules(L, m, n, k, why):
+    for fn in (L.gemm_a8w8_ptpc, L.gemm_a8w8_blockscale, L.gemm_a8w8_mxfp8):
+        assert fn(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, m, n, k, None) == 1
+        assert why in L.dmm_last_error().decode()
+
+
+def test_gemm_pointer_rules(L):
+    bad = ctypes.c_void_p((1 << 20) + 4)
+    assert L.gemm_a8w8_ptpc(None, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 64, 256, 256, None) == 1
+    assert b"a:" in L.dmm_last_error()
+    assert L.gemm_a8w8_ptpc(ALIGNED, bad, ALIGNED, ALIGNED, ALIGNED, 64, 256, 256, None) == 1
+    assert b"b:" in L.dmm_last_error()
+    assert L.gemm_bf16(ALIGNED, ALIGNED, None, 64, 256, 256, None) == 1
+
+
+def test_quantiser_and_preshuffle_rules(L):
+    assert L.quantize_per_token(ALIGNED, ALIGNED, ALIGNED, 0, 256, None) == 1
+    assert L.quantize_per_token(ALIGNED, ALIGNED, ALIGNED, 4, 17, None) == 1
+    assert L.quantize_blockscale_a(ALIGNED, ALIGNED, ALIGNED, 4, 100, None) == 1
+    assert L.quantize_blockscale_b(ALIGNED, ALIGNED, ALIGNED, 20, 128, None) == 1
+    assert L.quantize_mxfp8(ALIGNED, ALIGNED, ALIGNED, 4, 96, None) == 1
+    assert L.preshuffle_b(ALIGNED, ALIGNED, 24, 128, None) == 1
+    # overlapping source and destination
+    assert L.preshuffle_b(ALIGNED, ctypes.c_void_p((1 << 20) + 256), 16, 128, None) == 1
+    assert b"overlap" in L.dmm_last_error()
+    assert L.gemm_bf16(ALIGNED, ALIGNED, ALIGNED, 4, 16, 96, None) == 1

@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerance for floating-point results (the GEMM): element-wise
+|gpu - ref| <= 2e-2 |ref| + 1e-3 and relL2 < 3e-3 against the bf16-rounded
+oracle, the relL2 gate being the one mori PR 785 (section Test) and PR 809
+(section Results) validate against.  Exact-arithmetic inputs (small integer
+codes, power-of-two scales) must match bitwise, as must the quantisers'
+codes and scales.  Each case is printed before it runs, so a failure names
+its shape and seed.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dense_matmul_amd import inputs
+from oracle import tolerance
+
+pytestmark = pytest.mark.gpu
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+REL_L2 = GOLD["rel_l2_gate"]["value"]
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def dmm():
+    import dense_matmul_amd as d
+
+    d.lib()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return d
+
+
+def announce(*a):
+    print("[case]", *a, flush=True)
+
+
+def bf16_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bits_to_f64(h):
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_close(got_bits, ref_bits, what, mode=None, operands=None, rows=None):
+    """The acceptance rule of oracle.tolerance (the benchmark spec's element-wise and
+    relL2 gates, plus the measured matrix-core bound for the rare near-zero
+    outputs); prints the statistics."""
+    stats = tolerance.check(got_bits, ref_bits, what, mode=mode, operands=operands, rows=rows)
+    print("[stats]", what, stats, flush=True)
+    return stats
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+# ------------------------------------------------------------ quantisers
+@pytest.mark.parametrize("rows,cols,seed", [(512, 256, 1), (300, 1792, 2), (7, 7168, 3), (64, 16, 4)])
+def test_quantize_per_token_bitexact(dmm, rows, cols, seed):
+    announce("quantize_per_token", rows, cols, seed)
+    x = inputs.normal((rows, cols), seed)
+    x[0] = 0.0
+    if rows > 2:
+        x[1] = 0.0
+        x[1, cols // 2] = -3.25
+        x[2] *= 1e-3
+    q, s = dmm.quantize_per_token(to_dev(x))
+    oq, os_ = oracle.quantize_per_token(x)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), oq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,k,seed", [(300, 384, 5), (64, 128, 6), (33, 2048, 7)])
+def test_quantize_blockscale_a_bitexact(dmm, m, k, seed):
+    announce("quantize_blockscale_a", m, k, seed)
+    x = inputs.normal((m, k), seed)
+    x[3, 128:256] = 0.0
+    q, s = dmm.quantize_blockscale_a(to_dev(x))
+    oq, os_ = oracle.quantize_blockscale_a(x)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), oq)
+    assert np.array_equal(s.cpu().numpy(), os_)
+
+
+@pytest.mark.parametrize("n,k,seed", [(272, 384, 8), (16, 128, 9), (1168, 256, 10)])
+def test_quantize_blockscale_b_bitexact(dmm, n, k, seed):
+    announce("quantize_blockscale_b", n, k, seed)
+    x = inputs.normal((n, k), seed)
+    q, s = dmm.quantize_blockscale_b(to_dev(x))
+    oq, os_ = oracle.quantize_blockscale_b(x)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), oq)
+    assert np.array_equal(s.cpu().numpy(), os_)
+
+
+@pytest.mark.parametrize("rows,k,seed", [(300, 384, 11), (17, 1792, 12), (64, 128, 13)])
+def test_quantize_mxfp8_bitexact(dmm, rows, k, seed):
+    announce("quantize_mxfp8", rows, k, seed)
+    x = inputs.normal((rows, k), seed)
+    x[1, 32:64] = 0.0
+    x[2, :32] *= 1e-20
+    x[3, 64:96] *= 1e4
+    q, e = dmm.quantize_mxfp8(to_dev(x))
+    oq, oe = oracle.quantize_mxfp8(x)
+    assert np.array_equal(e.cpu().numpy(), oe)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), oq)
+
+
+# ------------------------------------------------------------ preshuffle
+def unshuffle(bs, n, k):
+    """Inverse of the library's B order, written from its documented layout:
+    chunk (j, kt) of 2 KiB; byte 16 l + t of half h is
+    B[16 j + l % 16][128 kt + 64 h + 16 (l / 16) + t]."""
+    ki = k // 128
+    v = bs.reshape(n // 16, ki, 2, 4, 16, 16)  # j, kt, h, l/16 (g), l%16 (i), t
+    # B[16 j + i][128 kt + 64 h + 16 g + t]
+    return v.transpose(0, 4, 1, 2, 3, 5).reshape(n, k)
+
+
+@pytest.mark.parametrize("n,k", [(16, 128), (272, 384), (1168, 1792)])
+def test_preshuffle_is_the_documented_permutation(dmm, n, k):
+    announce("preshuffle_b", n, k)
+    b = np.random.default_rng(n + k).integers(0, 256, size=(n, k), dtype=np.uint8)
+    bs = dmm.preshuffle_b(to_dev(b)).cpu().numpy()
+    assert np.array_equal(np.bincount(bs.ravel(), minlength=256), np.bincount(b.ravel(), minlength=256))
+    assert np.array_equal(unshuffle(bs, n, k), b)
+
+
+# ------------------------------------------------------------------ GEMM
+def quantised_operands(mode, m, n, k, seed_a, seed_b):
+    """fp32 N(0,1) operands quantised by the oracle's quantisers."""
+    a = inputs.operand_a(m, k, seed_a)
+    b = inputs.normal((n, k), seed_b)
+    if mode == "ptpc":
+        qa, sa = oracle.quantize_per_token(a)
+        qb, sb = oracle.quantize_per_token(b)
+    elif mode == "blockscale":
+        qa, sa = oracle.quantize_blockscale_a(a)
+        qb, sb = oracle.quantize_blockscale_b(b)
+    else:
+        qa, sa = oracle.quantize_mxfp8(a)
+        qb, sb = oracle.quantize_mxfp8(b)
+    return qa, qb, sa, sb
+
+
+def gpu_gemm(dmm, mode, qa, qb, sa, sb, out=None):
+    b_shuf = dmm.preshuffle_b(to_dev(qb))
+    fn = {"ptpc": dmm.gemm_a8w8_ptpc, "blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
+    return fn(to_dev(qa), b_shuf, to_dev(sa), to_dev(sb), out=out)
+
+
+def exact_operands(mode, m, n, k, seed):
+    vals = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0], np.float32)
+    codes = oracle.enc_e4m3(vals)
+    qa = inputs.choice((m, k), codes, seed)
+    qb = inputs.choice((n, k), codes, seed + 1)
+    p2 = np.array([0.25, 0.5, 1.0, 2.0, 4.0], np.float32)
+    if mode == "ptpc":
+        sa, sb = inputs.choice((m,), p2, seed + 2), inputs.choice((n,), p2, seed + 3)
+    elif mode == "blockscale":
+        sa = inputs.choice((k // 128, m), p2, seed + 2)
+        sb = inputs.choice(((n + 127) // 128, k // 128), p2, seed + 3)
+    else:
+        e = np.arange(125, 130, dtype=np.uint8)
+        sa, sb = inputs.choice((k // 32, m), e, seed + 2), inputs.choice((k // 32, n), e, seed + 3)
+    return qa, qb, sa, sb
+
+
+EXACT_SHAPES = [(1, 16, 128), (17, 272, 256), (300, 1168, 384), (256, 256, 512), (513, 528, 640), (64, 48, 1792)]
+
+
+@pytest.mark.parametrize("mode", ["ptpc", "blockscale", "mxfp8"])
+@pytest.mark.parametrize("m,n,k", EXACT_SHAPES)
+def test_gemm_exact_regime_bitwise(dmm, mode, m, n, k):
+    """Every partial sum exact in fp32: the GPU must equal the oracle bitwise,
+    including the partial last row and column tiles and K = 128 / 256."""
+    announce("exact", mode, m, n, k)
+    qa, qb, sa, sb = exact_operands(mode, m, n, k, m + n + k)
+    c = gpu_gemm(dmm, mode, qa, qb, sa, sb)
+    ref = oracle.gemm_a8w8({"ptpc": 0, "blockscale": 1, "mxfp8": 2}[mode], qa, qb, sa, sb)
+    got = bf16_bits(c)
+    mism = np.argwhere(got != ref)
+    assert mism.size == 0, f"{mode} {m}x{n}x{k}: {len(mism)} mismatches, first at {mism[:4].tolist()}"
+
+
+@pytest.mark.parametrize("mode", ["ptpc", "blockscale", "mxfp8"])
+@pytest.mark.parametrize("m,n,k,sa_seed,sb_seed", [(512, 1024, 256, 1, 2), (300, 1168, 1792, 61, 62),
+                                                   (17, 16, 128, 3, 4), (1000, 3648, 512, 5, 6)])
+def test_gemm_normal_inputs_within_tolerance(dmm, mode, m, n, k, sa_seed, sb_seed):
+    announce("normal", mode, m, n, k)
+    qa, qb, sa, sb = quantised_operands(mode, m, n, k, sa_seed, sb_seed)
+    c = gpu_gemm(dmm, mode, qa, qb, sa, sb)
+    ref = oracle.gemm_a8w8({"ptpc": 0, "blockscale": 1, "mxfp8": 2}[mode], qa, qb, sa, sb)
+    check_close(bf16_bits(c), ref, f"{mode} {m}x{n}x{k}", mode, (qa, qb, sa, sb))
+
+
+def run_poisoned(dmm, mode, qa, qb, sa, sb, launches, hog=False):
+    """``launches`` launches, each into a freshly NaN-poisoned C followed by a
+    4 KiB canary; returns the outputs (bf16 bits) of every launch."""
+    m, n = qa.shape[0], qb.shape[0]
+    b_shuf = dmm.preshuffle_b(to_dev(qb))
+    a, s_a, s_b = to_dev(qa), to_dev(sa), to_dev(sb)
+    fn = {"ptpc": dmm.gemm_a8w8_ptpc, "blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
+    buf = torch.empty(m * n + 2048, dtype=torch.bfloat16, device=DEV)
+    c = buf[: m * n].view(m, n)
+    canary = buf[m * n:]
+    hog_src = torch.empty(64 << 20, dtype=torch.uint8, device=DEV) if hog else None
+    hog_dst = torch.empty_like(hog_src) if hog else None
+    side = torch.cuda.Stream() if hog else None
+    outs = []
+    for _ in range(launches):
+        buf.fill_(float("nan"))
+        canary.view(torch.int16).fill_(0x5A5A)
+        if hog:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(4):
+                    hog_dst.copy_(hog_src)
+        fn(a, b_shuf, s_a, s_b, out=c)
+        torch.cuda.synchronize()
+        assert (canary.view(torch.int16) == 0x5A5A).all(), "write past the end of C"
+        outs.append(bf16_bits(c))
+    return outs
+
+
+@pytest.mark.parametrize("m,n,k,seed_a,seed_b", [(4096, 7168, 256, 11, 12), (16384, 7168, 512, 21, 22)])
+def test_race_shapes_bit_stable_and_correct(dmm, m, n, k, seed_a, seed_b):
+    """The pages' race shapes (mori PR 785, Test table): 20 launches into a
+    NaN-poisoned C must be bitwise identical, leave no NaN, and match the
+    oracle on sampled rows (every row of the first and last 256-row tiles
+    plus one per 64-row band)."""
+    announce("race", m, n, k)
+    qa, qb, sa, sb = quantised_operands("ptpc", m, n, k, seed_a, seed_b)
+    outs = run_poisoned(dmm, "ptpc", qa, qb, sa, sb, 20)
+    for i, o in enumerate(outs[1:], 1):
+        diff = np.count_nonzero(o != outs[0])
+        assert diff == 0, f"launch {i} differs from launch 0 in {diff} elements"
+    assert not np.isnan(bits_to_f64(outs[0])).any()
+    rows = inputs.rows_sample(m, seed=m)
+    ref = oracle.gemm_ptpc(qa, qb, sa, sb, rows=rows)
+    check_close(outs[0][rows], ref, f"ptpc {m}x{n}x{k} sampled rows", "ptpc", (qa, qb, sa, sb), rows)
+
+
+@pytest.mark.parametrize("mode", ["ptpc", "mxfp8", "blockscale"])
+def test_bit_stable_under_concurrent_copy(dmm, mode):
+    """Same 20-launch identity with an HBM copy loop on a second stream."""
+    m, n, k = 4096, 7168, 256
+    announce("hog", mode, m, n, k)
+    qa, qb, sa, sb = quantised_operands(mode, m, n, k, 11, 12)
+    outs = run_poisoned(dmm, mode, qa, qb, sa, sb, 20, hog=True)
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(o, outs[0]), f"launch {i} differs"
+    assert not np.isnan(bits_to_f64(outs[0])).any()
+
+
+def test_bf16_gemm(dmm):
+    m, k, n = GOLD["bf16_shape_mkn"]["value"]
+    announce("bf16", m, k, n)
+    a32, b_kn = inputs.bf16_operands(m, k, n, GOLD["bf16_seed"]["value"])
+    a = torch.from_numpy(a32).to(torch.bfloat16)
+    b = torch.from_numpy(np.ascontiguousarray(b_kn.T)).to(torch.bfloat16)  # [N, K]
+    c = dmm.gemm_bf16(a.to(DEV), b.to(DEV))
+    ref = oracle.gemm_bf16(a.view(torch.int16).numpy().view(np.uint16), b.view(torch.int16).numpy().view(np.uint16))
+    check_close(bf16_bits(c), ref, "bf16 4096x1024x896")
+    outs = [bf16_bits(dmm.gemm_bf16(a.to(DEV), b.to(DEV))) for _ in range(20)]
+    assert all(np.array_equal(o, outs[0]) for o in outs)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 64), (200, 272, 192), (129, 144, 1024)])
+def test_bf16_gemm_edges(dmm, m, n, k):
+    announce("bf16 edge", m, n, k)
+    vals = np.array([0, 1, -1, 2, -2, 0.5], np.float32)
+    a = torch.from_numpy(inputs.choice((m, k), vals, m)).to(torch.bfloat16)
+    b = torch.from_numpy(inputs.choice((n, k), vals, n)).to(torch.bfloat16)
+    c = dmm.gemm_bf16(a.to(DEV), b.to(DEV))
+    ref = oracle.gemm_bf16(a.view(torch.int16).numpy().view(np.uint16), b.view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(bf16_bits(c), ref)
+
+
+def test_invalid_arguments_raise_value_error(dmm):
+    a = torch.zeros((64, 256), dtype=torch.uint8, device=DEV)
+    b = torch.zeros((24, 256), dtype=torch.uint8, device=DEV)  # N not a multiple of 16
+    s = torch.ones(64, dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):
+        dmm.gemm_a8w8_ptpc(a, b, s, torch.ones(24, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        dmm.gemm_a8w8_ptpc(a[:, :200].contiguous(), b[:16, :200].contiguous(), s,
+                           torch.ones(16, dtype=torch.float32, device=DEV))

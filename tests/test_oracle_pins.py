@@ -342,3 +342,23 @@ def test_gemm_bf16_exact_and_bounded(orc):
     bound = K * u / (1 - K * u) * (np.abs(bf16_to_f64(a)) @ np.abs(bf16_to_f64(b)).T)
     assert np.all(np.abs(got32 - exact) <= bound)
     assert np.array_equal(got, t_bf16(got32))
+
+
+# ------------------------------------------------- the acceptance rule
+def test_tolerance_accepts_a_reordered_sum_and_rejects_a_missing_k_tile(orc):
+    """The GPU acceptance rule passes a correct result summed in another
+    order (numpy BLAS) and fails one that drops a single 128-wide K tile --
+    the corruption the pages describe (a band one K tile off)."""
+    from oracle import tolerance
+
+    M, N, K = 256, 512, 1024
+    qa, sa = orc.quantize_rows(inputs.normal((M, K), 70))
+    qb, sb = orc.quantize_rows(inputs.normal((N, K), 71))
+    ref = orc.gemm_ptpc(qa, qb, sa, sb)
+    blas = (t_dec_e4m3(qa) * sa[:, None]) @ (t_dec_e4m3(qb) * sb[:, None]).T
+    tolerance.check(t_bf16(blas), ref, "reordered", "ptpc", (qa, qb, sa, sb))
+    qa_bad = qa.copy()
+    qa_bad[16:48, 384:512] = 0  # a 32-row band misses K tile 3
+    bad = orc.gemm_ptpc(qa_bad, qb, sa, sb)
+    with pytest.raises(AssertionError):
+        tolerance.check(bad, ref, "one tile off", "ptpc", (qa, qb, sa, sb))

@@ -22,6 +22,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Direct global -> LDS load of 16 bytes per lane through a buffer
+// descriptor: lane l writes lds + 16 l (lds must be wave-uniform).  The host
+// compilation pass cannot type-check this builtin inside device function
+// templates, so the call exists in the device pass only; the host pass never
+// executes device code.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voffset, 0, 0, 0);
+#else
+    (void)r;
+    (void)lds;
+    (void)voffset;
+#endif
+}
+
 // s_waitcnt immediate for the gfx9 encoding: vmcnt in bits [3:0] and
 // [15:14], expcnt [6:4], lgkmcnt [11:8]; fields set to their maximum do not
 // wait.

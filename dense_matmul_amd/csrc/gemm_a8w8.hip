@@ -5,33 +5,39 @@
 //
 //   C[m, n] = bf16( sum_k A[m, k] sa(m, k) * B[n, k] sb(n, k) ),  fp32 accumulate
 //
-// Structure (one 256-thread workgroup = 4 waves per output tile):
+// Structure (persistent: one 256-thread workgroup = 4 waves per CU, each
+// walking its list of output tiles as one continuous stream of K tiles, so
+// the loads of the next tile overlap the end of the current one and its
+// stores):
 //   * Output tile 16*MB x 256 (MB = 16 for ptpc / mxfp8, 8 for blockscale).
 //     Wave w owns all tile rows and the 64 columns [64w, 64w + 64).
 //   * A (row-major codes) streams global -> LDS with direct-to-LDS buffer
 //     loads (16 B per lane) through a 4-stage ring of separate LDS arrays,
-//     refilled three K tiles ahead.  Rows are stored 128 B apart with the
-//     16-byte chunks XOR-swizzled by (row / MB) & 7 so that fragment reads
-//     are bank-conflict free.
+//     refilled three K tiles ahead.  Rows sit 128 B apart; the 16-byte
+//     chunks are XOR-swizzled by (row / MB) & 7 and rows 128..255 swap slot
+//     parity, so a fragment read by 16 lanes touches all 64 banks once.
 //   * B comes pre-shuffled (preshuffle_b) into the matrix-core operand order,
 //     so every wave loads its fragments straight into registers with fully
 //     coalesced 1 KiB loads, one K tile ahead (register double buffer).
 //   * v_mfma_scale_f32_16x16x128_f8f6f4: src0 = 16 B rows (output columns),
-//     src1 = 16 A rows (output rows).  Lane l holds row l%16 and, in bytes
+//     src1 = 16 A rows (output rows).  Lane l holds row l % 16 and, in bytes
 //     0-15 / 16-31, K values 16(l/16)+[0,16) / 64+16(l/16)+[0,16) of the
-//     128-wide K tile; the result lane l holds C rows for column... see
-//     store_tile.  mxfp8 passes the E8M0 scales to the instruction (lane
-//     16q + i carries the scale of row i, K group q); ptpc applies both
-//     scales in the epilogue; blockscale folds one scale per 128-K tile into
-//     fp32 accumulators in VGPRs.
+//     128-wide K tile (the instruction's operand layout on gfx950).  mxfp8
+//     passes the E8M0 scales to the instruction (lane 16q + i carries the
+//     scale of row i, K group q); ptpc applies both scales in the epilogue;
+//     blockscale folds one scale per 128-K tile into fp32 accumulators.
 //   * Every LDS read of a K tile follows "s_waitcnt vmcnt(c) lgkmcnt(0);
 //     s_barrier" where c comes from kpipe.h and covers that tile's DMA in
-//     every wave.  Every step issues its loads unconditionally (tiles past
-//     the end go through a zero-length buffer descriptor), so the counts are
-//     constants and the tail -- the last three K tiles, all of K = 256 --
-//     runs the same waits as the middle of the loop.
+//     every wave.  Every step issues its loads unconditionally (positions
+//     past the end go through a zero-length buffer descriptor), so the
+//     counts never depend on K: the tail, K = 256 and K = 128 run the same
+//     rule as the middle of a long K loop.
+//   * Epilogue: permlane16 swaps give each lane 8 consecutive columns, so
+//     the bf16 tile leaves in 16-byte stores; rows past M fall outside the
+//     C descriptor, 16-column blocks past N are masked.
 #include "common.h"
 #include "kpipe.h"
+#include "lds_layout.h"
 
 #include <type_traits>
 
@@ -48,14 +54,17 @@ __shared__ __attribute__((aligned(1024))) char g_lds_a0[kMaxStageBytes];
 __shared__ __attribute__((aligned(1024))) char g_lds_a1[kMaxStageBytes];
 __shared__ __attribute__((aligned(1024))) char g_lds_a2[kMaxStageBytes];
 __shared__ __attribute__((aligned(1024))) char g_lds_a3[kMaxStageBytes];
+// ptpc epilogue scales: per wave 1 KiB of a_scale (the tile's 256 rows) and
+// 1 KiB of b_scale (the tile's 256 columns)
+__shared__ __attribute__((aligned(1024))) char g_lds_scale[4 * 2048];
 
-template <int S>
-__device__ __forceinline__ char* stage_ptr() {
-    if constexpr (S == 0) return g_lds_a0;
-    else if constexpr (S == 1) return g_lds_a1;
-    else if constexpr (S == 2) return g_lds_a2;
-    else return g_lds_a3;
-}
+// The kernel body takes the four stage addresses and carries them in its
+// context (the host compilation pass only accepts references to the LDS
+// arrays there); after inlining they are constants again.
+struct Stages {
+    char* p[4];
+    char* scale;
+};
 
 template <int I, int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -82,19 +91,37 @@ struct Cfg {
     static constexpr int NA = MB / 2;                             // DMA instructions per wave per K tile
     // vector-memory instructions of one B event: 8 fragment loads plus scales
     static constexpr int NB = MODE == MODE_PTPC ? 8 : MODE == MODE_MXFP8 ? 8 + 2 + 4 : 8 + MB + 1;
+    // vector-memory instructions of the ptpc epilogue's scale loads (two
+    // 1 KiB DMAs per wave)
+    static constexpr int NSC = MODE == MODE_PTPC ? 2 : 0;
     static_assert(2 * NB + NA <= 63, "vmcnt range");
 };
 
-// Workgroup -> output tile.  The dispatcher hands consecutive workgroups to
-// the 8 XCDs in turn, so workgroup w runs on XCD w % 8; each XCD is given a
-// contiguous range of the tile order, which walks GROUP row tiles across all
-// column tiles so that concurrently running tiles share A and B in that
-// XCD's L2.
-__device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
+// Per-workgroup tile list of the persistent grid.  Workgroup w runs on XCD
+// w % 8 (the dispatcher deals workgroups to the XCDs in turn); the XCD owns a
+// contiguous range of the tile order and its workgroups stride through it, so
+// the tiles in flight on one XCD at any time are neighbours in that order.
+struct TileList {
+    int start, count, slot, slots;  // XCD range, this workgroup's slot, slots on the XCD
+    __device__ __forceinline__ int ntiles() const { return slot < count ? (count - slot + slots - 1) / slots : 0; }
+    __device__ __forceinline__ int tile(int j) const { return start + slot + j * slots; }
+};
+
+__device__ __forceinline__ TileList tile_list(int wg, int grid, int T) {
+    TileList L;
+    const int x = wg & 7, per = T >> 3, rem = T & 7;
+    L.start = x * per + (x < rem ? x : rem);
+    L.count = per + (x < rem ? 1 : 0);
+    L.slot = wg >> 3;
+    L.slots = (grid - x + 7) >> 3;
+    return L;
+}
+
+// Linear tile index -> (row tile, column tile): GROUP row tiles sweep all
+// column tiles, so the tiles an XCD runs together share A rows and B columns
+// in its L2.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
     constexpr int GROUP = 4;
-    const int T = tiles_m * tiles_n;
-    const int x = wg & 7, s = wg >> 3, per = T >> 3, rem = T & 7;
-    const int t = x * per + (x < rem ? x : rem) + s;
     const int group = t / (GROUP * tiles_n);
     const int first = group * GROUP;
     const int gsize = tiles_m - first < GROUP ? tiles_m - first : GROUP;
@@ -106,82 +133,136 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& t
 template <int MODE>
 struct Ctx {
     using C = Cfg<MODE>;
-    // buffer descriptors are built at each use from (base, bytes) in SGPRs
-    const void *pa, *pb, *psa, *psb;
-    uint32_t na, nb, nsa, nsb;
-    int KI, M, N, K, m0, n0, w, lane, i, g;
-    int dma_lds;                   // byte offset of this wave's DMA slots in a stage
-    int voff_a[C::NA];             // per-lane global byte offsets of the DMA rows
-    int voff_b[4];                 // per-lane global byte offsets of the B fragments
-    int rd0, rd1;                  // per-lane LDS byte offsets of the two 16-B halves
-    int voff_sa[Cfg<MODE>::MB];    // blockscale: per-row A scale offsets (row clamped to M-1)
-    int voff_sb;                   // B scale offset (mode dependent)
+    Stages lds;
+    const uint8_t* a;
+    const uint8_t* b;
+    const void* sa;
+    const void* sb;
+    uint16_t* c;
+    int M, N, K, KI, tiles_m, tiles_n;
+    TileList tl;
+    int ntiles;
+    int w, lane, i, g;
+    int dma_lds;        // byte offset of this wave's DMA slots in a stage
+    int voff_a[C::NA];  // per-lane byte offsets of the DMA rows, relative to the tile's first row
+    int voff_b[4];      // per-lane byte offsets of the B fragments, relative to the tile's first column
+    int rd[2][2];       // LDS byte offsets of the two 16-byte halves of an A fragment, for even / odd mb
     v4f acc[C::MB][4];
-    v8i bq[2][4];                  // B fragments, double buffered across K tiles
-    v8i pre[2];                    // first two A fragments of the next K tile
-    // mxfp8: E8M0 bytes for A (16 rows, 4 words + spill word) and B (4 columns)
+    v8i bq[2][4];       // B fragments, double buffered across K tiles
+    v8i pre[2];         // first two A fragments of the next K tile
+    // mxfp8: E8M0 bytes for A (a 16-byte window plus one word to realign) and B (one per block)
     v4i sxa[2];
     int sxa_tail[2];
+    int sxa_shift[2];
     int sxb[2][4];
     // blockscale: A scales of this lane's MB rows and the wave's B block scale
     v4f sfa[2][C::MB / 4];
     float sfb[2];
+
+    // (m0, n0) of this workgroup's tile j; m0 < 0 when j is past the list
+    __device__ __forceinline__ void origin(int j, int& m0, int& n0) const {
+        if (j >= ntiles) {
+            m0 = -1;
+            n0 = -1;
+            return;
+        }
+        int tm, tn;
+        tile_coords(tl.tile(j), tiles_m, tiles_n, tm, tn);
+        m0 = tm * C::BM;
+        n0 = tn * BN;
+    }
+};
+
+// Stream position of a load: tile j + dj of the list, K tile kt.
+struct Pos {
+    int m0, n0, kt;  // m0 < 0: past the end (zero-length descriptors)
 };
 
 // ---------------------------------------------------------------- issue
+// B event of one K tile: the B fragments (8 x 1 KiB loads per wave) plus
+// the per-K-tile scales of the mode.  Past the end of the stream every load
+// goes through a zero-length descriptor: no data moves, the instructions
+// still count in vmcnt.
 template <int MODE, int T>
-__device__ __forceinline__ void issue_b(Ctx<MODE>& x, int kt, bool valid) {
+__device__ __forceinline__ void issue_b(Ctx<MODE>& x, const Pos& p) {
     using C = Cfg<MODE>;
-    // a tile past the end is loaded through zero-length descriptors: no data
-    // moves, but the instructions still count in vmcnt
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.pb, valid ? x.nb : 0u);
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x.psa, valid ? x.nsa : 0u);
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(x.psb, valid ? x.nsb : 0u);
-    // B fragments: 2 KiB per (16-column block, K tile), lane l at byte 16 l
-    // of each 1 KiB half.
+    const bool valid = p.m0 >= 0;
+    const int n0 = valid ? p.n0 : 0, m0 = valid ? p.m0 : 0;
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(x.b + (size_t)(n0 / 16) * x.KI * 2048, valid ? (uint32_t)(x.N - n0) * (uint32_t)x.K : 0u);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-        v4i lo = __builtin_amdgcn_raw_buffer_load_b128(rb, x.voff_b[nb] + kt * 2048, 0, 0);
-        v4i hi = __builtin_amdgcn_raw_buffer_load_b128(rb, x.voff_b[nb] + kt * 2048 + 1024, 0, 0);
+        const int off = x.voff_b[nb] + p.kt * 2048;
+        v4i lo = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+        v4i hi = __builtin_amdgcn_raw_buffer_load_b128(rb, off + 1024, 0, 0);
         x.bq[T][nb] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
     if constexpr (MODE == MODE_MXFP8) {
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x.sa, valid ? (uint32_t)(x.K / 32) * (uint32_t)x.M : 0u);
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(x.sb, valid ? (uint32_t)(x.K / 32) * (uint32_t)x.N : 0u);
         // A: 16 consecutive E8M0 bytes (rows 16i .. 16i+15 of the tile) of K
         // group 4kt + g; the row stride M need not be a multiple of 4, so
-        // load the dword-aligned window and realign in registers.
-        const int off = (4 * kt + x.g) * x.M + x.m0 + 16 * x.i;
+        // load the dword-aligned window and realign in registers
+        const int off = (4 * p.kt + x.g) * x.M + m0 + 16 * x.i;
         const int base = off & ~3;
         x.sxa[T] = __builtin_amdgcn_raw_buffer_load_b128(rsa, base, 0, 0);
         x.sxa_tail[T] = __builtin_amdgcn_raw_buffer_load_b32(rsa, base + 16, 0, 0);
+        x.sxa_shift[T] = off & 3;
         // B: the byte of column 16 nb + i of the wave's 64, K group 4kt + g
+        const int boff = (4 * p.kt + x.g) * x.N + n0 + 64 * x.w + x.i;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-            x.sxb[T][nb] = __builtin_amdgcn_raw_buffer_load_b8(rsb, x.voff_sb + (4 * kt) * x.N + nb * 16, 0, 0);
+        for (int nb = 0; nb < 4; ++nb) x.sxb[T][nb] = __builtin_amdgcn_raw_buffer_load_b8(rsb, boff + 16 * nb, 0, 0);
     } else if constexpr (MODE == MODE_BLOCKSCALE) {
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x.sa, valid ? (uint32_t)x.KI * (uint32_t)x.M * 4u : 0u);
+        const __amdgpu_buffer_rsrc_t rsb =
+            make_rsrc(x.sb, valid ? (uint32_t)((x.N + 127) / 128) * (uint32_t)x.KI * 4u : 0u);
         // one dword per row; rows past M read row M-1 (their output is dropped)
 #pragma unroll
-        for (int r = 0; r < C::MB; ++r)
-            x.sfa[T][r / 4][r % 4] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(rsa, x.voff_sa[r] + kt * x.M * 4, 0, 0));
-        x.sfb[T] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsb, x.voff_sb + kt * 4, 0, 0));
+        for (int r = 0; r < C::MB; ++r) {
+            const int row = min(m0 + C::MB * x.i + r, x.M - 1);
+            x.sfa[T][r / 4][r % 4] =
+                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, (p.kt * x.M + row) * 4, 0, 0));
+        }
+        x.sfb[T] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rsb, (((n0 + 64 * x.w) / 128) * x.KI + p.kt) * 4, 0, 0));
     }
 }
 
+// ptpc epilogue scales of the tile at (m0, n0): NSC = 2 DMAs per wave into
+// the wave's own 2 KiB of g_lds_scale (a_scale of rows m0 .. m0+255, then
+// b_scale of columns n0 .. n0+255; entries past M or N read as zero).
 template <int MODE>
-__device__ __forceinline__ void dma_a_tile(Ctx<MODE>& x, char* stage, int kt, bool valid) {
+__device__ __forceinline__ void issue_epilogue_scales(Ctx<MODE>& x, int m0, int n0) {
+    if constexpr (MODE == MODE_PTPC) {
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc((const float*)x.sa + m0, (uint32_t)(x.M - m0) * 4u);
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc((const float*)x.sb + n0, (uint32_t)(x.N - n0) * 4u);
+        char* dst = x.lds.scale + x.w * 2048;
+        lds_dma16(rsa, dst, 16 * x.lane);
+        lds_dma16(rsb, dst + 1024, 16 * x.lane);
+    }
+}
+
+// Global -> LDS DMA of one A K tile (NA instructions per wave).  The tile's
+// rows start at m0; the descriptor covers rows m0 .. M-1 only, so rows past M
+// read as zero.
+template <int MODE>
+__device__ __forceinline__ void issue_a(Ctx<MODE>& x, char* stage, const Pos& p) {
     using C = Cfg<MODE>;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.pa, valid ? x.na : 0u);
+    const bool valid = p.m0 >= 0;
+    const int m0 = valid ? p.m0 : 0;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(x.a + (size_t)m0 * x.K, valid ? (uint32_t)(x.M - m0) * (uint32_t)x.K : 0u);
     char* dst = stage + x.dma_lds;
 #pragma unroll
     for (int j = 0; j < C::NA; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + j * 1024), 16, x.voff_a[j] + kt * BK, 0, 0, 0);
+        lds_dma16(ra, dst + j * 1024, x.voff_a[j] + p.kt * BK);
 }
 
 template <int MODE, int S>
 __device__ __forceinline__ v8i read_a(const Ctx<MODE>& x, int mb) {
-    const char* st = stage_ptr<S>();
-    v4i lo = *(const v4i*)(st + x.rd0 + mb * 128);
-    v4i hi = *(const v4i*)(st + x.rd1 + mb * 128);
+    const char* st = x.lds.p[S];
+    v4i lo = *(const v4i*)(st + x.rd[mb & 1][0] + mb * 128);
+    v4i hi = *(const v4i*)(st + x.rd[mb & 1][1] + mb * 128);
     return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -193,14 +274,17 @@ __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
         for (int nb = 0; nb < 4; ++nb)
             x.acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x.bq[T][nb], a, x.acc[mb][nb], 0, 0, 0, 0, 0, 0);
     } else if constexpr (MODE == MODE_MXFP8) {
-        // src1 (A) scale: byte mb % 4 of word mb / 4 of the realigned bytes
+        // src1 (A) scale: byte mb % 4 of word mb / 4 of the realigned bytes;
+        // src0 (B) scale: byte 0 of the block's own register
         const int sa_word = x.sxa[T][mb / 4];
         static_for<0, 4>([&](auto NBc) {
             constexpr int nb = decltype(NBc)::value;
-            x.acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                x.bq[T][nb], a, x.acc[mb][nb], 0, 0, 0, x.sxb[T][nb], mb % 4, sa_word);
+            x.acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x.bq[T][nb], a, x.acc[mb][nb], 0, 0, 0,
+                                                                            x.sxb[T][nb], mb % 4, sa_word);
         });
     } else {
+        // blockscale: one fp32 scale per (row, 128-wide K tile) times the
+        // B block's scale, applied to the tile's partial sum
         const float s = x.sfa[T][mb / 4][mb % 4] * x.sfb[T];
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -213,40 +297,94 @@ __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
 
 // Realign the 20 loaded E8M0 bytes so word q holds the bytes of rows 4q..4q+3.
 template <int MODE, int T>
-__device__ __forceinline__ void realign_mx(Ctx<MODE>& x, int kt) {
+__device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
     if constexpr (MODE == MODE_MXFP8) {
-        const int off = (4 * kt + x.g) * x.M + x.m0 + 16 * x.i;
-        const int sh = off & 3;
+        const int sh = x.sxa_shift[T];
         if (sh) {
-            v4i w = x.sxa[T];
-            int t = x.sxa_tail[T];
+            const v4i w = x.sxa[T];
+            const int t = x.sxa_tail[T];
             // alignbyte(hi, lo, s) = bytes s..s+3 of the 64-bit hi:lo
             x.sxa[T] = (v4i){(int)__builtin_amdgcn_alignbyte(w[1], w[0], sh), (int)__builtin_amdgcn_alignbyte(w[2], w[1], sh),
-                              (int)__builtin_amdgcn_alignbyte(w[3], w[2], sh), (int)__builtin_amdgcn_alignbyte(t, w[3], sh)};
+                             (int)__builtin_amdgcn_alignbyte(w[3], w[2], sh), (int)__builtin_amdgcn_alignbyte(t, w[3], sh)};
         }
     }
-    (void)x;
-    (void)kt;
+}
+
+// ------------------------------------------------------------ epilogue
+// Result lane l, register v of block (mb, nb) holds row MB (l % 16) + mb,
+// column 64 w + 16 nb + 4 (l / 16) + v of the tile.  One permlane16 swap per
+// pair of blocks moves the data so that each lane holds 8 consecutive
+// columns; the 4 lanes of a row then write 64 contiguous bytes per store.
+template <int MODE>
+__device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
+    using C = Cfg<MODE>;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(x.c, (uint32_t)x.M * (uint32_t)x.N * 2u);
+    const int row0 = m0 + C::MB * x.i;
+    v4f eas[C::MB / 4], ebs[4];
+    if constexpr (MODE == MODE_PTPC) {
+        const char* sc = x.lds.scale + x.w * 2048;
+#pragma unroll
+        for (int q = 0; q < C::MB / 4; ++q) eas[q] = *(const v4f*)(sc + (C::MB * x.i + 4 * q) * 4);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) ebs[nb] = *(const v4f*)(sc + 1024 + (64 * x.w + 16 * nb + 4 * x.g) * 4);
+    }
+#pragma unroll
+    for (int pair = 0; pair < 2; ++pair) {
+        const int nb0 = 2 * pair, nb1 = 2 * pair + 1;
+        // after the swap: g=0 holds block nb0 columns 0-7, g=1 nb1 0-7,
+        // g=2 nb0 8-15, g=3 nb1 8-15
+        const int my_nb = (x.g & 1) ? nb1 : nb0;
+        const int col = n0 + 64 * x.w + 16 * my_nb + 8 * (x.g >> 1);
+        const bool col_ok = n0 + 64 * x.w + 16 * my_nb < x.N;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) {
+            v4f u = x.acc[mb][nb0], v = x.acc[mb][nb1];
+            if constexpr (MODE == MODE_PTPC) {
+                const float sa = eas[mb / 4][mb % 4];
+                u = u * sa * ebs[nb0];
+                v = v * sa * ebs[nb1];
+            }
+            const uint32_t u0 = pack_bf16(u[0], u[1]), u1 = pack_bf16(u[2], u[3]);
+            const uint32_t v0 = pack_bf16(v[0], v[1]), v1 = pack_bf16(v[2], v[3]);
+            const auto s0 = __builtin_amdgcn_permlane16_swap(u0, v0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(u1, v1, false, false);
+            const v4i data = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+            // rows at or past M fall outside the buffer and are dropped
+            if (col_ok) __builtin_amdgcn_raw_buffer_store_b128(data, rc, ((row0 + mb) * x.N + col) * 2, 0, 0);
+            // keep the scheduler from hoisting every accumulator read of the
+            // epilogue at once (the next tile's loads are live here)
+            if ((mb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
 }
 
 template <int MODE>
-__device__ __forceinline__ void wait_mid(int k) {
-    using C = Cfg<MODE>;
-    if (k == 0) wait_vm_lgkm0<sched::mid_wait(0, C::NA, C::NB)>();
-    else wait_vm_lgkm0<sched::mid_wait(1, C::NA, C::NB)>();
+__device__ __forceinline__ void zero_acc(Ctx<MODE>& x) {
+#pragma unroll
+    for (int mb = 0; mb < Cfg<MODE>::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) x.acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
 }
 
-// One K tile.  S = k % 4 selects the LDS stage, T = k % 2 the B registers.
-template <int MODE, int S>
-__device__ __forceinline__ void kstep(Ctx<MODE>& x, int k) {
+// ---------------------------------------------------------------- step
+// Stream step s = K tile k of tile j.  S = s % 4 is the LDS stage of the
+// tile, T = s % 2 the B register buffer.  FIRST / LAST: k == 0 / k == KI-1
+// (both for KI == 1).  cur/n1/n2: origins of tiles j, j+1, j+2, for loads
+// that run ahead into the next tiles.
+template <int MODE, int S, bool FIRST, bool LAST>
+__device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, int m0c, int n0c, int m01, int n01, int m02,
+                                      int n02) {
     using C = Cfg<MODE>;
     constexpr int T = S & 1;
     constexpr int SR = (S + 3) & 3;  // stage refilled by this step (tile k-1's)
-    constexpr int SN = (S + 1) & 3;  // stage of tile k+1
-    issue_b<MODE, T ^ 1>(x, k + 1, sched::b_valid(k, x.KI));
-    realign_mx<MODE, T>(x, k);
-    // first half of the row blocks; the first two A fragments were read at
-    // the end of the previous step
+    constexpr int SN = (S + 1) & 3;  // stage of the next K tile
+    constexpr int NA = C::NA, NB = C::NB, NSC = C::NSC;
+    const int KI = x.KI;
+    // B event of stream step s+1 (the next tile's first K tile after LAST)
+    if constexpr (LAST) issue_b<MODE, T ^ 1>(x, Pos{m01, n01, 0});
+    else issue_b<MODE, T ^ 1>(x, Pos{m0c, n0c, k + 1});
+    if constexpr (LAST) issue_epilogue_scales<MODE>(x, m0c, n0c);
+    realign_mx<MODE, T>(x);
     static_for<0, C::MB / 2>([&](auto MBc) {
         constexpr int mb = decltype(MBc)::value;
         v8i a;
@@ -254,166 +392,189 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int k) {
         else a = read_a<MODE, S>(x, mb);
         mfma_row<MODE, T, mb>(x, a);
     });
-    // RAW: K tile k+1 has landed in every wave's share of LDS.
-    // WAR: every wave's reads of stage SR (K tile k-1) have retired.
-    wait_mid<MODE>(k);
+    // RAW: K tile s+1 has landed in every wave's share of LDS.
+    // WAR: every wave's reads of stage SR (stream step s-1) have retired.
+    // The count is sched::wait_at(s, k, KI, ...), specialised: only the
+    // stream's very first step differs from the rest of its kind.
+    constexpr int XT = (LAST ? 1 : 0) + (FIRST ? 1 : 0);
+    if constexpr (FIRST) {
+        if (s == 0) wait_vm_lgkm0<sched::cap(sched::first_mid_wait(NA, NB) + (LAST ? NSC : 0))>();
+        else wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB) + XT * NSC)>();
+    } else {
+        wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB) + XT * NSC)>();
+    }
     __builtin_amdgcn_s_barrier();
     {
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.pa, sched::a_valid(k, x.KI) ? x.na : 0u);
-        char* dst = stage_ptr<SR>() + x.dma_lds;
-#pragma unroll
-        for (int j = 0; j < C::NA; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + j * 1024), 16, x.voff_a[j] + (k + 3) * BK,
-                                                     0, 0, 0);
+        // A DMA of stream step s+3: K tile k+3 of this tile or of the next two
+        const int kk = k + 3;
+        const bool in0 = kk < KI, in1 = kk < 2 * KI;
+        const Pos p{in0 ? m0c : (in1 ? m01 : m02), in0 ? n0c : (in1 ? n01 : n02), in0 ? kk : (in1 ? kk - KI : kk - 2 * KI)};
+        issue_a<MODE>(x, x.lds.p[SR], p);
     }
     static_for<C::MB / 2, C::MB>([&](auto MBc) {
         constexpr int mb = decltype(MBc)::value;
         v8i a = read_a<MODE, S>(x, mb);
         mfma_row<MODE, T, mb>(x, a);
     });
-    // prefetch the next tile's first fragments (covered by the barrier
-    // above; after the last tile the values are unused)
+    // the next K tile's first fragments (covered by the barrier above;
+    // after the last tile of the stream the values are unused)
     x.pre[0] = read_a<MODE, SN>(x, 0);
     x.pre[1] = read_a<MODE, SN>(x, 1);
 }
 
-// ------------------------------------------------------------ epilogue
-template <int MODE>
-__device__ __forceinline__ void store_tile(Ctx<MODE>& x, const GemmArgs& p) {
-    using C = Cfg<MODE>;
-    // result lane l, register v of block (mb, nb):
-    //   row    m0 + MB * (l % 16) + mb
-    //   column n0 + 64 w + 16 nb + 4 (l / 16) + v
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (uint32_t)p.m * (uint32_t)p.n * 2u);
-    v4f as[C::MB / 4];
-    v4f bs[4];
-    if constexpr (MODE == MODE_PTPC) {
-        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sa, (uint32_t)p.m * 4u);
-        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.sb, (uint32_t)p.n * 4u);
-#pragma unroll
-        for (int r = 0; r < C::MB; ++r) {
-            const int row = x.m0 + C::MB * x.i + r;
-            as[r / 4][r % 4] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(rsa, (row < x.M ? row : x.M - 1) * 4, 0, 0));
+// All K tiles of tile j, whose first K tile sits in stage P, then its
+// epilogue.  CASE = KI % 4 for KI >= 2, or 4 for KI == 1, is a compile-time
+// constant of the kernel: the first and last steps are peeled, the KI - 2
+// middle steps run as whole groups of four plus exactly (CASE - 2) & 3 more,
+// so every stage index and every wait count is a constant.
+template <int MODE, int P, int CASE>
+__device__ __forceinline__ void tile_body(Ctx<MODE>& x, int s0, int m0c, int n0c, int m01, int n01, int m02, int n02) {
+    const int KI = x.KI;
+    if constexpr (CASE == 4) {
+        kstep<MODE, P, true, true>(x, s0, 0, m0c, n0c, m01, n01, m02, n02);
+    } else {
+        constexpr int REM = (CASE - 2) & 3;  // (KI - 2) % 4
+        kstep<MODE, P, true, false>(x, s0, 0, m0c, n0c, m01, n01, m02, n02);
+        int k = 1;
+        for (; k + 4 <= KI - 1; k += 4) {
+            kstep<MODE, (P + 1) & 3, false, false>(x, s0 + k, k, m0c, n0c, m01, n01, m02, n02);
+            kstep<MODE, (P + 2) & 3, false, false>(x, s0 + k + 1, k + 1, m0c, n0c, m01, n01, m02, n02);
+            kstep<MODE, (P + 3) & 3, false, false>(x, s0 + k + 2, k + 2, m0c, n0c, m01, n01, m02, n02);
+            kstep<MODE, (P + 0) & 3, false, false>(x, s0 + k + 3, k + 3, m0c, n0c, m01, n01, m02, n02);
         }
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-            bs[nb] = __builtin_bit_cast(
-                v4f, __builtin_amdgcn_raw_buffer_load_b128(rsb, (x.n0 + 64 * x.w + 16 * nb + 4 * x.g) * 4, 0, 0));
+        if constexpr (REM >= 1) kstep<MODE, (P + 1) & 3, false, false>(x, s0 + k, k, m0c, n0c, m01, n01, m02, n02);
+        if constexpr (REM >= 2) kstep<MODE, (P + 2) & 3, false, false>(x, s0 + k + 1, k + 1, m0c, n0c, m01, n01, m02, n02);
+        if constexpr (REM >= 3) kstep<MODE, (P + 3) & 3, false, false>(x, s0 + k + 2, k + 2, m0c, n0c, m01, n01, m02, n02);
+        kstep<MODE, (P + CASE - 1) & 3, false, true>(x, s0 + KI - 1, KI - 1, m0c, n0c, m01, n01, m02, n02);
     }
-    const int row0 = x.m0 + C::MB * x.i;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int col = x.n0 + 64 * x.w + 16 * nb;
-        if (col >= x.N) continue;  // wave-uniform: the 16-column block is past N
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) {
-            v4f v = x.acc[mb][nb];
-            if constexpr (MODE == MODE_PTPC) v = v * as[mb / 4][mb % 4] * bs[nb];
-            v2i packed = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-            // rows at or past M fall outside the buffer and are dropped
-            __builtin_amdgcn_raw_buffer_store_b64(packed, rc, ((row0 + mb) * x.N + col + 4 * x.g) * 2, 0, 0);
-        }
-    }
+    store_tile<MODE>(x, m0c, n0c);
+    zero_acc<MODE>(x);
+}
+
+// Origins of tiles j, j+1, j+2 of the list, rotated as the stream advances.
+struct Ring {
+    int m0c, n0c, m01, n01, m02, n02;
+};
+
+template <int MODE, int P, int CASE>
+__device__ __forceinline__ void run_tile(Ctx<MODE>& x, int j, Ring& g) {
+    tile_body<MODE, P, CASE>(x, j * x.KI, g.m0c, g.n0c, g.m01, g.n01, g.m02, g.n02);
+    int m03, n03;
+    x.origin(j + 3, m03, n03);
+    g = Ring{g.m01, g.n01, g.m02, g.n02, m03, n03};
 }
 
 // -------------------------------------------------------------- kernel
-template <int MODE>
+// CASE = (K / 128) % 4 (4 when K == 128): the LDS stage of a tile's first K
+// tile advances by KI % 4 from one tile to the next, so tiles come in
+// cycles of 1, 2 or 4 phases.
+template <int MODE, int CASE>
 __global__ void __launch_bounds__(NTHREADS, 1) gemm_a8w8_kernel(GemmArgs p) {
     using C = Cfg<MODE>;
     Ctx<MODE> x;
-    int tm, tn;
-    tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    x.lds = Stages{{g_lds_a0, g_lds_a1, g_lds_a2, g_lds_a3}, g_lds_scale};
+    x.a = p.a;
+    x.b = p.b;
+    x.sa = p.sa;
+    x.sb = p.sb;
+    x.c = p.c;
     x.M = p.m;
     x.N = p.n;
     x.K = p.k;
     x.KI = p.k / BK;
-    x.m0 = tm * C::BM;
-    x.n0 = tn * BN;
+    x.tiles_m = p.tiles_m;
+    x.tiles_n = p.tiles_n;
+    x.tl = tile_list(blockIdx.x, gridDim.x, p.tiles_m * p.tiles_n);
+    x.ntiles = x.tl.ntiles();
+    if (x.ntiles == 0) return;
     x.w = wave_id();
     x.lane = lane_id();
     x.i = x.lane & 15;
     x.g = x.lane >> 4;
-    x.pa = p.a;
-    x.na = (uint32_t)p.m * (uint32_t)p.k;
-    x.pb = p.b;
-    x.nb = (uint32_t)p.n * (uint32_t)p.k;
-    x.psa = p.sa;
-    x.psb = p.sb;
-    x.nsa = x.nsb = 0;
 
-    // DMA: instruction j of wave w fills LDS rows 8 (NA w + j) .. +7, lane l
-    // writing bytes 16 (l % 8) of row 8 (NA w + j) + l / 8; it fetches the
-    // 16-byte chunk whose swizzled position that is.
-    x.dma_lds = x.w * C::NA * 1024;
+    // A tile placement in LDS (lds_layout.h): the DMA lane fetches the row
+    // and chunk that belong at the address it writes; a fragment read by 16
+    // lanes touches every one of the 64 banks once.
+    x.dma_lds = lds::dma_lds_byte(x.w, 0, 0, C::MB);
 #pragma unroll
-    for (int j = 0; j < C::NA; ++j) {
-        const int r = 8 * (C::NA * x.w + j) + (x.lane >> 3);
-        const int chunk = (x.lane & 7) ^ ((r / C::MB) & 7);
-        x.voff_a[j] = (x.m0 + r) * x.K + chunk * 16;
-    }
-    // A fragment of row block mb: lane (i, g) reads row MB i + mb, K chunks
-    // g (bytes 0-15) and 4 + g (bytes 16-31), each at its swizzled position.
-    x.rd0 = C::MB * x.i * 128 + ((x.g ^ (x.i & 7)) * 16);
-    x.rd1 = C::MB * x.i * 128 + (((4 + x.g) ^ (x.i & 7)) * 16);
-    // B fragments: 16-column block (n0 + 64 w) / 16 + nb, K tile kt at
-    // ((block * KI) + kt) * 2048; lane l reads 16 B at 16 l of each half.
+    for (int j = 0; j < C::NA; ++j)
+        x.voff_a[j] = lds::dma_row(x.w, j, x.lane, C::MB) * x.K + lds::dma_chunk(x.w, j, x.lane, C::MB) * 16;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) x.voff_b[nb] = (((x.n0 + 64 * x.w) / 16 + nb) * x.KI) * 2048 + 16 * x.lane;
-    if constexpr (MODE == MODE_MXFP8) {
-        x.nsa = (uint32_t)(x.K / 32) * (uint32_t)p.m;
-        x.nsb = (uint32_t)(x.K / 32) * (uint32_t)p.n;
-        x.voff_sb = x.g * x.N + x.n0 + 64 * x.w + x.i;
-    } else if constexpr (MODE == MODE_BLOCKSCALE) {
-        x.nsa = (uint32_t)x.KI * (uint32_t)p.m * 4u;
-        x.nsb = (uint32_t)((p.n + 127) / 128) * (uint32_t)x.KI * 4u;
+    for (int odd = 0; odd < 2; ++odd)
 #pragma unroll
-        for (int r = 0; r < C::MB; ++r) {
-            const int row = x.m0 + C::MB * x.i + r;
-            x.voff_sa[r] = (row < x.M ? row : x.M - 1) * 4;
-        }
-        x.voff_sb = ((x.n0 + 64 * x.w) / 128) * x.KI * 4;
-    }
+        for (int half = 0; half < 2; ++half) x.rd[odd][half] = lds::frag_base(x.i, x.g, odd, half, C::MB);
+    // B fragments: 16-column block 4 w + nb of the tile, K tile kt at
+    // (block * KI + kt) * 2048; lane l reads 16 bytes at 16 l of each half.
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) x.acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 4; ++nb) x.voff_b[nb] = ((4 * x.w + nb) * x.KI) * 2048 + 16 * x.lane;
+    zero_acc<MODE>(x);
 
-    // prologue: Bev(0), A(0), A(1), A(2)
-    issue_b<MODE, 0>(x, 0, true);
-    dma_a_tile<MODE>(x, stage_ptr<0>(), 0, true);
-    dma_a_tile<MODE>(x, stage_ptr<1>(), 1, 1 < x.KI);
-    dma_a_tile<MODE>(x, stage_ptr<2>(), 2, 2 < x.KI);
+    int m0c, n0c, m01, n01, m02, n02;
+    x.origin(0, m0c, n0c);
+    x.origin(1, m01, n01);
+    x.origin(2, m02, n02);
+
+    // prologue: Bev(0), A(0), A(1), A(2) of the stream
+    {
+        const int KI = x.KI;
+        issue_b<MODE, 0>(x, Pos{m0c, n0c, 0});
+        auto pos = [&](int sidx) {
+            if (sidx < KI) return Pos{m0c, n0c, sidx};
+            if (sidx < 2 * KI) return Pos{m01, n01, sidx - KI};
+            return Pos{m02, n02, sidx - 2 * KI};
+        };
+        issue_a<MODE>(x, x.lds.p[0], pos(0));
+        issue_a<MODE>(x, x.lds.p[1], pos(1));
+        issue_a<MODE>(x, x.lds.p[2], pos(2));
+    }
     wait_vm_lgkm0<sched::prologue_wait(C::NA)>();
     __builtin_amdgcn_s_barrier();
     x.pre[0] = read_a<MODE, 0>(x, 0);
     x.pre[1] = read_a<MODE, 0>(x, 1);
 
-    // K loop, unrolled by the 4 LDS stages: whole groups of four steps,
-    // then up to three guarded steps whose stages are again static.  Every
-    // step issues its loads unconditionally, so the compiler's own vmcnt
-    // tracking stays exact across the guards.
-    int k = 0;
-    for (; k + 4 <= x.KI; k += 4) {
-        kstep<MODE, 0>(x, k);
-        kstep<MODE, 1>(x, k + 1);
-        kstep<MODE, 2>(x, k + 2);
-        kstep<MODE, 3>(x, k + 3);
+    Ring g{m0c, n0c, m01, n01, m02, n02};
+    constexpr int R = CASE & 3;  // KI % 4
+    constexpr int CYCLE = R == 0 ? 1 : R == 2 ? 2 : 4;
+    for (int j = 0; j < x.ntiles; j += CYCLE) {
+        run_tile<MODE, 0, CASE>(x, j, g);
+        if constexpr (CYCLE >= 2) {
+            if (j + 1 < x.ntiles) run_tile<MODE, (R * 1) & 3, CASE>(x, j + 1, g);
+        }
+        if constexpr (CYCLE == 4) {
+            if (j + 2 < x.ntiles) run_tile<MODE, (R * 2) & 3, CASE>(x, j + 2, g);
+            if (j + 3 < x.ntiles) run_tile<MODE, (R * 3) & 3, CASE>(x, j + 3, g);
+        }
     }
-    if (k < x.KI) kstep<MODE, 0>(x, k);
-    if (k + 1 < x.KI) kstep<MODE, 1>(x, k + 1);
-    if (k + 2 < x.KI) kstep<MODE, 2>(x, k + 2);
-    store_tile<MODE>(x, p);
 }
 
 // -------------------------------------------------------------- launch
+static int device_cus() {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int MODE>
 static hipError_t launch_gemm(const GemmArgs& base, hipStream_t stream) {
     GemmArgs p = base;
     p.tiles_m = (p.m + Cfg<MODE>::BM - 1) / Cfg<MODE>::BM;
     p.tiles_n = (p.n + BN - 1) / BN;
     const int tiles = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL(gemm_a8w8_kernel<MODE>, dim3(tiles), dim3(NTHREADS), 0, stream, p);
+    const int grid = tiles < device_cus() ? tiles : device_cus();
+    const int ki = p.k / BK;
+    switch (ki == 1 ? 4 : ki & 3) {
+        case 4: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 4>), dim3(grid), dim3(NTHREADS), 0, stream, p); break;
+        case 0: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 0>), dim3(grid), dim3(NTHREADS), 0, stream, p); break;
+        case 1: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 1>), dim3(grid), dim3(NTHREADS), 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 2>), dim3(grid), dim3(NTHREADS), 0, stream, p); break;
+        default: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 3>), dim3(grid), dim3(NTHREADS), 0, stream, p); break;
+    }
     return hipGetLastError();
 }
 

@@ -8,50 +8,66 @@
 // LDS read that a barrier lets through before every wave's global->LDS copy of
 // that tile has landed.  Here each wait names exactly which copy it covers.
 //
-// Per wave, in issue order (KI = K / 128 tiles, NA / NB instructions):
+// A workgroup walks a stream of K tiles: all K tiles of its first output
+// tile, then all of the next, and so on (s = stream position, k = K tile
+// within the output tile, KI = K / 128).  Per wave, in issue order:
 //   prologue : Bev(0), A(0), A(1), A(2);
 //              wait vmcnt(prologue_wait) lgkmcnt(0); s_barrier
-//   step k   : top : Bev(k+1)
-//              mid : wait vmcnt(mid_wait(k)) lgkmcnt(0); s_barrier;
-//                    A(k+3) into LDS stage (k+3) % 4
-// A(j) is the global->LDS DMA of K tile j (NA instructions per wave), Bev(j)
-// the direct-to-register loads of tile j's B fragments plus any per-tile scale
-// loads (NB instructions per wave).  Every step issues both, always: a load
-// of a tile index >= KI goes through a zero-length buffer descriptor, so it
-// moves no data but still counts in vmcnt.  The counts therefore never depend
-// on K, and the tail -- including K = 256, where no step refills anything
-// real -- runs exactly the same waits as the middle of a long K loop.
+//   step s   : top : Bev(s+1) [, E if k == KI-1]
+//              mid : wait vmcnt(c(s)) lgkmcnt(0); s_barrier;
+//                    A(s+3) into LDS stage (s+3) % 4
+//              end : [stores of the output tile if k == KI-1]
+// A(j) is the global->LDS DMA of stream K tile j (NA loads per wave), Bev(j)
+// the direct-to-register loads of its B fragments plus any per-K-tile scales
+// (NB loads), E the ptpc epilogue's scale loads (NSC loads).  Every step
+// issues its loads unconditionally: a position past the end of the stream
+// goes through a zero-length buffer descriptor, moves no data and still
+// counts in vmcnt.  So the counts below depend only on where a step sits in
+// its output tile, never on K or on the stream's length: the peeled tail,
+// K = 256 (two steps per tile) and K = 128 (one) run the same rule.
 //
 // A wait vmcnt(c) leaves at most the c most recently issued vector-memory
-// instructions outstanding, and they complete in issue order, so the wait
-// covers a DMA exactly when c is at most the number of instructions issued
-// after it.  The functions return that number (the loosest count that still
-// covers the DMA); the barrier that follows extends the guarantee from this
-// wave's share of the tile to every wave's.  The lgkmcnt(0) before the same
-// barrier retires this wave's LDS reads of stage (k+3) % 4 (tile k-1) before
-// any wave refills it.
+// operations outstanding.  Loads complete in issue order, so a wait covers a
+// load exactly when c is at most the number of LOADS issued after it; stores
+// (the epilogue's) are left out of that number on purpose -- they only make
+// the counter larger, so a wait that ignores them is still sufficient even
+// if stores and loads complete out of order with respect to each other.
+// The functions return that number (the loosest count that still covers
+// the load), capped at the 6-bit field.  The barrier after the wait extends
+// the guarantee from this wave's share of the tile to every wave's; the
+// lgkmcnt(0) before the same barrier retires this wave's LDS reads of stage
+// (s+3) % 4 (K tile s-1) before any wave refills it.
 #pragma once
 
 namespace dmm {
 namespace sched {
 
 constexpr int kStages = 4;  // LDS stages of the A tile
+constexpr int kVmcntMax = 63;
+
+constexpr int cap(int c) { return c > kVmcntMax ? kVmcntMax : c; }
 
 // Prologue wait: covers A(0); A(1) and A(2) were issued after it.
 constexpr int prologue_wait(int NA) { return 2 * NA; }
 
-// Mid-step wait of step k: covers A(k+1).
-//   k == 0: A(1) is followed by A(2) and Bev(1).
-//   k >= 1: A(k+1) is followed by Bev(k), A(k+2) and Bev(k+1).
-constexpr int mid_wait(int k, int NA, int NB) { return k == 0 ? NA + NB : 2 * NB + NA; }
+// Mid-step wait of the stream's first step: A(1) is followed by A(2) and
+// Bev(1) (plus E if the first output tile has a single K tile).
+constexpr int first_mid_wait(int NA, int NB) { return NA + NB; }
 
-// Which issues of step k move real data (the rest are zero-length).
-constexpr bool b_valid(int k, int KI) { return k + 1 < KI; }
-constexpr bool a_valid(int k, int KI) { return k + 3 < KI; }
+// Mid-step wait of step s >= 1: A(s+1) (issued at step s-2, or in the
+// prologue for s = 1) is followed by Bev(s), A(s+2) and Bev(s+1), plus NSC
+// for each of steps s-1 and s that closed its output tile.
+constexpr int mid_wait(int NA, int NB) { return 2 * NB + NA; }
 
-// LDS stage holding K tile j, and the stage step k refills.
+// The full rule, as the kernel applies it.
+constexpr int wait_at(int s, int k, int KI, int NA, int NB, int NSC) {
+    const int extra = (k == KI - 1 ? 1 : 0) + (s > 0 && k == 0 ? 1 : 0);
+    return cap((s == 0 ? first_mid_wait(NA, NB) : mid_wait(NA, NB)) + extra * NSC);
+}
+
+// LDS stage holding stream K tile j, and the stage step s refills.
 constexpr int stage_of(int j) { return j % kStages; }
-constexpr int refill_stage(int k) { return (k + 3) % kStages; }
+constexpr int refill_stage(int s) { return (s + 3) % kStages; }
 
 }  // namespace sched
 }  // namespace dmm

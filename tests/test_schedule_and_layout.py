@@ -1,0 +1,252 @@
+"""CPU proofs for the fp8 GEMM's pipeline (no GPU).
+
+The kernel takes every wait count from ``kpipe.h`` and every LDS address from
+``lds_layout.h``; this test compiles those two headers into a host shim with
+g++ and checks, exhaustively over the shapes that matter:
+
+* the schedule: for every K-tile count KI in 1..40 and 1..5 output tiles per
+  workgroup, each LDS read of stream K tile j happens after a wait + barrier
+  that covers the DMA of tile j in every wave (RAW), each DMA into a stage
+  happens after a barrier that every wave passed only after its reads of the
+  stage's previous tile retired (WAR), and every count is exactly the number
+  of loads issued after the covered DMA (the loosest safe value, capped at
+  the 6-bit field).  This is the property the pages' tail fix restores
+  (mori PR 785, sections Problem and Fix): no LDS read of a K tile -- in the
+  main loop, the peeled tail, or a K = 256 tile with no main loop at all --
+  can run ahead of that tile's producers.
+* the layout: the DMA lanes together write every (row, chunk) of a stage
+  exactly once, each fragment read finds the (row, chunk) it needs, and each
+  16-lane read phase touches 16 distinct 16-byte bank groups (64 banks).
+The mutants at the end show the checker has teeth.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "dense_matmul_amd", "csrc")
+
+SHIM = r"""
+#include "kpipe.h"
+#include "lds_layout.h"
+using namespace dmm;
+extern "C" {
+int prologue_wait(int NA) { return sched::prologue_wait(NA); }
+int wait_at(int s, int k, int KI, int NA, int NB, int NSC) { return sched::wait_at(s, k, KI, NA, NB, NSC); }
+int stage_of(int j) { return sched::stage_of(j); }
+int refill_stage(int s) { return sched::refill_stage(s); }
+int dma_lds_byte(int w, int j, int l, int MB) { return lds::dma_lds_byte(w, j, l, MB); }
+int dma_row(int w, int j, int l, int MB) { return lds::dma_row(w, j, l, MB); }
+int dma_chunk(int w, int j, int l, int MB) { return lds::dma_chunk(w, j, l, MB); }
+int frag_byte(int i, int g, int mb, int half, int MB) { return lds::frag_byte(i, g, mb, half, MB); }
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def shim(tmp_path_factory):
+    d = tmp_path_factory.mktemp("shim")
+    src = d / "shim.cpp"
+    src.write_text(SHIM)
+    lib = d / "libshim.so"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-shared", "-fPIC", "-I", CSRC, str(src), "-o", str(lib)], check=True)
+    L = ctypes.CDLL(str(lib))
+    for f in ("prologue_wait", "wait_at", "stage_of", "refill_stage", "dma_lds_byte", "dma_row", "dma_chunk",
+              "frag_byte"):
+        getattr(L, f).restype = ctypes.c_int
+    return L
+
+
+# ---------------------------------------------------------------- schedule
+MODES = {"ptpc": (8, 8, 2), "mxfp8": (8, 14, 0), "blockscale": (4, 17, 0)}  # NA, NB, NSC per wave
+
+
+def program(L, KI, ntiles, NA, NB, NSC, wait_fn=None):
+    """One wave's event list for a workgroup stream, as the kernel issues it:
+    ("load", kind, index, n), ("store", n), ("wait", c), ("barrier",),
+    ("read", stream tile), ("read_done",) -- the same for every wave."""
+    wait_fn = wait_fn or (lambda s, k: L.wait_at(s, k, KI, NA, NB, NSC))
+    S = KI * ntiles
+    ev = [("load", "B", 0, NB), ("load", "A", 0, NA), ("load", "A", 1, NA), ("load", "A", 2, NA),
+          ("wait", L.prologue_wait(NA)), ("barrier",), ("read", 0)]
+    for s in range(S):
+        k = s % KI
+        ev.append(("load", "B", s + 1, NB))
+        if k == KI - 1 and NSC:
+            ev.append(("load", "E", s, NSC))
+        ev.append(("read", s))  # first half of the row blocks
+        ev.append(("wait", wait_fn(s, k)))
+        ev.append(("barrier",))
+        ev.append(("load", "A", s + 3, NA))
+        ev.append(("read", s))  # second half
+        ev.append(("read", s + 1))  # the next tile's first two fragments
+        if k == KI - 1:
+            ev.append(("store", 32))
+    return ev
+
+
+def check_program(ev, L):
+    """Returns a list of violations (empty when the schedule is proven).
+
+    Loads complete in issue order, so a wait vmcnt(c) completes every load
+    except the last c issued (stores are not counted: they can only delay a
+    wait).  All waves run the same program and pass a barrier only after
+    their own wait, so what one wave has completed at a barrier every wave
+    has; the lgkmcnt(0) in every wait retires the wave's LDS reads."""
+    bad = []
+    n_loads = 0
+    last_instr = {}  # A tile -> index of its last DMA instruction
+    complete_upto = 0  # loads with index < complete_upto are complete
+    covered = -1  # watermark at the latest barrier
+    unretired = set()  # tiles read since the latest barrier
+    for e in ev:
+        kind = e[0]
+        if kind == "load":
+            _, what, idx, n = e
+            if what == "A" and (idx - 4) in unretired:
+                bad.append(f"DMA of tile {idx} into stage {L.stage_of(idx)} while tile {idx - 4} may still be read")
+            n_loads += n
+            if what == "A":
+                last_instr[idx] = n_loads - 1
+        elif kind == "wait":
+            complete_upto = max(complete_upto, n_loads - e[1])
+        elif kind == "barrier":
+            covered = complete_upto
+            unretired.clear()
+        elif kind == "read":
+            t = e[1]
+            if t not in last_instr or last_instr[t] >= covered:
+                bad.append(f"read of tile {t} before a barrier covering its DMA in every wave")
+            unretired.add(t)
+    return bad
+
+
+def tight(L, KI, ntiles, NA, NB, NSC):
+    """Every wait count equals the number of loads issued after the covered
+    DMA (capped at 63): no count is stricter than it needs to be."""
+    ev = program(L, KI, ntiles, NA, NB, NSC)
+    issued, s = [], -1
+    out = []
+    for e in ev:
+        if e[0] == "load":
+            issued += [(e[1], e[2])] * e[3]
+        elif e[0] == "wait":
+            target = 0 if s < 0 else s + 1
+            last = max(p for p, x in enumerate(issued) if x == ("A", target))
+            after = len(issued) - 1 - last
+            out.append((e[1], min(after, 63)))
+        if e[0] == "barrier":
+            s += 1
+    return out
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_every_lds_read_is_covered(shim, mode):
+    NA, NB, NSC = MODES[mode]
+    for KI in range(1, 41):
+        for ntiles in range(1, 6):
+            bad = check_program(program(shim, KI, ntiles, NA, NB, NSC), shim)
+            assert not bad, f"{mode} KI={KI} tiles={ntiles}: {bad[:3]}"
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_counts_are_exact(shim, mode):
+    NA, NB, NSC = MODES[mode]
+    for KI in range(1, 21):
+        for ntiles in range(1, 4):
+            for got, want in tight(shim, KI, ntiles, NA, NB, NSC):
+                assert got == want, f"{mode} KI={KI} tiles={ntiles}: wait {got}, loads after target {want}"
+
+
+def test_k256_runs_the_tail_only_and_is_covered(shim):
+    """K = 256: two K tiles per output tile, no middle steps at all."""
+    NA, NB, NSC = MODES["ptpc"]
+    ev = program(shim, 2, 3, NA, NB, NSC)
+    assert check_program(ev, shim) == []
+
+
+def test_checker_catches_a_bare_barrier(shim):
+    """Mutant: the tail's wait replaced by vmcnt(63) -- the 'bare barrier'
+    of the pages -- must be flagged for K = 256 and for long K."""
+    NA, NB, NSC = MODES["ptpc"]
+    for KI in (2, 14):
+        def wf(s, k, KI=KI):
+            return 63 if k == KI - 1 else shim.wait_at(s, k, KI, NA, NB, NSC)
+        assert check_program(program(shim, KI, 2, NA, NB, NSC, wf), shim), KI
+
+
+def test_checker_catches_a_count_one_too_high(shim):
+    NA, NB, NSC = MODES["mxfp8"]
+    for KI in (2, 3, 14):
+        def wf(s, k, KI=KI):
+            return shim.wait_at(s, k, KI, NA, NB, NSC) + NA
+        assert check_program(program(shim, KI, 2, NA, NB, NSC, wf), shim), KI
+
+
+def test_checker_catches_a_missing_war_barrier(shim):
+    """Mutant: the DMA issued before the barrier instead of after it."""
+    NA, NB, NSC = MODES["ptpc"]
+    out = program(shim, 6, 1, NA, NB, NSC)
+    # move each step's DMA in front of its wait + barrier
+    mutated = []
+    i = 0
+    while i < len(out):
+        if out[i][0] == "wait" and i + 2 < len(out) and out[i + 2][0] == "load" and out[i + 2][1] == "A" \
+                and out[i + 1][0] == "barrier":
+            mutated += [out[i + 2], out[i], out[i + 1]]
+            i += 3
+        else:
+            mutated.append(out[i])
+            i += 1
+    assert check_program(mutated, shim)
+
+
+# ------------------------------------------------------------------ layout
+@pytest.mark.parametrize("MB", [16, 8])
+def test_dma_writes_every_row_chunk_once(shim, MB):
+    NA = MB // 2
+    seen = {}
+    for w in range(4):
+        for j in range(NA):
+            for l in range(64):
+                addr = shim.dma_lds_byte(w, j, l, MB)
+                assert addr % 16 == 0 and 0 <= addr < 16 * MB * 128
+                assert addr not in seen
+                seen[addr] = (shim.dma_row(w, j, l, MB), shim.dma_chunk(w, j, l, MB))
+    assert sorted(seen.values()) == [(r, c) for r in range(16 * MB) for c in range(8)]
+    # every lane group of 8 fetches one whole 128-byte row (coalesced)
+    for w in range(4):
+        for j in range(NA):
+            for q in range(8):
+                rows = {shim.dma_row(w, j, 8 * q + t, MB) for t in range(8)}
+                chunks = {shim.dma_chunk(w, j, 8 * q + t, MB) for t in range(8)}
+                assert len(rows) == 1 and chunks == set(range(8))
+
+
+@pytest.mark.parametrize("MB", [16, 8])
+def test_fragment_reads_find_their_data(shim, MB):
+    NA = MB // 2
+    where = {}
+    for w in range(4):
+        for j in range(NA):
+            for l in range(64):
+                where[shim.dma_lds_byte(w, j, l, MB)] = (shim.dma_row(w, j, l, MB), shim.dma_chunk(w, j, l, MB))
+    for l in range(64):
+        i, g = l % 16, l // 16
+        for mb in range(MB):
+            for half in (0, 1):
+                addr = shim.frag_byte(i, g, mb, half, MB)
+                assert where.get(addr) == (MB * i + mb, 4 * half + g), (MB, l, mb, half)
+
+
+@pytest.mark.parametrize("MB", [16, 8])
+def test_fragment_reads_are_bank_conflict_free(shim, MB):
+    """64 banks x 4 bytes: the 16 lanes of each read phase hit 16 distinct
+    16-byte bank groups."""
+    for mb in range(MB):
+        for half in (0, 1):
+            for phase in range(4):
+                groups = {(shim.frag_byte(l % 16, l // 16, mb, half, MB) // 16) % 16 for l in range(16 * phase, 16 * phase + 16)}
+                assert len(groups) == 16, (MB, mb, half, phase, sorted(groups))

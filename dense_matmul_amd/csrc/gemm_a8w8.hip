@@ -267,31 +267,72 @@ __device__ __forceinline__ v8i read_a(const Ctx<MODE>& x, int mb) {
 }
 
 // ------------------------------------------------------------- compute
-template <int MODE, int T, int mb>
+// The accumulators are pinned to AGPRs through inline asm: with all 256 of
+// them in the 256 accumulation registers, the allocator has no reason to
+// shuttle tuples through VGPRs.  Because the compiler cannot see that these
+// statements are matrix ops, the two hazards they create are handled here:
+// the first K tile of an output tile uses the zero-accumulator form (no
+// register writes precede it), and the epilogue waits out the pipeline
+// (mfma_drain) before it reads the results.
+template <bool ZERO>
+__device__ __forceinline__ void mfma_acc(v4f& acc, const v8i& b, const v8i& a) {
+    if constexpr (ZERO) asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=a"(acc) : "v"(b), "v"(a));
+    else asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
+template <bool ZERO, int OA, int OB>
+__device__ __forceinline__ void mfma_scaled_acc(v4f& acc, const v8i& b, const v8i& a, int sb, int sa) {
+    if constexpr (ZERO)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
+                     : "=a"(acc)
+                     : "v"(b), "v"(a), "v"(sb), "v"(sa), "n"(OA & 1), "n"(OB & 1), "n"(OA >> 1), "n"(OB >> 1));
+    else
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
+                     : "+a"(acc)
+                     : "v"(b), "v"(a), "v"(sb), "v"(sa), "n"(OA & 1), "n"(OB & 1), "n"(OA >> 1), "n"(OB >> 1));
+}
+
+template <int MODE, int T, int mb, bool FIRST>
 __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
     if constexpr (MODE == MODE_PTPC) {
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-            x.acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x.bq[T][nb], a, x.acc[mb][nb], 0, 0, 0, 0, 0, 0);
+        static_for<0, 4>([&](auto NBc) {
+            constexpr int nb = decltype(NBc)::value;
+            mfma_acc<FIRST>(x.acc[mb][nb], x.bq[T][nb], a);
+        });
     } else if constexpr (MODE == MODE_MXFP8) {
         // src1 (A) scale: byte mb % 4 of word mb / 4 of the realigned bytes;
         // src0 (B) scale: byte 0 of the block's own register
         const int sa_word = x.sxa[T][mb / 4];
         static_for<0, 4>([&](auto NBc) {
             constexpr int nb = decltype(NBc)::value;
-            x.acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x.bq[T][nb], a, x.acc[mb][nb], 0, 0, 0,
-                                                                            x.sxb[T][nb], mb % 4, sa_word);
+            mfma_scaled_acc<FIRST, 0, mb % 4>(x.acc[mb][nb], x.bq[T][nb], a, x.sxb[T][nb], sa_word);
         });
     } else {
         // blockscale: one fp32 scale per (row, 128-wide K tile) times the
-        // B block's scale, applied to the tile's partial sum
+        // B block's scale, applied to the tile's partial sum in VGPRs
         const float s = x.sfa[T][mb / 4][mb % 4] * x.sfb[T];
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
             v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x.bq[T][nb], a, zero, 0, 0, 0, 0, 0, 0);
-            x.acc[mb][nb] += p * s;
+            if constexpr (FIRST) x.acc[mb][nb] = p * s;
+            else x.acc[mb][nb] += p * s;
         }
+    }
+}
+
+// Before the epilogue reads accumulators written by the asm matrix ops:
+// 32 wait states cover the longest result latency of the 16x16x128 op, and
+// the empty asm statements (ordered after the wait like all volatile asm)
+// make every later read of an accumulator depend on it.
+template <int MODE>
+__device__ __forceinline__ void mfma_drain(Ctx<MODE>& x) {
+    if constexpr (MODE != MODE_BLOCKSCALE) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+        for (int mb = 0; mb < Cfg<MODE>::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) asm volatile("" : "+a"(x.acc[mb][nb]));
     }
 }
 
@@ -390,7 +431,7 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, int m0c, int n
         v8i a;
         if constexpr (mb < 2) a = x.pre[mb];
         else a = read_a<MODE, S>(x, mb);
-        mfma_row<MODE, T, mb>(x, a);
+        mfma_row<MODE, T, mb, FIRST>(x, a);
     });
     // RAW: K tile s+1 has landed in every wave's share of LDS.
     // WAR: every wave's reads of stage SR (stream step s-1) have retired.
@@ -414,7 +455,7 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, int m0c, int n
     static_for<C::MB / 2, C::MB>([&](auto MBc) {
         constexpr int mb = decltype(MBc)::value;
         v8i a = read_a<MODE, S>(x, mb);
-        mfma_row<MODE, T, mb>(x, a);
+        mfma_row<MODE, T, mb, FIRST>(x, a);
     });
     // the next K tile's first fragments (covered by the barrier above;
     // after the last tile of the stream the values are unused)
@@ -447,8 +488,8 @@ __device__ __forceinline__ void tile_body(Ctx<MODE>& x, int s0, int m0c, int n0c
         if constexpr (REM >= 3) kstep<MODE, (P + 3) & 3, false, false>(x, s0 + k + 2, k + 2, m0c, n0c, m01, n01, m02, n02);
         kstep<MODE, (P + CASE - 1) & 3, false, true>(x, s0 + KI - 1, KI - 1, m0c, n0c, m01, n01, m02, n02);
     }
+    mfma_drain<MODE>(x);
     store_tile<MODE>(x, m0c, n0c);
-    zero_acc<MODE>(x);
 }
 
 // Origins of tiles j, j+1, j+2 of the list, rotated as the stream advances.
@@ -507,7 +548,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_a8w8_kernel(GemmArgs p) {
     // (block * KI + kt) * 2048; lane l reads 16 bytes at 16 l of each half.
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) x.voff_b[nb] = ((4 * x.w + nb) * x.KI) * 2048 + 16 * x.lane;
-    zero_acc<MODE>(x);
 
     int m0c, n0c, m01, n01, m02, n02;
     x.origin(0, m0c, n0c);

@@ -13,6 +13,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
 
 // Raw buffer resource over [base, base + bytes).  Loads past the end return
 // zero and stores past the end are dropped, which is how the kernels mask
@@ -27,7 +28,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // compilation pass cannot type-check this builtin inside device function
 // templates, so the call exists in the device pass only; the host pass never
 // executes device code.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voffset) {
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_char* lds, int voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voffset, 0, 0, 0);
 #else

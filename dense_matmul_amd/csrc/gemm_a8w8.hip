@@ -62,8 +62,8 @@ __shared__ __attribute__((aligned(1024))) char g_lds_scale[4 * 2048];
 // context (the host compilation pass only accepts references to the LDS
 // arrays there); after inlining they are constants again.
 struct Stages {
-    char* p[4];
-    char* scale;
+    lds_char* p[4];
+    lds_char* scale;
 };
 
 template <int I, int N, class F>
@@ -236,7 +236,7 @@ __device__ __forceinline__ void issue_epilogue_scales(Ctx<MODE>& x, int m0, int 
     if constexpr (MODE == MODE_PTPC) {
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc((const float*)x.sa + m0, (uint32_t)(x.M - m0) * 4u);
         const __amdgpu_buffer_rsrc_t rsb = make_rsrc((const float*)x.sb + n0, (uint32_t)(x.N - n0) * 4u);
-        char* dst = x.lds.scale + x.w * 2048;
+        lds_char* dst = x.lds.scale + x.w * 2048;
         lds_dma16(rsa, dst, 16 * x.lane);
         lds_dma16(rsb, dst + 1024, 16 * x.lane);
     }
@@ -246,13 +246,13 @@ __device__ __forceinline__ void issue_epilogue_scales(Ctx<MODE>& x, int m0, int 
 // rows start at m0; the descriptor covers rows m0 .. M-1 only, so rows past M
 // read as zero.
 template <int MODE>
-__device__ __forceinline__ void issue_a(Ctx<MODE>& x, char* stage, const Pos& p) {
+__device__ __forceinline__ void issue_a(Ctx<MODE>& x, lds_char* stage, const Pos& p) {
     using C = Cfg<MODE>;
     const bool valid = p.m0 >= 0;
     const int m0 = valid ? p.m0 : 0;
     const __amdgpu_buffer_rsrc_t ra =
         make_rsrc(x.a + (size_t)m0 * x.K, valid ? (uint32_t)(x.M - m0) * (uint32_t)x.K : 0u);
-    char* dst = stage + x.dma_lds;
+    lds_char* dst = stage + x.dma_lds;
 #pragma unroll
     for (int j = 0; j < C::NA; ++j)
         lds_dma16(ra, dst + j * 1024, x.voff_a[j] + p.kt * BK);
@@ -260,9 +260,10 @@ __device__ __forceinline__ void issue_a(Ctx<MODE>& x, char* stage, const Pos& p)
 
 template <int MODE, int S>
 __device__ __forceinline__ v8i read_a(const Ctx<MODE>& x, int mb) {
-    const char* st = x.lds.p[S];
-    v4i lo = *(const v4i*)(st + x.rd[mb & 1][0] + mb * 128);
-    v4i hi = *(const v4i*)(st + x.rd[mb & 1][1] + mb * 128);
+    const lds_char* st = x.lds.p[S];
+    typedef __attribute__((address_space(3))) const v4i lds_v4i;
+    v4i lo = *(lds_v4i*)(st + x.rd[mb & 1][0] + mb * 128);
+    v4i hi = *(lds_v4i*)(st + x.rd[mb & 1][1] + mb * 128);
     return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -363,11 +364,12 @@ __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
     const int row0 = m0 + C::MB * x.i;
     v4f eas[C::MB / 4], ebs[4];
     if constexpr (MODE == MODE_PTPC) {
-        const char* sc = x.lds.scale + x.w * 2048;
+        typedef __attribute__((address_space(3))) const v4f lds_v4f;
+        const lds_char* sc = x.lds.scale + x.w * 2048;
 #pragma unroll
-        for (int q = 0; q < C::MB / 4; ++q) eas[q] = *(const v4f*)(sc + (C::MB * x.i + 4 * q) * 4);
+        for (int q = 0; q < C::MB / 4; ++q) eas[q] = *(lds_v4f*)(sc + (C::MB * x.i + 4 * q) * 4);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) ebs[nb] = *(const v4f*)(sc + 1024 + (64 * x.w + 16 * nb + 4 * x.g) * 4);
+        for (int nb = 0; nb < 4; ++nb) ebs[nb] = *(lds_v4f*)(sc + 1024 + (64 * x.w + 16 * nb + 4 * x.g) * 4);
     }
 #pragma unroll
     for (int pair = 0; pair < 2; ++pair) {
@@ -408,59 +410,84 @@ __device__ __forceinline__ void zero_acc(Ctx<MODE>& x) {
 }
 
 // ---------------------------------------------------------------- step
-// Stream step s = K tile k of tile j.  S = s % 4 is the LDS stage of the
-// tile, T = s % 2 the B register buffer.  FIRST / LAST: k == 0 / k == KI-1
-// (both for KI == 1).  cur/n1/n2: origins of tiles j, j+1, j+2, for loads
+// Where a stream step sits: s = stream position, k = K tile within its
+// output tile, and the origins of tiles j, j+1, j+2 (cur/n1/n2) for loads
 // that run ahead into the next tiles.
+struct Step {
+    int s, k, m0c, n0c, m01, n01, m02, n02;
+};
+
+// The middle of a step: wait + barrier, then the A DMA of stream step s+3
+// into stage SR.  RAW: K tile s+1 has landed in every wave's share of LDS.
+// WAR: every wave's reads of stage SR (stream step s-1) have retired.  The
+// count is sched::wait_at(s, k, KI, ...), specialised: only the stream's
+// very first step differs from the rest of its kind.
 template <int MODE, int S, bool FIRST, bool LAST>
-__device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, int m0c, int n0c, int m01, int n01, int m02,
-                                      int n02) {
+__device__ __forceinline__ void mid_step(Ctx<MODE>& x, Step t) {
     using C = Cfg<MODE>;
-    constexpr int T = S & 1;
-    constexpr int SR = (S + 3) & 3;  // stage refilled by this step (tile k-1's)
-    constexpr int SN = (S + 1) & 3;  // stage of the next K tile
+    constexpr int SR = (S + 3) & 3;
     constexpr int NA = C::NA, NB = C::NB, NSC = C::NSC;
-    const int KI = x.KI;
-    // B event of stream step s+1 (the next tile's first K tile after LAST)
-    if constexpr (LAST) issue_b<MODE, T ^ 1>(x, Pos{m01, n01, 0});
-    else issue_b<MODE, T ^ 1>(x, Pos{m0c, n0c, k + 1});
-    if constexpr (LAST) issue_epilogue_scales<MODE>(x, m0c, n0c);
-    realign_mx<MODE, T>(x);
-    static_for<0, C::MB / 2>([&](auto MBc) {
-        constexpr int mb = decltype(MBc)::value;
-        v8i a;
-        if constexpr (mb < 2) a = x.pre[mb];
-        else a = read_a<MODE, S>(x, mb);
-        mfma_row<MODE, T, mb, FIRST>(x, a);
-    });
-    // RAW: K tile s+1 has landed in every wave's share of LDS.
-    // WAR: every wave's reads of stage SR (stream step s-1) have retired.
-    // The count is sched::wait_at(s, k, KI, ...), specialised: only the
-    // stream's very first step differs from the rest of its kind.
     constexpr int XT = (LAST ? 1 : 0) + (FIRST ? 1 : 0);
     if constexpr (FIRST) {
-        if (s == 0) wait_vm_lgkm0<sched::cap(sched::first_mid_wait(NA, NB) + (LAST ? NSC : 0))>();
+        if (t.s == 0) wait_vm_lgkm0<sched::cap(sched::first_mid_wait(NA, NB) + (LAST ? NSC : 0))>();
         else wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB) + XT * NSC)>();
     } else {
         wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB) + XT * NSC)>();
     }
     __builtin_amdgcn_s_barrier();
-    {
-        // A DMA of stream step s+3: K tile k+3 of this tile or of the next two
-        const int kk = k + 3;
-        const bool in0 = kk < KI, in1 = kk < 2 * KI;
-        const Pos p{in0 ? m0c : (in1 ? m01 : m02), in0 ? n0c : (in1 ? n01 : n02), in0 ? kk : (in1 ? kk - KI : kk - 2 * KI)};
-        issue_a<MODE>(x, x.lds.p[SR], p);
+    // K tile k+3 of this tile or of one of the next two
+    const int KI = x.KI;
+    const int kk = t.k + 3;
+    const bool in0 = kk < KI, in1 = kk < 2 * KI;
+    const Pos p{in0 ? t.m0c : (in1 ? t.m01 : t.m02), in0 ? t.n0c : (in1 ? t.n01 : t.n02),
+                in0 ? kk : (in1 ? kk - KI : kk - 2 * KI)};
+    issue_a<MODE>(x, x.lds.p[SR], p);
+}
+
+// Row blocks mb .. MB-1 of a step.  A fragments run two row blocks ahead
+// through a three-deep register ring (f0, f1, f2 hold fragments = 0, 1, 2
+// mod 3): fragment mb + 2 is read while mb's matrix ops run.  Reads of this
+// step's stage S need no barrier (the previous step's covered its tile);
+// the next stage's first two fragments, read in the last two row blocks,
+// come after this step's barrier at mb = MB / 2.
+template <int MODE, int S, bool FIRST, bool LAST, int mb>
+__device__ __forceinline__ void step_rows(Ctx<MODE>& x, Step t, v8i& f0, v8i& f1, v8i& f2) {
+    using C = Cfg<MODE>;
+    if constexpr (mb < C::MB) {
+        constexpr int T = S & 1;
+        constexpr int SN = (S + 1) & 3;
+        constexpr int nxt = mb + 2;
+        if constexpr (mb == C::MB / 2) mid_step<MODE, S, FIRST, LAST>(x, t);
+        if constexpr (nxt < C::MB) {
+            v8i fr = read_a<MODE, S>(x, nxt);
+            if constexpr (nxt % 3 == 0) f0 = fr;
+            else if constexpr (nxt % 3 == 1) f1 = fr;
+            else f2 = fr;
+        } else {
+            x.pre[nxt - C::MB] = read_a<MODE, SN>(x, nxt - C::MB);
+        }
+        if constexpr (mb % 3 == 0) mfma_row<MODE, T, mb, FIRST>(x, f0);
+        else if constexpr (mb % 3 == 1) mfma_row<MODE, T, mb, FIRST>(x, f1);
+        else mfma_row<MODE, T, mb, FIRST>(x, f2);
+        step_rows<MODE, S, FIRST, LAST, mb + 1>(x, t, f0, f1, f2);
     }
-    static_for<C::MB / 2, C::MB>([&](auto MBc) {
-        constexpr int mb = decltype(MBc)::value;
-        v8i a = read_a<MODE, S>(x, mb);
-        mfma_row<MODE, T, mb, FIRST>(x, a);
-    });
-    // the next K tile's first fragments (covered by the barrier above;
-    // after the last tile of the stream the values are unused)
-    x.pre[0] = read_a<MODE, SN>(x, 0);
-    x.pre[1] = read_a<MODE, SN>(x, 1);
+}
+
+// Stream step s = K tile k of tile j.  S = s % 4 is the LDS stage of the
+// tile, T = s % 2 the B register buffer.  FIRST / LAST: k == 0 / k == KI-1
+// (both for KI == 1).
+template <int MODE, int S, bool FIRST, bool LAST>
+__device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, int m0c, int n0c, int m01, int n01, int m02,
+                                      int n02) {
+    constexpr int T = S & 1;
+    const Step t{s, k, m0c, n0c, m01, n01, m02, n02};
+    // B event of stream step s+1 (the next tile's first K tile after LAST)
+    if constexpr (LAST) issue_b<MODE, T ^ 1>(x, Pos{m01, n01, 0});
+    else issue_b<MODE, T ^ 1>(x, Pos{m0c, n0c, k + 1});
+    if constexpr (LAST) issue_epilogue_scales<MODE>(x, m0c, n0c);
+    realign_mx<MODE, T>(x);
+    v8i f0 = x.pre[0], f1 = x.pre[1], f2;
+    step_rows<MODE, S, FIRST, LAST, 0>(x, t, f0, f1, f2);
 }
 
 // All K tiles of tile j, whose first K tile sits in stage P, then its
@@ -513,7 +540,8 @@ template <int MODE, int CASE>
 __global__ void __launch_bounds__(NTHREADS, 1) gemm_a8w8_kernel(GemmArgs p) {
     using C = Cfg<MODE>;
     Ctx<MODE> x;
-    x.lds = Stages{{g_lds_a0, g_lds_a1, g_lds_a2, g_lds_a3}, g_lds_scale};
+    x.lds = Stages{{(lds_char*)g_lds_a0, (lds_char*)g_lds_a1, (lds_char*)g_lds_a2, (lds_char*)g_lds_a3},
+                   (lds_char*)g_lds_scale};
     x.a = p.a;
     x.b = p.b;
     x.sa = p.sa;

@@ -64,8 +64,8 @@ __device__ __forceinline__ void issue(Ctx& x, int kt) {
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.pb, valid ? x.nb : 0u);
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-        lds_dma16(ra, sa<S>() + x.dma_lds + j * 1024, x.voff_a[j] + kt * BK * 2);
-        lds_dma16(rb, sb<S>() + x.dma_lds + j * 1024, x.voff_b[j] + kt * BK * 2);
+        lds_dma16(ra, (lds_char*)(sa<S>() + x.dma_lds + j * 1024), x.voff_a[j] + kt * BK * 2);
+        lds_dma16(rb, (lds_char*)(sb<S>() + x.dma_lds + j * 1024), x.voff_b[j] + kt * BK * 2);
     }
 }
 

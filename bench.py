@@ -33,11 +33,14 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--extra", action="store_true", help="also time the other modes and shapes")
-    p.add_argument("--cpu-rows", type=int, default=1024, help="rows of the headline the oracle computes")
+    p.add_argument("--cpu-rows", type=int, default=16384, help="rows of the headline the oracle computes")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run a plain 1 GiB HBM copy kernel 3 times (the reference dispatch for "
+                        "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return p.parse_args()
 
 
@@ -78,17 +81,51 @@ def headline_operands(dmm, torch, m, n, k, seed_a, seed_b, mode="ptpc"):
     return qa, bs, sa, sb
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(torch):
+    """A plain elementwise copy (negation) of COPY_BYTES of fp32, read once
+    and written once, far larger than the last-level cache: its counters
+    give bytes-per-counted-byte for FETCH_SIZE and WRITE_SIZE."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+KERNEL_SOURCES = ("gemm_a8w8.hip", "common.h", "kpipe.h", "lds_layout.h")
+
+
+def kernel_source_hash():
+    """sha256 over the fp8 GEMM kernel's source files, to tell whether a
+    counter summary was taken for the kernel as it is now."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dense_matmul_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def traffic_from_profiles(kernel_tag):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if one
-    exists for the current kernel build (profiles/<tag>_traffic.json)."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    profiles/<tag>_traffic.json, or None when there is none or it was taken
+    for other kernel sources than the current ones."""
     path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         d = json.load(open(path))
-        return d.get("bytes_per_launch")
-    except Exception:
+    except (OSError, ValueError):
         return None
+    if d.get("source_sha256") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
 
 
 def cpu_baseline(m, n, k, rows_n):
@@ -104,7 +141,9 @@ def cpu_baseline(m, n, k, rows_n):
     qa, sa = oracle.quantize_per_token(a)
     qb, sb = oracle.quantize_per_token(b)
     rows = np.linspace(0, m - 1, rows_n).astype(np.int64)
-    threads = os.cpu_count() or 1
+    # every host thread of this process's CPU share (OMP_NUM_THREADS caps it
+    # where the machine's count is larger than the share)
+    threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "0")) or 1 << 30)
     t0 = time.perf_counter()
     oracle.gemm_ptpc(qa, qb, sa, sb, rows=rows, threads=threads)
     dt = time.perf_counter() - t0
@@ -124,6 +163,8 @@ def main():
     import dense_matmul_amd as dmm
 
     dmm.lib()
+    if args.copy_calibration:
+        copy_calibration(torch)
     m, n, k = 32768, 7168, 1792
     qa, bs, sa, sb = headline_operands(dmm, torch, m, n, k, 31, 32)
     out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")

@@ -364,12 +364,30 @@ __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
     const int row0 = m0 + C::MB * x.i;
     v4f eas[C::MB / 4], ebs[4];
     if constexpr (MODE == MODE_PTPC) {
-        typedef __attribute__((address_space(3))) const v4f lds_v4f;
-        const lds_char* sc = x.lds.scale + x.w * 2048;
-#pragma unroll
-        for (int q = 0; q < C::MB / 4; ++q) eas[q] = *(lds_v4f*)(sc + (C::MB * x.i + 4 * q) * 4);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) ebs[nb] = *(lds_v4f*)(sc + 1024 + (64 * x.w + 16 * nb + 4 * x.g) * 4);
+        // This wave's scale DMAs (issue_epilogue_scales, top of the last K
+        // step) were followed only by the NA A-tile DMAs of that step, so
+        // vmcnt(NA) covers them; each wave reads only the region it filled.
+        // The reads are written out so that the compiler, which cannot tell
+        // the A-tile DMAs still in flight from writes to this region, does
+        // not drain the whole prefetch pipeline (vmcnt(0)) before them.
+        static_assert(C::MB == 16, "ptpc epilogue reads four A-scale vectors");
+        wait_vm<C::NA>();
+        const uint32_t sc = (uint32_t)(uintptr_t)(x.lds.scale + x.w * 2048);
+        const uint32_t pa = sc + C::MB * x.i * 4, pb = sc + 1024 + (64 * x.w + 4 * x.g) * 4;
+        asm volatile(
+            "ds_read_b128 %0, %8\n"
+            "ds_read_b128 %1, %8 offset:16\n"
+            "ds_read_b128 %2, %8 offset:32\n"
+            "ds_read_b128 %3, %8 offset:48\n"
+            "ds_read_b128 %4, %9\n"
+            "ds_read_b128 %5, %9 offset:64\n"
+            "ds_read_b128 %6, %9 offset:128\n"
+            "ds_read_b128 %7, %9 offset:192\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(eas[0]), "=&v"(eas[1]), "=&v"(eas[2]), "=&v"(eas[3]), "=&v"(ebs[0]), "=&v"(ebs[1]),
+              "=&v"(ebs[2]), "=&v"(ebs[3])
+            : "v"(pa), "v"(pb)
+            : "memory");
     }
 #pragma unroll
     for (int pair = 0; pair < 2; ++pair) {

@@ -74,6 +74,11 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
+// Cache policy of the C stores: non-temporal (the aux bit that sets NT).  C is
+// written once and never re-read by the kernel; streaming it keeps the L2 and
+// last-level cache for the A and B panels that every tile re-reads.
+constexpr int kCacheStream = 2;
+
 struct GemmArgs {
     const uint8_t* a;
     const uint8_t* b;
@@ -130,6 +135,16 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
     tn = within / gsize;
 }
 
+// One output tile of a workgroup's list: its origin and the byte offsets of
+// its A rows and preshuffled B blocks.  Loads go through descriptors over the
+// whole of A or B, so rows past M and column blocks past N fall outside them
+// and read as zero.  Past the end of the list m0 = -1: the descriptors of
+// such loads are empty, so they move no data but still count in vmcnt.
+struct TileRef {
+    int m0, n0;
+    int a_off, b_off;
+};
+
 template <int MODE>
 struct Ctx {
     using C = Cfg<MODE>;
@@ -159,57 +174,68 @@ struct Ctx {
     v4f sfa[2][C::MB / 4];
     float sfb[2];
 
-    // (m0, n0) of this workgroup's tile j; m0 < 0 when j is past the list
-    __device__ __forceinline__ void origin(int j, int& m0, int& n0) const {
-        if (j >= ntiles) {
-            m0 = -1;
-            n0 = -1;
-            return;
-        }
-        int tm, tn;
-        tile_coords(tl.tile(j), tiles_m, tiles_n, tm, tn);
-        m0 = tm * C::BM;
-        n0 = tn * BN;
-    }
+    // Tile j of this workgroup's list with the buffer descriptors its loads
+    // use (see TileRef).
+    __device__ __forceinline__ TileRef ref(int j) const;
 };
 
-// Stream position of a load: tile j + dj of the list, K tile kt.
-struct Pos {
-    int m0, n0, kt;  // m0 < 0: past the end (zero-length descriptors)
-};
+template <int MODE>
+__device__ __forceinline__ TileRef Ctx<MODE>::ref(int j) const {
+    if (j >= ntiles) return TileRef{-1, -1, 0, 0};
+    int tm, tn;
+    tile_coords(tl.tile(j), tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * C::BM, n0 = tn * BN;
+    return TileRef{m0, n0, m0 * K, (n0 / 16) * KI * 2048};
+}
+
+// Descriptors over all of A or B, or empty for a tile past the list.
+template <int MODE>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t a_rsrc(const Ctx<MODE>& x, bool valid) {
+    return make_rsrc(x.a, valid ? (uint32_t)x.M * (uint32_t)x.K : 0u);
+}
+template <int MODE>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t b_rsrc(const Ctx<MODE>& x, bool valid) {
+    return make_rsrc(x.b, valid ? (uint32_t)x.N * (uint32_t)x.K : 0u);
+}
 
 // ---------------------------------------------------------------- issue
 // B event of one K tile: the B fragments (8 x 1 KiB loads per wave) plus
-// the per-K-tile scales of the mode.  Past the end of the stream every load
-// goes through a zero-length descriptor: no data moves, the instructions
-// still count in vmcnt.
+// the per-K-tile scales of the mode.  A step spreads the fragment loads over
+// its first row blocks, one or two between consecutive groups of matrix ops.
+//
+// Fragment load Q (0..7): half Q % 2 of column block Q / 2; base = the
+// tile's B offset + 2048 kt for K tile kt.
+template <int MODE, int T, int Q>
+__device__ __forceinline__ void b_piece(Ctx<MODE>& x, __amdgpu_buffer_rsrc_t rb, int base) {
+    const int off = x.voff_b[Q / 2] + base + (Q % 2) * 1024;
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+    v8i& d = x.bq[T][Q / 2];
+    constexpr int h = 4 * (Q % 2);
+    d[h + 0] = v[0];
+    d[h + 1] = v[1];
+    d[h + 2] = v[2];
+    d[h + 3] = v[3];
+}
+
+// The mode's per-K-tile scales of a B event (none for ptpc).
 template <int MODE, int T>
-__device__ __forceinline__ void issue_b(Ctx<MODE>& x, const Pos& p) {
+__device__ __forceinline__ void b_scales(Ctx<MODE>& x, TileRef r, int kt) {
     using C = Cfg<MODE>;
-    const bool valid = p.m0 >= 0;
-    const int n0 = valid ? p.n0 : 0, m0 = valid ? p.m0 : 0;
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(x.b + (size_t)(n0 / 16) * x.KI * 2048, valid ? (uint32_t)(x.N - n0) * (uint32_t)x.K : 0u);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int off = x.voff_b[nb] + p.kt * 2048;
-        v4i lo = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-        v4i hi = __builtin_amdgcn_raw_buffer_load_b128(rb, off + 1024, 0, 0);
-        x.bq[T][nb] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
+    const bool valid = r.m0 >= 0;
+    const int n0 = valid ? r.n0 : 0, m0 = valid ? r.m0 : 0;
     if constexpr (MODE == MODE_MXFP8) {
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x.sa, valid ? (uint32_t)(x.K / 32) * (uint32_t)x.M : 0u);
         const __amdgpu_buffer_rsrc_t rsb = make_rsrc(x.sb, valid ? (uint32_t)(x.K / 32) * (uint32_t)x.N : 0u);
         // A: 16 consecutive E8M0 bytes (rows 16i .. 16i+15 of the tile) of K
         // group 4kt + g; the row stride M need not be a multiple of 4, so
         // load the dword-aligned window and realign in registers
-        const int off = (4 * p.kt + x.g) * x.M + m0 + 16 * x.i;
+        const int off = (4 * kt + x.g) * x.M + m0 + 16 * x.i;
         const int base = off & ~3;
         x.sxa[T] = __builtin_amdgcn_raw_buffer_load_b128(rsa, base, 0, 0);
         x.sxa_tail[T] = __builtin_amdgcn_raw_buffer_load_b32(rsa, base + 16, 0, 0);
         x.sxa_shift[T] = off & 3;
         // B: the byte of column 16 nb + i of the wave's 64, K group 4kt + g
-        const int boff = (4 * p.kt + x.g) * x.N + n0 + 64 * x.w + x.i;
+        const int boff = (4 * kt + x.g) * x.N + n0 + 64 * x.w + x.i;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) x.sxb[T][nb] = __builtin_amdgcn_raw_buffer_load_b8(rsb, boff + 16 * nb, 0, 0);
     } else if constexpr (MODE == MODE_BLOCKSCALE) {
@@ -221,11 +247,27 @@ __device__ __forceinline__ void issue_b(Ctx<MODE>& x, const Pos& p) {
         for (int r = 0; r < C::MB; ++r) {
             const int row = min(m0 + C::MB * x.i + r, x.M - 1);
             x.sfa[T][r / 4][r % 4] =
-                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, (p.kt * x.M + row) * 4, 0, 0));
+                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, (kt * x.M + row) * 4, 0, 0));
         }
         x.sfb[T] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rsb, (((n0 + 64 * x.w) / 128) * x.KI + p.kt) * 4, 0, 0));
+            float, __builtin_amdgcn_raw_buffer_load_b32(rsb, (((n0 + 64 * x.w) / 128) * x.KI + kt) * 4, 0, 0));
     }
+}
+
+// A whole B event at once (the prologue's).
+template <int MODE, int T>
+__device__ __forceinline__ void issue_b(Ctx<MODE>& x, TileRef r, int kt) {
+    const __amdgpu_buffer_rsrc_t rb = b_rsrc(x, r.m0 >= 0);
+    const int base = r.b_off + kt * 2048;
+    b_piece<MODE, T, 0>(x, rb, base);
+    b_piece<MODE, T, 1>(x, rb, base);
+    b_piece<MODE, T, 2>(x, rb, base);
+    b_piece<MODE, T, 3>(x, rb, base);
+    b_piece<MODE, T, 4>(x, rb, base);
+    b_piece<MODE, T, 5>(x, rb, base);
+    b_piece<MODE, T, 6>(x, rb, base);
+    b_piece<MODE, T, 7>(x, rb, base);
+    b_scales<MODE, T>(x, r, kt);
 }
 
 // ptpc epilogue scales of the tile at (m0, n0): NSC = 2 DMAs per wave into
@@ -242,20 +284,19 @@ __device__ __forceinline__ void issue_epilogue_scales(Ctx<MODE>& x, int m0, int 
     }
 }
 
-// Global -> LDS DMA of one A K tile (NA instructions per wave).  The tile's
-// rows start at m0; the descriptor covers rows m0 .. M-1 only, so rows past M
-// read as zero.
+// Global -> LDS DMA of one A K tile: NA instructions per wave; instruction
+// j moves 1 KiB (8 rows x 128 bytes).  base = the tile's A offset + 128 kt
+// for K tile kt; rows past M fall outside the descriptor and read as zero.
 template <int MODE>
-__device__ __forceinline__ void issue_a(Ctx<MODE>& x, lds_char* stage, const Pos& p) {
-    using C = Cfg<MODE>;
-    const bool valid = p.m0 >= 0;
-    const int m0 = valid ? p.m0 : 0;
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(x.a + (size_t)m0 * x.K, valid ? (uint32_t)(x.M - m0) * (uint32_t)x.K : 0u);
-    lds_char* dst = stage + x.dma_lds;
+__device__ __forceinline__ void a_piece(Ctx<MODE>& x, lds_char* stage, __amdgpu_buffer_rsrc_t ra, int base, int j) {
+    lds_dma16(ra, stage + x.dma_lds + j * 1024, x.voff_a[j] + base);
+}
+
+template <int MODE>
+__device__ __forceinline__ void issue_a(Ctx<MODE>& x, lds_char* stage, TileRef r, int kt) {
+    const __amdgpu_buffer_rsrc_t ra = a_rsrc(x, r.m0 >= 0);
 #pragma unroll
-    for (int j = 0; j < C::NA; ++j)
-        lds_dma16(ra, dst + j * 1024, x.voff_a[j] + p.kt * BK);
+    for (int j = 0; j < Cfg<MODE>::NA; ++j) a_piece<MODE>(x, stage, ra, r.a_off + kt * BK, j);
 }
 
 template <int MODE, int S>
@@ -356,7 +397,8 @@ __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
 // Result lane l, register v of block (mb, nb) holds row MB (l % 16) + mb,
 // column 64 w + 16 nb + 4 (l / 16) + v of the tile.  One permlane16 swap per
 // pair of blocks moves the data so that each lane holds 8 consecutive
-// columns; the 4 lanes of a row then write 64 contiguous bytes per store.
+// columns; the 4 lanes of a row then write 64 contiguous bytes per store,
+// and the two stores of a row block cover its 128-byte row segments.
 template <int MODE>
 __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
     using C = Cfg<MODE>;
@@ -389,16 +431,23 @@ __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
             : "v"(pa), "v"(pb)
             : "memory");
     }
+    // column of this lane's 8 values for block pair 0 (blocks 0, 1) and 1
+    // (blocks 2, 3): after the swap g=0 holds the pair's first block columns
+    // 0-7, g=1 the second block's 0-7, g=2 the first's 8-15, g=3 the second's
+    int col[2];
+    bool col_ok[2];
 #pragma unroll
     for (int pair = 0; pair < 2; ++pair) {
-        const int nb0 = 2 * pair, nb1 = 2 * pair + 1;
-        // after the swap: g=0 holds block nb0 columns 0-7, g=1 nb1 0-7,
-        // g=2 nb0 8-15, g=3 nb1 8-15
-        const int my_nb = (x.g & 1) ? nb1 : nb0;
-        const int col = n0 + 64 * x.w + 16 * my_nb + 8 * (x.g >> 1);
-        const bool col_ok = n0 + 64 * x.w + 16 * my_nb < x.N;
+        const int my_nb = 2 * pair + (x.g & 1);
+        col[pair] = n0 + 64 * x.w + 16 * my_nb + 8 * (x.g >> 1);
+        col_ok[pair] = n0 + 64 * x.w + 16 * my_nb < x.N;
+    }
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) {
+    for (int mb = 0; mb < C::MB; ++mb) {
+        // both halves of each 128-byte row segment go out back to back
+#pragma unroll
+        for (int pair = 0; pair < 2; ++pair) {
+            const int nb0 = 2 * pair, nb1 = 2 * pair + 1;
             v4f u = x.acc[mb][nb0], v = x.acc[mb][nb1];
             if constexpr (MODE == MODE_PTPC) {
                 const float sa = eas[mb / 4][mb % 4];
@@ -411,11 +460,12 @@ __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
             const auto s1 = __builtin_amdgcn_permlane16_swap(u1, v1, false, false);
             const v4i data = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
             // rows at or past M fall outside the buffer and are dropped
-            if (col_ok) __builtin_amdgcn_raw_buffer_store_b128(data, rc, ((row0 + mb) * x.N + col) * 2, 0, 0);
-            // keep the scheduler from hoisting every accumulator read of the
-            // epilogue at once (the next tile's loads are live here)
-            if ((mb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            if (col_ok[pair])
+                __builtin_amdgcn_raw_buffer_store_b128(data, rc, ((row0 + mb) * x.N + col[pair]) * 2, 0, kCacheStream);
         }
+        // keep the scheduler from hoisting every accumulator read of the
+        // epilogue at once (the next tile's loads are live here)
+        if ((mb & 1) == 1) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -428,54 +478,73 @@ __device__ __forceinline__ void zero_acc(Ctx<MODE>& x) {
 }
 
 // ---------------------------------------------------------------- step
-// Where a stream step sits: s = stream position, k = K tile within its
-// output tile, and the origins of tiles j, j+1, j+2 (cur/n1/n2) for loads
-// that run ahead into the next tiles.
-struct Step {
-    int s, k, m0c, n0c, m01, n01, m02, n02;
+// Origins and operand extents of tiles j, j+1, j+2 of the list, rotated as
+// the stream advances: loads run up to two tiles ahead of the one computed.
+struct Ring {
+    TileRef t0, t1, t2;
 };
 
-// The middle of a step: wait + barrier, then the A DMA of stream step s+3
-// into stage SR.  RAW: K tile s+1 has landed in every wave's share of LDS.
-// WAR: every wave's reads of stage SR (stream step s-1) have retired.  The
-// count is sched::wait_at(s, k, KI, ...), specialised: only the stream's
-// very first step differs from the rest of its kind.
+// Where one stream step's loads go: the B event of step s+1 and the A DMA of
+// step s+3 (K tile k+3 of this tile or of one of the next two).
+struct StepLoads {
+    __amdgpu_buffer_rsrc_t rb, ra;
+    int bbase, abase;  // byte offsets of the B event's and the A DMA's K tile
+    int bkt;           // K tile of the B event (for the mode's scales)
+    TileRef bref;
+};
+
+// The middle of a step.  RAW: K tile s+1 has landed in every wave's share of
+// LDS.  WAR: every wave's reads of stage (S+3)%4 (stream step s-1) have
+// retired, so the A DMAs that follow may refill it.  The count is
+// sched::wait_at(s, k, KI, ...), specialised: only the stream's very first
+// step differs from the rest of its kind.
 template <int MODE, int S, bool FIRST, bool LAST>
-__device__ __forceinline__ void mid_step(Ctx<MODE>& x, Step t) {
+__device__ __forceinline__ void mid_step(int s) {
     using C = Cfg<MODE>;
-    constexpr int SR = (S + 3) & 3;
     constexpr int NA = C::NA, NB = C::NB, NSC = C::NSC;
     constexpr int XT = (LAST ? 1 : 0) + (FIRST ? 1 : 0);
     if constexpr (FIRST) {
-        if (t.s == 0) wait_vm_lgkm0<sched::cap(sched::first_mid_wait(NA, NB) + (LAST ? NSC : 0))>();
+        if (s == 0) wait_vm_lgkm0<sched::cap(sched::first_mid_wait(NA, NB) + (LAST ? NSC : 0))>();
         else wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB) + XT * NSC)>();
     } else {
         wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB) + XT * NSC)>();
     }
     __builtin_amdgcn_s_barrier();
-    // K tile k+3 of this tile or of one of the next two
-    const int KI = x.KI;
-    const int kk = t.k + 3;
-    const bool in0 = kk < KI, in1 = kk < 2 * KI;
-    const Pos p{in0 ? t.m0c : (in1 ? t.m01 : t.m02), in0 ? t.n0c : (in1 ? t.n01 : t.n02),
-                in0 ? kk : (in1 ? kk - KI : kk - 2 * KI)};
-    issue_a<MODE>(x, x.lds.p[SR], p);
 }
 
-// Row blocks mb .. MB-1 of a step.  A fragments run two row blocks ahead
-// through a three-deep register ring (f0, f1, f2 hold fragments = 0, 1, 2
-// mod 3): fragment mb + 2 is read while mb's matrix ops run.  Reads of this
-// step's stage S need no barrier (the previous step's covered its tile);
-// the next stage's first two fragments, read in the last two row blocks,
-// come after this step's barrier at mb = MB / 2.
+// Row blocks mb .. MB-1 of a step; each row block's four matrix ops are
+// separated by at most a few other instructions:
+// - A fragments run two row blocks ahead through a three-deep register ring
+//   (f0, f1, f2 hold fragments = 0, 1, 2 mod 3): fragment mb + 2 is read
+//   while mb's matrix ops run.  Reads of this step's stage S need no barrier
+//   (the previous step's covered its tile); the next stage's first two
+//   fragments, read in the last two row blocks, come after this step's
+//   barrier.
+// - The next B event is spread over the first half (8 / (MB/2) fragment
+//   loads per row block, then the mode's scales and, in the last K step of a
+//   tile, the epilogue's scale DMAs); the wait + barrier sits at MB/2; the A
+//   DMA of step s+3 follows it, one instruction per row block.  The order of
+//   the loads relative to the wait is the one sched::wait_at counts.
 template <int MODE, int S, bool FIRST, bool LAST, int mb>
-__device__ __forceinline__ void step_rows(Ctx<MODE>& x, Step t, v8i& f0, v8i& f1, v8i& f2) {
+__device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, StepLoads L, v8i& f0, v8i& f1, v8i& f2) {
     using C = Cfg<MODE>;
     if constexpr (mb < C::MB) {
         constexpr int T = S & 1;
-        constexpr int SN = (S + 1) & 3;
+        constexpr int SR = (S + 3) & 3;  // stage refilled by this step (tile k-1's)
+        constexpr int SN = (S + 1) & 3;  // stage of the next K tile
+        constexpr int HALF = C::MB / 2;
+        constexpr int BPR = 8 / HALF;  // B fragment loads per row block
         constexpr int nxt = mb + 2;
-        if constexpr (mb == C::MB / 2) mid_step<MODE, S, FIRST, LAST>(x, t);
+        if constexpr (mb < HALF) {
+            b_piece<MODE, T ^ 1, mb * BPR>(x, L.rb, L.bbase);
+            if constexpr (BPR == 2) b_piece<MODE, T ^ 1, mb * BPR + 1>(x, L.rb, L.bbase);
+            if constexpr (mb == HALF - 1) {
+                b_scales<MODE, T ^ 1>(x, L.bref, L.bkt);
+                if constexpr (LAST) issue_epilogue_scales<MODE>(x, cur.m0, cur.n0);
+            }
+        }
+        if constexpr (mb == HALF) mid_step<MODE, S, FIRST, LAST>(s);
+        if constexpr (mb >= HALF) a_piece<MODE>(x, x.lds.p[SR], L.ra, L.abase, mb - HALF);
         if constexpr (nxt < C::MB) {
             v8i fr = read_a<MODE, S>(x, nxt);
             if constexpr (nxt % 3 == 0) f0 = fr;
@@ -487,7 +556,7 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, Step t, v8i& f0, v8i& f1
         if constexpr (mb % 3 == 0) mfma_row<MODE, T, mb, FIRST>(x, f0);
         else if constexpr (mb % 3 == 1) mfma_row<MODE, T, mb, FIRST>(x, f1);
         else mfma_row<MODE, T, mb, FIRST>(x, f2);
-        step_rows<MODE, S, FIRST, LAST, mb + 1>(x, t, f0, f1, f2);
+        step_rows<MODE, S, FIRST, LAST, mb + 1>(x, s, cur, L, f0, f1, f2);
     }
 }
 
@@ -495,17 +564,31 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, Step t, v8i& f0, v8i& f1
 // tile, T = s % 2 the B register buffer.  FIRST / LAST: k == 0 / k == KI-1
 // (both for KI == 1).
 template <int MODE, int S, bool FIRST, bool LAST>
-__device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, int m0c, int n0c, int m01, int n01, int m02,
-                                      int n02) {
+__device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g) {
     constexpr int T = S & 1;
-    const Step t{s, k, m0c, n0c, m01, n01, m02, n02};
-    // B event of stream step s+1 (the next tile's first K tile after LAST)
-    if constexpr (LAST) issue_b<MODE, T ^ 1>(x, Pos{m01, n01, 0});
-    else issue_b<MODE, T ^ 1>(x, Pos{m0c, n0c, k + 1});
-    if constexpr (LAST) issue_epilogue_scales<MODE>(x, m0c, n0c);
+    const int KI = x.KI;
+    StepLoads L;
+    // B event of stream step s+1: the next K tile, or the next tile's first
+    L.bref = LAST ? g.t1 : g.t0;
+    L.bkt = LAST ? 0 : k + 1;
+    L.rb = b_rsrc(x, L.bref.m0 >= 0);
+    L.bbase = L.bref.b_off + L.bkt * 2048;
+    // A DMA of stream step s+3: K tile k+3 of this tile or of one of the next
+    // two (selected without branches)
+    const int kk = k + 3;
+    const bool in0 = kk < KI, in1 = kk < 2 * KI;
+    int a_off = g.t2.a_off, a_m0 = g.t2.m0, akt = kk - 2 * KI;
+    a_off = in1 ? g.t1.a_off : a_off;
+    a_m0 = in1 ? g.t1.m0 : a_m0;
+    akt = in1 ? kk - KI : akt;
+    a_off = in0 ? g.t0.a_off : a_off;
+    a_m0 = in0 ? g.t0.m0 : a_m0;
+    akt = in0 ? kk : akt;
+    L.ra = a_rsrc(x, a_m0 >= 0);
+    L.abase = a_off + akt * BK;
     realign_mx<MODE, T>(x);
     v8i f0 = x.pre[0], f1 = x.pre[1], f2;
-    step_rows<MODE, S, FIRST, LAST, 0>(x, t, f0, f1, f2);
+    step_rows<MODE, S, FIRST, LAST, 0>(x, s, g.t0, L, f0, f1, f2);
 }
 
 // All K tiles of tile j, whose first K tile sits in stage P, then its
@@ -514,40 +597,33 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, int m0c, int n
 // middle steps run as whole groups of four plus exactly (CASE - 2) & 3 more,
 // so every stage index and every wait count is a constant.
 template <int MODE, int P, int CASE>
-__device__ __forceinline__ void tile_body(Ctx<MODE>& x, int s0, int m0c, int n0c, int m01, int n01, int m02, int n02) {
+__device__ __forceinline__ void tile_body(Ctx<MODE>& x, int s0, Ring g) {
     const int KI = x.KI;
     if constexpr (CASE == 4) {
-        kstep<MODE, P, true, true>(x, s0, 0, m0c, n0c, m01, n01, m02, n02);
+        kstep<MODE, P, true, true>(x, s0, 0, g);
     } else {
         constexpr int REM = (CASE - 2) & 3;  // (KI - 2) % 4
-        kstep<MODE, P, true, false>(x, s0, 0, m0c, n0c, m01, n01, m02, n02);
+        kstep<MODE, P, true, false>(x, s0, 0, g);
         int k = 1;
         for (; k + 4 <= KI - 1; k += 4) {
-            kstep<MODE, (P + 1) & 3, false, false>(x, s0 + k, k, m0c, n0c, m01, n01, m02, n02);
-            kstep<MODE, (P + 2) & 3, false, false>(x, s0 + k + 1, k + 1, m0c, n0c, m01, n01, m02, n02);
-            kstep<MODE, (P + 3) & 3, false, false>(x, s0 + k + 2, k + 2, m0c, n0c, m01, n01, m02, n02);
-            kstep<MODE, (P + 0) & 3, false, false>(x, s0 + k + 3, k + 3, m0c, n0c, m01, n01, m02, n02);
+            kstep<MODE, (P + 1) & 3, false, false>(x, s0 + k, k, g);
+            kstep<MODE, (P + 2) & 3, false, false>(x, s0 + k + 1, k + 1, g);
+            kstep<MODE, (P + 3) & 3, false, false>(x, s0 + k + 2, k + 2, g);
+            kstep<MODE, (P + 0) & 3, false, false>(x, s0 + k + 3, k + 3, g);
         }
-        if constexpr (REM >= 1) kstep<MODE, (P + 1) & 3, false, false>(x, s0 + k, k, m0c, n0c, m01, n01, m02, n02);
-        if constexpr (REM >= 2) kstep<MODE, (P + 2) & 3, false, false>(x, s0 + k + 1, k + 1, m0c, n0c, m01, n01, m02, n02);
-        if constexpr (REM >= 3) kstep<MODE, (P + 3) & 3, false, false>(x, s0 + k + 2, k + 2, m0c, n0c, m01, n01, m02, n02);
-        kstep<MODE, (P + CASE - 1) & 3, false, true>(x, s0 + KI - 1, KI - 1, m0c, n0c, m01, n01, m02, n02);
+        if constexpr (REM >= 1) kstep<MODE, (P + 1) & 3, false, false>(x, s0 + k, k, g);
+        if constexpr (REM >= 2) kstep<MODE, (P + 2) & 3, false, false>(x, s0 + k + 1, k + 1, g);
+        if constexpr (REM >= 3) kstep<MODE, (P + 3) & 3, false, false>(x, s0 + k + 2, k + 2, g);
+        kstep<MODE, (P + CASE - 1) & 3, false, true>(x, s0 + KI - 1, KI - 1, g);
     }
     mfma_drain<MODE>(x);
-    store_tile<MODE>(x, m0c, n0c);
+    store_tile<MODE>(x, g.t0.m0, g.t0.n0);
 }
-
-// Origins of tiles j, j+1, j+2 of the list, rotated as the stream advances.
-struct Ring {
-    int m0c, n0c, m01, n01, m02, n02;
-};
 
 template <int MODE, int P, int CASE>
 __device__ __forceinline__ void run_tile(Ctx<MODE>& x, int j, Ring& g) {
-    tile_body<MODE, P, CASE>(x, j * x.KI, g.m0c, g.n0c, g.m01, g.n01, g.m02, g.n02);
-    int m03, n03;
-    x.origin(j + 3, m03, n03);
-    g = Ring{g.m01, g.n01, g.m02, g.n02, m03, n03};
+    tile_body<MODE, P, CASE>(x, j * x.KI, g);
+    g = Ring{g.t1, g.t2, x.ref(j + 3)};
 }
 
 // -------------------------------------------------------------- kernel
@@ -595,30 +671,29 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_a8w8_kernel(GemmArgs p) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) x.voff_b[nb] = ((4 * x.w + nb) * x.KI) * 2048 + 16 * x.lane;
 
-    int m0c, n0c, m01, n01, m02, n02;
-    x.origin(0, m0c, n0c);
-    x.origin(1, m01, n01);
-    x.origin(2, m02, n02);
+    Ring g{x.ref(0), x.ref(1), x.ref(2)};
 
     // prologue: Bev(0), A(0), A(1), A(2) of the stream
     {
         const int KI = x.KI;
-        issue_b<MODE, 0>(x, Pos{m0c, n0c, 0});
-        auto pos = [&](int sidx) {
-            if (sidx < KI) return Pos{m0c, n0c, sidx};
-            if (sidx < 2 * KI) return Pos{m01, n01, sidx - KI};
-            return Pos{m02, n02, sidx - 2 * KI};
+        issue_b<MODE, 0>(x, g.t0, 0);
+        auto pos = [&](int sidx, int& kt) {
+            if (sidx < KI) { kt = sidx; return g.t0; }
+            if (sidx < 2 * KI) { kt = sidx - KI; return g.t1; }
+            kt = sidx - 2 * KI;
+            return g.t2;
         };
-        issue_a<MODE>(x, x.lds.p[0], pos(0));
-        issue_a<MODE>(x, x.lds.p[1], pos(1));
-        issue_a<MODE>(x, x.lds.p[2], pos(2));
+        int kt0, kt1, kt2;
+        const TileRef r0 = pos(0, kt0), r1 = pos(1, kt1), r2 = pos(2, kt2);
+        issue_a<MODE>(x, x.lds.p[0], r0, kt0);
+        issue_a<MODE>(x, x.lds.p[1], r1, kt1);
+        issue_a<MODE>(x, x.lds.p[2], r2, kt2);
     }
     wait_vm_lgkm0<sched::prologue_wait(C::NA)>();
     __builtin_amdgcn_s_barrier();
     x.pre[0] = read_a<MODE, 0>(x, 0);
     x.pre[1] = read_a<MODE, 0>(x, 1);
 
-    Ring g{m0c, n0c, m01, n01, m02, n02};
     constexpr int R = CASE & 3;  // KI % 4
     constexpr int CYCLE = R == 0 ? 1 : R == 2 ? 2 : 4;
     for (int j = 0; j < x.ntiles; j += CYCLE) {

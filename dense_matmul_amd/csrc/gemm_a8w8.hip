@@ -74,11 +74,6 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// Cache policy of the C stores: non-temporal (the aux bit that sets NT).  C is
-// written once and never re-read by the kernel; streaming it keeps the L2 and
-// last-level cache for the A and B panels that every tile re-reads.
-constexpr int kCacheStream = 2;
-
 struct GemmArgs {
     const uint8_t* a;
     const uint8_t* b;
@@ -461,7 +456,7 @@ __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
             const v4i data = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
             // rows at or past M fall outside the buffer and are dropped
             if (col_ok[pair])
-                __builtin_amdgcn_raw_buffer_store_b128(data, rc, ((row0 + mb) * x.N + col[pair]) * 2, 0, kCacheStream);
+                __builtin_amdgcn_raw_buffer_store_b128(data, rc, ((row0 + mb) * x.N + col[pair]) * 2, 0, 0);
         }
         // keep the scheduler from hoisting every accumulator read of the
         // epilogue at once (the next tile's loads are live here)

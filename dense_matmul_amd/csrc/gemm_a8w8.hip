@@ -74,6 +74,11 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
+// DPP control of row_ror:8 (rotate each 16-lane row by 8 lanes) and the
+// cache-policy bits of a non-temporal store (nt).
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kStoreStream = 2;
+
 struct GemmArgs {
     const uint8_t* a;
     const uint8_t* b;
@@ -392,13 +397,12 @@ __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
 // Result lane l, register v of block (mb, nb) holds row MB (l % 16) + mb,
 // column 64 w + 16 nb + 4 (l / 16) + v of the tile.  One permlane16 swap per
 // pair of blocks moves the data so that each lane holds 8 consecutive
-// columns; the 4 lanes of a row then write 64 contiguous bytes per store,
-// and the two stores of a row block cover its 128-byte row segments.
+// columns, and a DPP exchange between lanes i and i + 8 makes every store
+// write whole 128-byte row segments.
 template <int MODE>
 __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
     using C = Cfg<MODE>;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(x.c, (uint32_t)x.M * (uint32_t)x.N * 2u);
-    const int row0 = m0 + C::MB * x.i;
     v4f eas[C::MB / 4], ebs[4];
     if constexpr (MODE == MODE_PTPC) {
         // This wave's scale DMAs (issue_epilogue_scales, top of the last K
@@ -426,20 +430,21 @@ __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
             : "v"(pa), "v"(pb)
             : "memory");
     }
-    // column of this lane's 8 values for block pair 0 (blocks 0, 1) and 1
-    // (blocks 2, 3): after the swap g=0 holds the pair's first block columns
-    // 0-7, g=1 the second block's 0-7, g=2 the first's 8-15, g=3 the second's
-    int col[2];
-    bool col_ok[2];
-#pragma unroll
-    for (int pair = 0; pair < 2; ++pair) {
-        const int my_nb = 2 * pair + (x.g & 1);
-        col[pair] = n0 + 64 * x.w + 16 * my_nb + 8 * (x.g >> 1);
-        col_ok[pair] = n0 + 64 * x.w + 16 * my_nb < x.N;
-    }
+    // After the swap lane (i, g) holds 8 consecutive columns of row
+    // MB i + mb for each block pair: pair p, g = 0..3 -> columns
+    // 32 p + {0, 16, 8, 24} .. +7 of the wave's 64.  Lanes i and i + 8 then
+    // trade one pair (row_ror:8 within each 16-lane row, bank masks picking
+    // lanes 0-7 or 8-15), so that each store writes 8 whole 128-byte row
+    // segments: store 0 rows MB (i % 8) + mb, store 1 rows MB (i % 8 + 8) +
+    // mb, lane i writing pair i / 8 of the row.
+    const int pair_of_lane = x.i >> 3;
+    const int nb_of_lane = 2 * pair_of_lane + (x.g & 1);
+    const int col = n0 + 64 * x.w + 16 * nb_of_lane + 8 * (x.g >> 1);
+    const bool col_ok = n0 + 64 * x.w + 16 * nb_of_lane < x.N;
+    const int row_lo = m0 + C::MB * (x.i & 7);
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
-        // both halves of each 128-byte row segment go out back to back
+        v4i d[2];
 #pragma unroll
         for (int pair = 0; pair < 2; ++pair) {
             const int nb0 = 2 * pair, nb1 = 2 * pair + 1;
@@ -453,10 +458,21 @@ __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
             const uint32_t v0 = pack_bf16(v[0], v[1]), v1 = pack_bf16(v[2], v[3]);
             const auto s0 = __builtin_amdgcn_permlane16_swap(u0, v0, false, false);
             const auto s1 = __builtin_amdgcn_permlane16_swap(u1, v1, false, false);
-            const v4i data = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
-            // rows at or past M fall outside the buffer and are dropped
-            if (col_ok[pair])
-                __builtin_amdgcn_raw_buffer_store_b128(data, rc, ((row0 + mb) * x.N + col[pair]) * 2, 0, 0);
+            d[pair] = (v4i){(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+        }
+        v4i lo, hi;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            lo[q] = __builtin_amdgcn_update_dpp(d[0][q], d[1][q], kDppRowRor8, 0xF, 0xC, false);
+            hi[q] = __builtin_amdgcn_update_dpp(d[1][q], d[0][q], kDppRowRor8, 0xF, 0x3, false);
+        }
+        // rows at or past M fall outside the buffer and are dropped; C is
+        // written once and never read back, so the stores stream past the
+        // caches that hold the A and B panels
+        if (col_ok) {
+            __builtin_amdgcn_raw_buffer_store_b128(lo, rc, ((row_lo + mb) * x.N + col) * 2, 0, kStoreStream);
+            __builtin_amdgcn_raw_buffer_store_b128(hi, rc, ((row_lo + 8 * C::MB + mb) * x.N + col) * 2, 0,
+                                                   kStoreStream);
         }
         // keep the scheduler from hoisting every accumulator read of the
         // epilogue at once (the next tile's loads are live here)

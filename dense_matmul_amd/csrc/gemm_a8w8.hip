@@ -45,7 +45,7 @@ namespace dmm {
 
 enum { MODE_PTPC = 0, MODE_BLOCKSCALE = 1, MODE_MXFP8 = 2 };
 
-constexpr int BN = 256, BK = 128, NTHREADS = 256;
+constexpr int BK = 128, NTHREADS = 256;
 
 // The LDS ring: four distinct arrays so that the compiler can tell the
 // stages apart (its own LDS-DMA dependency tracking is per object).
@@ -89,13 +89,22 @@ struct GemmArgs {
     int tiles_m, tiles_n;
 };
 
+// Tile shape per mode.  Each of the 4 waves owns NBW 16-column blocks side by
+// side and all MB 16-row blocks of the tile.  ptpc and mxfp8 keep their
+// 256 x 256 tile in the 256 accumulation registers; blockscale folds every
+// K tile's products into VGPR accumulators with its scales, so its tile is
+// 128 x 128 (64 accumulators per lane) to leave room for the products of two
+// row blocks in flight.
 template <int MODE>
 struct Cfg {
-    static constexpr int MB = MODE == MODE_BLOCKSCALE ? 8 : 16;  // 16-row blocks per wave
-    static constexpr int BM = 16 * MB;                            // tile rows
-    static constexpr int NA = MB / 2;                             // DMA instructions per wave per K tile
-    // vector-memory instructions of one B event: 8 fragment loads plus scales
-    static constexpr int NB = MODE == MODE_PTPC ? 8 : MODE == MODE_MXFP8 ? 8 + 2 + 4 : 8 + MB + 1;
+    static constexpr int MB = MODE == MODE_BLOCKSCALE ? 8 : 16;   // 16-row blocks per wave
+    static constexpr int NBW = MODE == MODE_BLOCKSCALE ? 2 : 4;   // 16-column blocks per wave
+    static constexpr int BM = 16 * MB;                             // tile rows
+    static constexpr int WN = 16 * NBW;                            // columns per wave
+    static constexpr int BN = 4 * WN;                              // tile columns
+    static constexpr int NA = MB / 2;                              // DMA instructions per wave per K tile
+    // vector-memory instructions of one B event: 2 NBW fragment loads plus scales
+    static constexpr int NB = MODE == MODE_PTPC ? 2 * NBW : MODE == MODE_MXFP8 ? 2 * NBW + 2 + NBW : 2 * NBW + MB + 1;
     // vector-memory instructions of the ptpc epilogue's scale loads (two
     // 1 KiB DMAs per wave)
     static constexpr int NSC = MODE == MODE_PTPC ? 2 : 0;
@@ -160,19 +169,21 @@ struct Ctx {
     int w, lane, i, g;
     int dma_lds;        // byte offset of this wave's DMA slots in a stage
     int voff_a[C::NA];  // per-lane byte offsets of the DMA rows, relative to the tile's first row
-    int voff_b[4];      // per-lane byte offsets of the B fragments, relative to the tile's first column
+    int voff_b[C::NBW]; // per-lane byte offsets of the B fragments, relative to the tile's first column
     int rd[2][2];       // LDS byte offsets of the two 16-byte halves of an A fragment, for even / odd mb
-    v4f acc[C::MB][4];
-    v8i bq[2][4];       // B fragments, double buffered across K tiles
+    v4f acc[C::MB][C::NBW];
+    v8i bq[2][C::NBW];  // B fragments, double buffered across K tiles
     v8i pre[2];         // first two A fragments of the next K tile
     // mxfp8: E8M0 bytes for A (a 16-byte window plus one word to realign) and B (one per block)
     v4i sxa[2];
     int sxa_tail[2];
     int sxa_shift[2];
-    int sxb[2][4];
-    // blockscale: A scales of this lane's MB rows and the wave's B block scale
+    int sxb[2][C::NBW];
+    // blockscale: A scales of this lane's MB rows and the wave's B block scale;
+    // the products of the last two row blocks, before they are scaled in
     v4f sfa[2][C::MB / 4];
     float sfb[2];
+    v4f bp[2][C::NBW];
 
     // Tile j of this workgroup's list with the buffer descriptors its loads
     // use (see TileRef).
@@ -184,7 +195,7 @@ __device__ __forceinline__ TileRef Ctx<MODE>::ref(int j) const {
     if (j >= ntiles) return TileRef{-1, -1, 0, 0};
     int tm, tn;
     tile_coords(tl.tile(j), tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * C::BM, n0 = tn * BN;
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
     return TileRef{m0, n0, m0 * K, (n0 / 16) * KI * 2048};
 }
 
@@ -203,7 +214,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t b_rsrc(const Ctx<MODE>& x, boo
 // the per-K-tile scales of the mode.  A step spreads the fragment loads over
 // its first row blocks, one or two between consecutive groups of matrix ops.
 //
-// Fragment load Q (0..7): half Q % 2 of column block Q / 2; base = the
+// Fragment load Q (0..2 NBW-1): half Q % 2 of column block Q / 2; base = the
 // tile's B offset + 2048 kt for K tile kt.
 template <int MODE, int T, int Q>
 __device__ __forceinline__ void b_piece(Ctx<MODE>& x, __amdgpu_buffer_rsrc_t rb, int base) {
@@ -235,9 +246,9 @@ __device__ __forceinline__ void b_scales(Ctx<MODE>& x, TileRef r, int kt) {
         x.sxa_tail[T] = __builtin_amdgcn_raw_buffer_load_b32(rsa, base + 16, 0, 0);
         x.sxa_shift[T] = off & 3;
         // B: the byte of column 16 nb + i of the wave's 64, K group 4kt + g
-        const int boff = (4 * kt + x.g) * x.N + n0 + 64 * x.w + x.i;
+        const int boff = (4 * kt + x.g) * x.N + n0 + C::WN * x.w + x.i;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) x.sxb[T][nb] = __builtin_amdgcn_raw_buffer_load_b8(rsb, boff + 16 * nb, 0, 0);
+        for (int nb = 0; nb < C::NBW; ++nb) x.sxb[T][nb] = __builtin_amdgcn_raw_buffer_load_b8(rsb, boff + 16 * nb, 0, 0);
     } else if constexpr (MODE == MODE_BLOCKSCALE) {
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x.sa, valid ? (uint32_t)x.KI * (uint32_t)x.M * 4u : 0u);
         const __amdgpu_buffer_rsrc_t rsb =
@@ -250,7 +261,7 @@ __device__ __forceinline__ void b_scales(Ctx<MODE>& x, TileRef r, int kt) {
                 __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, (kt * x.M + row) * 4, 0, 0));
         }
         x.sfb[T] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rsb, (((n0 + 64 * x.w) / 128) * x.KI + kt) * 4, 0, 0));
+            float, __builtin_amdgcn_raw_buffer_load_b32(rsb, (((n0 + C::WN * x.w) / 128) * x.KI + kt) * 4, 0, 0));
     }
 }
 
@@ -259,14 +270,7 @@ template <int MODE, int T>
 __device__ __forceinline__ void issue_b(Ctx<MODE>& x, TileRef r, int kt) {
     const __amdgpu_buffer_rsrc_t rb = b_rsrc(x, r.m0 >= 0);
     const int base = r.b_off + kt * 2048;
-    b_piece<MODE, T, 0>(x, rb, base);
-    b_piece<MODE, T, 1>(x, rb, base);
-    b_piece<MODE, T, 2>(x, rb, base);
-    b_piece<MODE, T, 3>(x, rb, base);
-    b_piece<MODE, T, 4>(x, rb, base);
-    b_piece<MODE, T, 5>(x, rb, base);
-    b_piece<MODE, T, 6>(x, rb, base);
-    b_piece<MODE, T, 7>(x, rb, base);
+    static_for<0, 2 * Cfg<MODE>::NBW>([&](auto Qc) { b_piece<MODE, T, decltype(Qc)::value>(x, rb, base); });
     b_scales<MODE, T>(x, r, kt);
 }
 
@@ -334,10 +338,40 @@ __device__ __forceinline__ void mfma_scaled_acc(v4f& acc, const v8i& b, const v8
                      : "v"(b), "v"(a), "v"(sb), "v"(sa), "n"(OA & 1), "n"(OB & 1), "n"(OA >> 1), "n"(OB >> 1));
 }
 
+// blockscale: acc[r] (+)= bp[r % 2] * sa(row, kt) * sb(block, kt).  The
+// products come from the matrix ops issued just before (at the latest two of
+// them earlier); the 20 wait states ahead of the first read cover the result
+// latency of the longest (16-pass) form of the instruction whatever the
+// compiler schedules in between, since the compiler cannot see the hazard
+// across the asm statements.
+template <int MODE, int T, int r, bool FIRST>
+__device__ __forceinline__ void fold_products(Ctx<MODE>& x) {
+    const float s = x.sfa[T][r / 4][r % 4] * x.sfb[T];
+    v4f& c0 = x.acc[r][0];
+    v4f& c1 = x.acc[r][1];
+    const v4f p0 = x.bp[r & 1][0], p1 = x.bp[r & 1][1];
+    if constexpr (FIRST) {
+        asm volatile(
+            "s_nop 7\n\ts_nop 7\n\ts_nop 3\n\t"
+            "v_mul_f32 %0, %8, %16\n\tv_mul_f32 %1, %9, %16\n\tv_mul_f32 %2, %10, %16\n\tv_mul_f32 %3, %11, %16\n\t"
+            "v_mul_f32 %4, %12, %16\n\tv_mul_f32 %5, %13, %16\n\tv_mul_f32 %6, %14, %16\n\tv_mul_f32 %7, %15, %16"
+            : "=&v"(c0[0]), "=&v"(c0[1]), "=&v"(c0[2]), "=&v"(c0[3]), "=&v"(c1[0]), "=&v"(c1[1]), "=&v"(c1[2]),
+              "=&v"(c1[3])
+            : "v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(p1[0]), "v"(p1[1]), "v"(p1[2]), "v"(p1[3]), "v"(s));
+    } else {
+        asm volatile(
+            "s_nop 7\n\ts_nop 7\n\ts_nop 3\n\t"
+            "v_fmac_f32 %0, %8, %16\n\tv_fmac_f32 %1, %9, %16\n\tv_fmac_f32 %2, %10, %16\n\tv_fmac_f32 %3, %11, %16\n\t"
+            "v_fmac_f32 %4, %12, %16\n\tv_fmac_f32 %5, %13, %16\n\tv_fmac_f32 %6, %14, %16\n\tv_fmac_f32 %7, %15, %16"
+            : "+v"(c0[0]), "+v"(c0[1]), "+v"(c0[2]), "+v"(c0[3]), "+v"(c1[0]), "+v"(c1[1]), "+v"(c1[2]), "+v"(c1[3])
+            : "v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(p1[0]), "v"(p1[1]), "v"(p1[2]), "v"(p1[3]), "v"(s));
+    }
+}
+
 template <int MODE, int T, int mb, bool FIRST>
 __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
     if constexpr (MODE == MODE_PTPC) {
-        static_for<0, 4>([&](auto NBc) {
+        static_for<0, Cfg<MODE>::NBW>([&](auto NBc) {
             constexpr int nb = decltype(NBc)::value;
             mfma_acc<FIRST>(x.acc[mb][nb], x.bq[T][nb], a);
         });
@@ -345,21 +379,24 @@ __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
         // src1 (A) scale: byte mb % 4 of word mb / 4 of the realigned bytes;
         // src0 (B) scale: byte 0 of the block's own register
         const int sa_word = x.sxa[T][mb / 4];
-        static_for<0, 4>([&](auto NBc) {
+        static_for<0, Cfg<MODE>::NBW>([&](auto NBc) {
             constexpr int nb = decltype(NBc)::value;
             mfma_scaled_acc<FIRST, 0, mb % 4>(x.acc[mb][nb], x.bq[T][nb], a, x.sxb[T][nb], sa_word);
         });
     } else {
         // blockscale: one fp32 scale per (row, 128-wide K tile) times the
-        // B block's scale, applied to the tile's partial sum in VGPRs
-        const float s = x.sfa[T][mb / 4][mb % 4] * x.sfb[T];
-        const v4f zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x.bq[T][nb], a, zero, 0, 0, 0, 0, 0, 0);
-            if constexpr (FIRST) x.acc[mb][nb] = p * s;
-            else x.acc[mb][nb] += p * s;
-        }
+        // B block's scale multiplies each K tile's products before they are
+        // added to the VGPR accumulators.  The products of row block mb go
+        // to bp[mb % 2]; row block mb - 1's are scaled in behind them, so
+        // the matrix ops of one row block overlap the additions of the last.
+        static_assert(Cfg<MODE>::NBW == 2, "two column blocks per wave");
+        asm volatile(
+            "v_mfma_f32_16x16x128_f8f6f4 %0, %2, %4, 0\n\t"
+            "v_mfma_f32_16x16x128_f8f6f4 %1, %3, %4, 0"
+            : "=&v"(x.bp[mb & 1][0]), "=&v"(x.bp[mb & 1][1])
+            : "v"(x.bq[T][0]), "v"(x.bq[T][1]), "v"(a));
+        if constexpr (mb > 0) fold_products<MODE, T, mb - 1, FIRST>(x);
+        if constexpr (mb == Cfg<MODE>::MB - 1) fold_products<MODE, T, mb, FIRST>(x);
     }
 }
 
@@ -374,7 +411,7 @@ __device__ __forceinline__ void mfma_drain(Ctx<MODE>& x) {
 #pragma unroll
         for (int mb = 0; mb < Cfg<MODE>::MB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) asm volatile("" : "+a"(x.acc[mb][nb]));
+            for (int nb = 0; nb < Cfg<MODE>::NBW; ++nb) asm volatile("" : "+a"(x.acc[mb][nb]));
     }
 }
 
@@ -403,7 +440,7 @@ template <int MODE>
 __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
     using C = Cfg<MODE>;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(x.c, (uint32_t)x.M * (uint32_t)x.N * 2u);
-    v4f eas[C::MB / 4], ebs[4];
+    v4f eas[C::MB / 4], ebs[C::NBW];
     if constexpr (MODE == MODE_PTPC) {
         // This wave's scale DMAs (issue_epilogue_scales, top of the last K
         // step) were followed only by the NA A-tile DMAs of that step, so
@@ -437,10 +474,30 @@ __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
     // lanes 0-7 or 8-15), so that each store writes 8 whole 128-byte row
     // segments: store 0 rows MB (i % 8) + mb, store 1 rows MB (i % 8 + 8) +
     // mb, lane i writing pair i / 8 of the row.
+    if constexpr (C::NBW == 2) {
+        // blockscale: one block pair per wave; after the swap the 4 lanes of
+        // row MB i + mb hold its 32 columns (64 bytes), and the neighbouring
+        // wave writes the other half of each 128-byte segment, so these
+        // stores go through the L2, which merges the halves
+        const int col = n0 + C::WN * x.w + 16 * (x.g & 1) + 8 * (x.g >> 1);
+        const bool col_ok = n0 + C::WN * x.w + 16 * (x.g & 1) < x.N;
+        const int row0 = m0 + C::MB * x.i;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) {
+            const v4f u = x.acc[mb][0], v = x.acc[mb][1];
+            const uint32_t u0 = pack_bf16(u[0], u[1]), u1 = pack_bf16(u[2], u[3]);
+            const uint32_t v0 = pack_bf16(v[0], v[1]), v1 = pack_bf16(v[2], v[3]);
+            const auto s0 = __builtin_amdgcn_permlane16_swap(u0, v0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(u1, v1, false, false);
+            const v4i d = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+            if (col_ok) __builtin_amdgcn_raw_buffer_store_b128(d, rc, ((row0 + mb) * x.N + col) * 2, 0, 0);
+            if ((mb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
     const int pair_of_lane = x.i >> 3;
     const int nb_of_lane = 2 * pair_of_lane + (x.g & 1);
-    const int col = n0 + 64 * x.w + 16 * nb_of_lane + 8 * (x.g >> 1);
-    const bool col_ok = n0 + 64 * x.w + 16 * nb_of_lane < x.N;
+    const int col = n0 + C::WN * x.w + 16 * nb_of_lane + 8 * (x.g >> 1);
+    const bool col_ok = n0 + C::WN * x.w + 16 * nb_of_lane < x.N;
     const int row_lo = m0 + C::MB * (x.i & 7);
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
@@ -478,6 +535,7 @@ __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
         // epilogue at once (the next tile's loads are live here)
         if ((mb & 1) == 1) __builtin_amdgcn_sched_barrier(0);
     }
+    }
 }
 
 template <int MODE>
@@ -485,7 +543,7 @@ __device__ __forceinline__ void zero_acc(Ctx<MODE>& x) {
 #pragma unroll
     for (int mb = 0; mb < Cfg<MODE>::MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) x.acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < Cfg<MODE>::NBW; ++nb) x.acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
 }
 
 // ---------------------------------------------------------------- step
@@ -544,7 +602,8 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, Step
         constexpr int SR = (S + 3) & 3;  // stage refilled by this step (tile k-1's)
         constexpr int SN = (S + 1) & 3;  // stage of the next K tile
         constexpr int HALF = C::MB / 2;
-        constexpr int BPR = 8 / HALF;  // B fragment loads per row block
+        constexpr int BPR = 2 * C::NBW / HALF;  // B fragment loads per row block
+        static_assert(BPR == 1 || BPR == 2, "B fragment loads spread over the first half");
         constexpr int nxt = mb + 2;
         if constexpr (mb < HALF) {
             b_piece<MODE, T ^ 1, mb * BPR>(x, L.rb, L.bbase);
@@ -677,10 +736,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_a8w8_kernel(GemmArgs p) {
     for (int odd = 0; odd < 2; ++odd)
 #pragma unroll
         for (int half = 0; half < 2; ++half) x.rd[odd][half] = lds::frag_base(x.i, x.g, odd, half, C::MB);
-    // B fragments: 16-column block 4 w + nb of the tile, K tile kt at
+    // B fragments: 16-column block NBW w + nb of the tile, K tile kt at
     // (block * KI + kt) * 2048; lane l reads 16 bytes at 16 l of each half.
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) x.voff_b[nb] = ((4 * x.w + nb) * x.KI) * 2048 + 16 * x.lane;
+    for (int nb = 0; nb < C::NBW; ++nb) x.voff_b[nb] = ((C::NBW * x.w + nb) * x.KI) * 2048 + 16 * x.lane;
 
     Ring g{x.ref(0), x.ref(1), x.ref(2)};
 
@@ -736,7 +795,7 @@ template <int MODE>
 static hipError_t launch_gemm(const GemmArgs& base, hipStream_t stream) {
     GemmArgs p = base;
     p.tiles_m = (p.m + Cfg<MODE>::BM - 1) / Cfg<MODE>::BM;
-    p.tiles_n = (p.n + BN - 1) / BN;
+    p.tiles_n = (p.n + Cfg<MODE>::BN - 1) / Cfg<MODE>::BN;
     const int tiles = p.tiles_m * p.tiles_n;
     const int grid = tiles < device_cus() ? tiles : device_cus();
     const int ki = p.k / BK;

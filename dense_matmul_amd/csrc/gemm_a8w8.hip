@@ -45,7 +45,7 @@ namespace dmm {
 
 enum { MODE_PTPC = 0, MODE_BLOCKSCALE = 1, MODE_MXFP8 = 2 };
 
-constexpr int BK = 128, NTHREADS = 256;
+constexpr int BK = 128;
 
 // The LDS ring: four distinct arrays so that the compiler can tell the
 // stages apart (its own LDS-DMA dependency tracking is per object).
@@ -89,22 +89,25 @@ struct GemmArgs {
     int tiles_m, tiles_n;
 };
 
-// Tile shape per mode.  Each of the 4 waves owns NBW 16-column blocks side by
-// side and all MB 16-row blocks of the tile.  ptpc and mxfp8 keep their
-// 256 x 256 tile in the 256 accumulation registers; blockscale folds every
-// K tile's products into VGPR accumulators with its scales, so its tile is
-// 128 x 128 (64 accumulators per lane) to leave room for the products of two
-// row blocks in flight.
+// Tile shape per mode.  Each of the WAVES waves owns NBW 16-column blocks
+// side by side and all MB 16-row blocks of the tile.  ptpc and mxfp8 keep
+// their 256 x 256 tile in the 256 accumulation registers of 4 waves (one per
+// SIMD).  Blockscale folds every K tile's products into VGPR accumulators
+// with its scales, so each of its waves owns 128 x 32 (64 accumulators per
+// lane) and 8 waves, two per SIMD, share a 128 x 256 tile: each SIMD then
+// has a second wave to issue matrix ops while one waits.
 template <int MODE>
 struct Cfg {
     static constexpr int MB = MODE == MODE_BLOCKSCALE ? 8 : 16;   // 16-row blocks per wave
     static constexpr int NBW = MODE == MODE_BLOCKSCALE ? 2 : 4;   // 16-column blocks per wave
+    static constexpr int WAVES = MODE == MODE_BLOCKSCALE ? 8 : 4;  // waves per workgroup
+    static constexpr int NTHREADS = 64 * WAVES;
     static constexpr int BM = 16 * MB;                             // tile rows
     static constexpr int WN = 16 * NBW;                            // columns per wave
-    static constexpr int BN = 4 * WN;                              // tile columns
-    static constexpr int NA = MB / 2;                              // DMA instructions per wave per K tile
+    static constexpr int BN = WAVES * WN;                          // tile columns
+    static constexpr int NA = 2 * MB / WAVES;                      // DMA instructions per wave per K tile
     // vector-memory instructions of one B event: 2 NBW fragment loads plus scales
-    static constexpr int NB = MODE == MODE_PTPC ? 2 * NBW : MODE == MODE_MXFP8 ? 2 * NBW + 2 + NBW : 2 * NBW + MB + 1;
+    static constexpr int NB = MODE == MODE_PTPC ? 2 * NBW : MODE == MODE_MXFP8 ? 2 * NBW + 2 + NBW : 2 * NBW + 2 + 1;
     // vector-memory instructions of the ptpc epilogue's scale loads (two
     // 1 KiB DMAs per wave)
     static constexpr int NSC = MODE == MODE_PTPC ? 2 : 0;
@@ -253,13 +256,13 @@ __device__ __forceinline__ void b_scales(Ctx<MODE>& x, TileRef r, int kt) {
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x.sa, valid ? (uint32_t)x.KI * (uint32_t)x.M * 4u : 0u);
         const __amdgpu_buffer_rsrc_t rsb =
             make_rsrc(x.sb, valid ? (uint32_t)((x.N + 127) / 128) * (uint32_t)x.KI * 4u : 0u);
-        // one dword per row; rows past M read row M-1 (their output is dropped)
-#pragma unroll
-        for (int r = 0; r < C::MB; ++r) {
-            const int row = min(m0 + C::MB * x.i + r, x.M - 1);
-            x.sfa[T][r / 4][r % 4] =
-                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, (kt * x.M + row) * 4, 0, 0));
-        }
+        // the MB consecutive rows MB i .. MB i + MB-1 of this lane: two
+        // 16-byte loads (rows past M read the next K block's scales or, at
+        // the end, zeros; their output is dropped)
+        static_assert(C::MB == 8, "two 16-byte loads of A scales per lane");
+        const int aoff = (kt * x.M + m0 + C::MB * x.i) * 4;
+        x.sfa[T][0] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rsa, aoff, 0, 0));
+        x.sfa[T][1] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rsa, aoff + 16, 0, 0));
         x.sfb[T] = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(rsb, (((n0 + C::WN * x.w) / 128) * x.KI + kt) * 4, 0, 0));
     }
@@ -589,11 +592,11 @@ __device__ __forceinline__ void mid_step(int s) {
 //   (the previous step's covered its tile); the next stage's first two
 //   fragments, read in the last two row blocks, come after this step's
 //   barrier.
-// - The next B event is spread over the first half (8 / (MB/2) fragment
+// - The next B event is spread over the first half (2 NBW / (MB/2) fragment
 //   loads per row block, then the mode's scales and, in the last K step of a
-//   tile, the epilogue's scale DMAs); the wait + barrier sits at MB/2; the A
-//   DMA of step s+3 follows it, one instruction per row block.  The order of
-//   the loads relative to the wait is the one sched::wait_at counts.
+//   tile, the epilogue's scale DMAs); the wait + barrier sits at MB/2; the NA
+//   A DMAs of step s+3 follow it, spread evenly over the second half.  The
+//   order of the loads relative to the wait is the one sched::wait_at counts.
 template <int MODE, int S, bool FIRST, bool LAST, int mb>
 __device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, StepLoads L, v8i& f0, v8i& f1, v8i& f2) {
     using C = Cfg<MODE>;
@@ -603,7 +606,8 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, Step
         constexpr int SN = (S + 1) & 3;  // stage of the next K tile
         constexpr int HALF = C::MB / 2;
         constexpr int BPR = 2 * C::NBW / HALF;  // B fragment loads per row block
-        static_assert(BPR == 1 || BPR == 2, "B fragment loads spread over the first half");
+        static_assert((BPR == 1 || BPR == 2) && BPR * HALF == 2 * C::NBW,
+                      "every B fragment load of the event, spread over the first half");
         constexpr int nxt = mb + 2;
         if constexpr (mb < HALF) {
             b_piece<MODE, T ^ 1, mb * BPR>(x, L.rb, L.bbase);
@@ -614,7 +618,11 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, Step
             }
         }
         if constexpr (mb == HALF) mid_step<MODE, S, FIRST, LAST>(s);
-        if constexpr (mb >= HALF) a_piece<MODE>(x, x.lds.p[SR], L.ra, L.abase, mb - HALF);
+        // NA DMAs spread over the second half, the first at mb = HALF
+        static_assert(C::NA <= HALF && HALF % C::NA == 0, "A DMAs spread evenly over the second half");
+        constexpr int DSTRIDE = HALF / C::NA;
+        if constexpr (mb >= HALF && (mb - HALF) % DSTRIDE == 0)
+            a_piece<MODE>(x, x.lds.p[SR], L.ra, L.abase, (mb - HALF) / DSTRIDE);
         if constexpr (nxt < C::MB) {
             v8i fr = read_a<MODE, S>(x, nxt);
             if constexpr (nxt % 3 == 0) f0 = fr;
@@ -701,7 +709,7 @@ __device__ __forceinline__ void run_tile(Ctx<MODE>& x, int j, Ring& g) {
 // tile advances by KI % 4 from one tile to the next, so tiles come in
 // cycles of 1, 2 or 4 phases.
 template <int MODE, int CASE>
-__global__ void __launch_bounds__(NTHREADS, 1) gemm_a8w8_kernel(GemmArgs p) {
+__global__ void __launch_bounds__(Cfg<MODE>::NTHREADS, 1) gemm_a8w8_kernel(GemmArgs p) {
     using C = Cfg<MODE>;
     Ctx<MODE> x;
     x.lds = Stages{{(lds_char*)g_lds_a0, (lds_char*)g_lds_a1, (lds_char*)g_lds_a2, (lds_char*)g_lds_a3},
@@ -728,10 +736,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_a8w8_kernel(GemmArgs p) {
     // A tile placement in LDS (lds_layout.h): the DMA lane fetches the row
     // and chunk that belong at the address it writes; a fragment read by 16
     // lanes touches every one of the 64 banks once.
-    x.dma_lds = lds::dma_lds_byte(x.w, 0, 0, C::MB);
+    x.dma_lds = lds::dma_lds_byte(C::NA * x.w, 0);
 #pragma unroll
     for (int j = 0; j < C::NA; ++j)
-        x.voff_a[j] = lds::dma_row(x.w, j, x.lane, C::MB) * x.K + lds::dma_chunk(x.w, j, x.lane, C::MB) * 16;
+        x.voff_a[j] = lds::dma_row(C::NA * x.w + j, x.lane, C::MB) * x.K + lds::dma_chunk(C::NA * x.w + j, x.lane, C::MB) * 16;
 #pragma unroll
     for (int odd = 0; odd < 2; ++odd)
 #pragma unroll
@@ -800,11 +808,11 @@ static hipError_t launch_gemm(const GemmArgs& base, hipStream_t stream) {
     const int grid = tiles < device_cus() ? tiles : device_cus();
     const int ki = p.k / BK;
     switch (ki == 1 ? 4 : ki & 3) {
-        case 4: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 4>), dim3(grid), dim3(NTHREADS), 0, stream, p); break;
-        case 0: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 0>), dim3(grid), dim3(NTHREADS), 0, stream, p); break;
-        case 1: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 1>), dim3(grid), dim3(NTHREADS), 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 2>), dim3(grid), dim3(NTHREADS), 0, stream, p); break;
-        default: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 3>), dim3(grid), dim3(NTHREADS), 0, stream, p); break;
+        case 4: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 4>), dim3(grid), dim3(Cfg<MODE>::NTHREADS), 0, stream, p); break;
+        case 0: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 0>), dim3(grid), dim3(Cfg<MODE>::NTHREADS), 0, stream, p); break;
+        case 1: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 1>), dim3(grid), dim3(Cfg<MODE>::NTHREADS), 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 2>), dim3(grid), dim3(Cfg<MODE>::NTHREADS), 0, stream, p); break;
+        default: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 3>), dim3(grid), dim3(Cfg<MODE>::NTHREADS), 0, stream, p); break;
     }
     return hipGetLastError();
 }

@@ -31,11 +31,12 @@ constexpr int row_of_slot(int q, int MB) { return slot_of_row(q, MB); }
 // position of chunk c of row r inside its slot (an involution in c)
 constexpr int chunk_pos(int r, int c, int MB) { return c ^ ((r / MB) & 7); }
 
-// DMA instruction j of wave w (NA = MB / 2 per wave), lane l: the LDS byte it
-// writes and the (row, chunk) it must fetch
-constexpr int dma_lds_byte(int w, int j, int l, int MB) { return ((MB / 2) * w + j) * 1024 + 16 * l; }
-constexpr int dma_row(int w, int j, int l, int MB) { return row_of_slot(8 * ((MB / 2) * w + j) + (l >> 3), MB); }
-constexpr int dma_chunk(int w, int j, int l, int MB) { return chunk_pos(dma_row(w, j, l, MB), l & 7, MB); }
+// The stage is written by 2 MB DMA instructions of 1 KiB; instruction j of
+// wave w is block b = NA w + j (NA = 2 MB / waves per wave).  Lane l of
+// block b: the LDS byte it writes and the (row, chunk) it must fetch.
+constexpr int dma_lds_byte(int b, int l) { return b * 1024 + 16 * l; }
+constexpr int dma_row(int b, int l, int MB) { return row_of_slot(8 * b + (l >> 3), MB); }
+constexpr int dma_chunk(int b, int l, int MB) { return chunk_pos(dma_row(b, l, MB), l & 7, MB); }
 
 // Fragment read of row block mb by lane (i, g), half 0 (chunk g) or 1
 // (chunk 4 + g): base[mb & 1][half] + 128 mb.  With h = (i >> 3) & 1 the

@@ -37,9 +37,9 @@ int prologue_wait(int NA) { return sched::prologue_wait(NA); }
 int wait_at(int s, int k, int KI, int NA, int NB, int NSC) { return sched::wait_at(s, k, KI, NA, NB, NSC); }
 int stage_of(int j) { return sched::stage_of(j); }
 int refill_stage(int s) { return sched::refill_stage(s); }
-int dma_lds_byte(int w, int j, int l, int MB) { return lds::dma_lds_byte(w, j, l, MB); }
-int dma_row(int w, int j, int l, int MB) { return lds::dma_row(w, j, l, MB); }
-int dma_chunk(int w, int j, int l, int MB) { return lds::dma_chunk(w, j, l, MB); }
+int dma_lds_byte(int b, int l) { return lds::dma_lds_byte(b, l); }
+int dma_row(int b, int l, int MB) { return lds::dma_row(b, l, MB); }
+int dma_chunk(int b, int l, int MB) { return lds::dma_chunk(b, l, MB); }
 int frag_byte(int i, int g, int mb, int half, int MB) { return lds::frag_byte(i, g, mb, half, MB); }
 }
 """
@@ -60,7 +60,7 @@ def shim(tmp_path_factory):
 
 
 # ---------------------------------------------------------------- schedule
-MODES = {"ptpc": (8, 8, 2), "mxfp8": (8, 14, 0), "blockscale": (4, 13, 0)}  # NA, NB, NSC per wave
+MODES = {"ptpc": (8, 8, 2), "mxfp8": (8, 14, 0), "blockscale": (2, 7, 0)}  # NA, NB, NSC per wave
 
 
 def program(L, KI, ntiles, NA, NB, NSC, wait_fn=None):
@@ -204,35 +204,39 @@ def test_checker_catches_a_missing_war_barrier(shim):
 
 
 # ------------------------------------------------------------------ layout
-@pytest.mark.parametrize("MB", [16, 8])
-def test_dma_writes_every_row_chunk_once(shim, MB):
-    NA = MB // 2
+# (row blocks per stage / 16, waves): ptpc and mxfp8, blockscale
+LAYOUTS = [(16, 4), (8, 8)]
+
+
+def dma_blocks(MB, waves):
+    NA = 2 * MB // waves
+    return [(w, j, NA * w + j) for w in range(waves) for j in range(NA)]
+
+
+@pytest.mark.parametrize("MB,waves", LAYOUTS)
+def test_dma_writes_every_row_chunk_once(shim, MB, waves):
     seen = {}
-    for w in range(4):
-        for j in range(NA):
-            for l in range(64):
-                addr = shim.dma_lds_byte(w, j, l, MB)
-                assert addr % 16 == 0 and 0 <= addr < 16 * MB * 128
-                assert addr not in seen
-                seen[addr] = (shim.dma_row(w, j, l, MB), shim.dma_chunk(w, j, l, MB))
+    for w, j, b in dma_blocks(MB, waves):
+        for l in range(64):
+            addr = shim.dma_lds_byte(b, l)
+            assert addr % 16 == 0 and 0 <= addr < 16 * MB * 128
+            assert addr not in seen
+            seen[addr] = (shim.dma_row(b, l, MB), shim.dma_chunk(b, l, MB))
     assert sorted(seen.values()) == [(r, c) for r in range(16 * MB) for c in range(8)]
     # every lane group of 8 fetches one whole 128-byte row (coalesced)
-    for w in range(4):
-        for j in range(NA):
-            for q in range(8):
-                rows = {shim.dma_row(w, j, 8 * q + t, MB) for t in range(8)}
-                chunks = {shim.dma_chunk(w, j, 8 * q + t, MB) for t in range(8)}
-                assert len(rows) == 1 and chunks == set(range(8))
+    for w, j, b in dma_blocks(MB, waves):
+        for q in range(8):
+            rows = {shim.dma_row(b, 8 * q + t, MB) for t in range(8)}
+            chunks = {shim.dma_chunk(b, 8 * q + t, MB) for t in range(8)}
+            assert len(rows) == 1 and chunks == set(range(8))
 
 
-@pytest.mark.parametrize("MB", [16, 8])
-def test_fragment_reads_find_their_data(shim, MB):
-    NA = MB // 2
+@pytest.mark.parametrize("MB,waves", LAYOUTS)
+def test_fragment_reads_find_their_data(shim, MB, waves):
     where = {}
-    for w in range(4):
-        for j in range(NA):
-            for l in range(64):
-                where[shim.dma_lds_byte(w, j, l, MB)] = (shim.dma_row(w, j, l, MB), shim.dma_chunk(w, j, l, MB))
+    for w, j, b in dma_blocks(MB, waves):
+        for l in range(64):
+            where[shim.dma_lds_byte(b, l)] = (shim.dma_row(b, l, MB), shim.dma_chunk(b, l, MB))
     for l in range(64):
         i, g = l % 16, l // 16
         for mb in range(MB):

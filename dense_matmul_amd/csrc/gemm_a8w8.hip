@@ -107,7 +107,7 @@ struct Cfg {
     static constexpr int BN = WAVES * WN;                          // tile columns
     static constexpr int NA = 2 * MB / WAVES;                      // DMA instructions per wave per K tile
     // vector-memory instructions of one B event: 2 NBW fragment loads plus scales
-    static constexpr int NB = MODE == MODE_PTPC ? 2 * NBW : MODE == MODE_MXFP8 ? 2 * NBW + 2 + NBW : 2 * NBW + 2 + 1;
+    static constexpr int NB = MODE == MODE_PTPC ? 2 * NBW : 2 * NBW + 2 + 1;
     // vector-memory instructions of the ptpc epilogue's scale loads (two
     // 1 KiB DMAs per wave)
     static constexpr int NSC = MODE == MODE_PTPC ? 2 : 0;
@@ -181,7 +181,8 @@ struct Ctx {
     v4i sxa[2];
     int sxa_tail[2];
     int sxa_shift[2];
-    int sxb[2][C::NBW];
+    int sxb_raw[2];      // B scale bytes of 4 columns as loaded
+    int sxb[C::NBW];     // B scale of this lane's column in each block (byte 0), current step
     // blockscale: A scales of this lane's MB rows and the wave's B block scale;
     // the products of the last two row blocks, before they are scaled in
     v4f sfa[2][C::MB / 4];
@@ -248,10 +249,11 @@ __device__ __forceinline__ void b_scales(Ctx<MODE>& x, TileRef r, int kt) {
         x.sxa[T] = __builtin_amdgcn_raw_buffer_load_b128(rsa, base, 0, 0);
         x.sxa_tail[T] = __builtin_amdgcn_raw_buffer_load_b32(rsa, base + 16, 0, 0);
         x.sxa_shift[T] = off & 3;
-        // B: the byte of column 16 nb + i of the wave's 64, K group 4kt + g
-        const int boff = (4 * kt + x.g) * x.N + n0 + C::WN * x.w + x.i;
-#pragma unroll
-        for (int nb = 0; nb < C::NBW; ++nb) x.sxb[T][nb] = __builtin_amdgcn_raw_buffer_load_b8(rsb, boff + 16 * nb, 0, 0);
+        // B: lane (i, g) loads columns 4i .. 4i+3 of the wave's 64 for K
+        // group 4kt + g (one aligned dword; N is a multiple of 16); the bytes
+        // are distributed across lanes when the step that uses them starts
+        const int boff = (4 * kt + x.g) * x.N + n0 + C::WN * x.w + 4 * x.i;
+        x.sxb_raw[T] = __builtin_amdgcn_raw_buffer_load_b32(rsb, boff, 0, 0);
     } else if constexpr (MODE == MODE_BLOCKSCALE) {
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x.sa, valid ? (uint32_t)x.KI * (uint32_t)x.M * 4u : 0u);
         const __amdgpu_buffer_rsrc_t rsb =
@@ -380,11 +382,11 @@ __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
         });
     } else if constexpr (MODE == MODE_MXFP8) {
         // src1 (A) scale: byte mb % 4 of word mb / 4 of the realigned bytes;
-        // src0 (B) scale: byte 0 of the block's own register
+        // src0 (B) scale: byte 0 of the block's register
         const int sa_word = x.sxa[T][mb / 4];
         static_for<0, Cfg<MODE>::NBW>([&](auto NBc) {
             constexpr int nb = decltype(NBc)::value;
-            mfma_scaled_acc<FIRST, 0, mb % 4>(x.acc[mb][nb], x.bq[T][nb], a, x.sxb[T][nb], sa_word);
+            mfma_scaled_acc<FIRST, 0, mb % 4>(x.acc[mb][nb], x.bq[T][nb], a, x.sxb[nb], sa_word);
         });
     } else {
         // blockscale: one fp32 scale per (row, 128-wide K tile) times the
@@ -418,7 +420,10 @@ __device__ __forceinline__ void mfma_drain(Ctx<MODE>& x) {
     }
 }
 
-// Realign the 20 loaded E8M0 bytes so word q holds the bytes of rows 4q..4q+3.
+// Start of a step's mxfp8 scales: realign the 20 loaded A-scale bytes so word
+// q holds the bytes of rows 4q..4q+3, and give lane (i, g) the B-scale byte
+// of column 16 nb + i of each block, which lane (4 nb + i / 4, g) loaded as
+// byte i % 4 of its dword.
 template <int MODE, int T>
 __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
     if constexpr (MODE == MODE_MXFP8) {
@@ -430,6 +435,11 @@ __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
             x.sxa[T] = (v4i){(int)__builtin_amdgcn_alignbyte(w[1], w[0], sh), (int)__builtin_amdgcn_alignbyte(w[2], w[1], sh),
                              (int)__builtin_amdgcn_alignbyte(w[3], w[2], sh), (int)__builtin_amdgcn_alignbyte(t, w[3], sh)};
         }
+        const int src = 4 * (16 * x.g + (x.i >> 2));
+        const int byte = 8 * (x.i & 3);
+#pragma unroll
+        for (int nb = 0; nb < Cfg<MODE>::NBW; ++nb)
+            x.sxb[nb] = (int)((uint32_t)__builtin_amdgcn_ds_bpermute(src + 16 * nb, x.sxb_raw[T]) >> byte);
     }
 }
 

@@ -205,7 +205,7 @@ def extra_shapes(dmm, torch, args):
     """Secondary lines: the other scaling modes, the tail-only and gathered
     shapes, and the bf16 GEMM (fewer steps each)."""
     res = {}
-    steps, warm = max(5, args.steps // 5), 3
+    steps, warm = max(5, args.steps // 4), 20
     for name, mode, m, n, k, sa_seed, sb_seed in [
         ("blockscale_16384x7168x2048", "blockscale", 16384, 7168, 2048, 41, 42),
         ("mxfp8_32768x7168x1792", "mxfp8", 32768, 7168, 1792, 31, 32),

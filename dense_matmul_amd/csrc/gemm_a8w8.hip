@@ -114,6 +114,11 @@ struct Cfg {
     static_assert(2 * NB + NA <= 63, "vmcnt range");
 };
 
+// Whether a tile's epilogue is deferred into the next tile's first K step
+// (modes whose accumulators live in AGPRs).
+template <int MODE>
+constexpr bool kDeferEpilogue = MODE != MODE_BLOCKSCALE;
+
 // Per-workgroup tile list of the persistent grid.  Workgroup w runs on XCD
 // w % 8 (the dispatcher deals workgroups to the XCDs in turn); the XCD owns a
 // contiguous range of the tile order and its workgroups stride through it, so
@@ -327,7 +332,7 @@ __device__ __forceinline__ v8i read_a(const Ctx<MODE>& x, int mb) {
 // (mfma_drain) before it reads the results.
 template <bool ZERO>
 __device__ __forceinline__ void mfma_acc(v4f& acc, const v8i& b, const v8i& a) {
-    if constexpr (ZERO) asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=a"(acc) : "v"(b), "v"(a));
+    if constexpr (ZERO) asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "+a"(acc) : "v"(b), "v"(a));
     else asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
 }
 
@@ -335,7 +340,7 @@ template <bool ZERO, int OA, int OB>
 __device__ __forceinline__ void mfma_scaled_acc(v4f& acc, const v8i& b, const v8i& a, int sb, int sa) {
     if constexpr (ZERO)
         asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
-                     : "=a"(acc)
+                     : "+a"(acc)
                      : "v"(b), "v"(a), "v"(sb), "v"(sa), "n"(OA & 1), "n"(OB & 1), "n"(OA >> 1), "n"(OB >> 1));
     else
         asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
@@ -445,26 +450,58 @@ __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
 
 // ------------------------------------------------------------ epilogue
 // Result lane l, register v of block (mb, nb) holds row MB (l % 16) + mb,
-// column 64 w + 16 nb + 4 (l / 16) + v of the tile.  One permlane16 swap per
+// column WN w + 16 nb + 4 (l / 16) + v of the tile.  One permlane16 swap per
 // pair of blocks moves the data so that each lane holds 8 consecutive
-// columns, and a DPP exchange between lanes i and i + 8 makes every store
-// write whole 128-byte row segments.
+// columns.  With two block pairs per wave (ptpc, mxfp8) a DPP exchange
+// between lanes i and i + 8 then makes every store write 8 whole 128-byte
+// row segments: store 0 rows MB (i % 8) + mb, store 1 rows MB (i % 8 + 8) +
+// mb, lane i writing pair i / 8 of the row.
+//
+// ptpc and mxfp8 run a tile's epilogue inside the first K step of the
+// workgroup's next tile: row block mb is scaled, converted and stored just
+// before that step's first matrix ops overwrite its accumulators, so the
+// conversion overlaps matrix work and the stores spread over the step.  The
+// workgroup's last tile is stored after its loop; blockscale (accumulators
+// in VGPRs, written by the compiler) stores each tile at its end.
+
+// What the epilogue of one tile needs besides the accumulators.
+struct Epi {
+    v4f eas[4], ebs[4];  // ptpc: a_scale of this lane's rows, b_scale of its columns
+    int row;             // first row this lane writes
+    int col;             // column of this lane's 8 values
+    int col_ok;          // that column group lies below N
+};
+
+// Start the epilogue of the tile at (m0, n0).  ptpc reads its scales from
+// this wave's LDS region: the scale DMAs (issue_epilogue_scales, in the
+// tile's last K step) were followed only by the NA A-tile DMAs of that step,
+// so vmcnt(NA) covers them; each wave reads only the region it filled.  The
+// reads are written out so that the compiler, which cannot tell the A-tile
+// DMAs still in flight from writes to this region, does not drain the whole
+// prefetch pipeline (vmcnt(0)) before them.
 template <int MODE>
-__device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
+__device__ __forceinline__ Epi epi_begin(Ctx<MODE>& x, int m0, int n0) {
     using C = Cfg<MODE>;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(x.c, (uint32_t)x.M * (uint32_t)x.N * 2u);
-    v4f eas[C::MB / 4], ebs[C::NBW];
+    Epi e;
+    if constexpr (C::NBW == 4) {
+        const int nb_of_lane = 2 * (x.i >> 3) + (x.g & 1);
+        e.col = n0 + C::WN * x.w + 16 * nb_of_lane + 8 * (x.g >> 1);
+        e.col_ok = n0 + C::WN * x.w + 16 * nb_of_lane < x.N;
+        e.row = m0 + C::MB * (x.i & 7);
+    } else {
+        // one block pair per wave: the 4 lanes of row MB i + mb hold its
+        // 64 bytes; the neighbouring wave writes the other half of each
+        // 128-byte segment, so these stores go through the L2, which merges
+        // the halves
+        e.col = n0 + C::WN * x.w + 16 * (x.g & 1) + 8 * (x.g >> 1);
+        e.col_ok = n0 + C::WN * x.w + 16 * (x.g & 1) < x.N;
+        e.row = m0 + C::MB * x.i;
+    }
     if constexpr (MODE == MODE_PTPC) {
-        // This wave's scale DMAs (issue_epilogue_scales, top of the last K
-        // step) were followed only by the NA A-tile DMAs of that step, so
-        // vmcnt(NA) covers them; each wave reads only the region it filled.
-        // The reads are written out so that the compiler, which cannot tell
-        // the A-tile DMAs still in flight from writes to this region, does
-        // not drain the whole prefetch pipeline (vmcnt(0)) before them.
-        static_assert(C::MB == 16, "ptpc epilogue reads four A-scale vectors");
+        static_assert(C::MB == 16 && C::NBW == 4, "ptpc epilogue reads four A- and four B-scale vectors");
         wait_vm<C::NA>();
         const uint32_t sc = (uint32_t)(uintptr_t)(x.lds.scale + x.w * 2048);
-        const uint32_t pa = sc + C::MB * x.i * 4, pb = sc + 1024 + (64 * x.w + 4 * x.g) * 4;
+        const uint32_t pa = sc + C::MB * x.i * 4, pb = sc + 1024 + (C::WN * x.w + 4 * x.g) * 4;
         asm volatile(
             "ds_read_b128 %0, %8\n"
             "ds_read_b128 %1, %8 offset:16\n"
@@ -475,80 +512,83 @@ __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
             "ds_read_b128 %6, %9 offset:128\n"
             "ds_read_b128 %7, %9 offset:192\n"
             "s_waitcnt lgkmcnt(0)"
-            : "=&v"(eas[0]), "=&v"(eas[1]), "=&v"(eas[2]), "=&v"(eas[3]), "=&v"(ebs[0]), "=&v"(ebs[1]),
-              "=&v"(ebs[2]), "=&v"(ebs[3])
+            : "=&v"(e.eas[0]), "=&v"(e.eas[1]), "=&v"(e.eas[2]), "=&v"(e.eas[3]), "=&v"(e.ebs[0]),
+              "=&v"(e.ebs[1]), "=&v"(e.ebs[2]), "=&v"(e.ebs[3])
             : "v"(pa), "v"(pb)
             : "memory");
     }
-    // After the swap lane (i, g) holds 8 consecutive columns of row
-    // MB i + mb for each block pair: pair p, g = 0..3 -> columns
-    // 32 p + {0, 16, 8, 24} .. +7 of the wave's 64.  Lanes i and i + 8 then
-    // trade one pair (row_ror:8 within each 16-lane row, bank masks picking
-    // lanes 0-7 or 8-15), so that each store writes 8 whole 128-byte row
-    // segments: store 0 rows MB (i % 8) + mb, store 1 rows MB (i % 8 + 8) +
-    // mb, lane i writing pair i / 8 of the row.
-    if constexpr (C::NBW == 2) {
-        // blockscale: one block pair per wave; after the swap the 4 lanes of
-        // row MB i + mb hold its 32 columns (64 bytes), and the neighbouring
-        // wave writes the other half of each 128-byte segment, so these
-        // stores go through the L2, which merges the halves
-        const int col = n0 + C::WN * x.w + 16 * (x.g & 1) + 8 * (x.g >> 1);
-        const bool col_ok = n0 + C::WN * x.w + 16 * (x.g & 1) < x.N;
-        const int row0 = m0 + C::MB * x.i;
+    return e;
+}
+
+// Scale, convert and store row block mb of the tile whose accumulators are
+// live.
+template <int MODE, int mb>
+__device__ __forceinline__ void epi_row(Ctx<MODE>& x, Epi e) {
+    using C = Cfg<MODE>;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(x.c, (uint32_t)x.M * (uint32_t)x.N * 2u);
+    v4i d[C::NBW / 2];
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) {
-            const v4f u = x.acc[mb][0], v = x.acc[mb][1];
-            const uint32_t u0 = pack_bf16(u[0], u[1]), u1 = pack_bf16(u[2], u[3]);
-            const uint32_t v0 = pack_bf16(v[0], v[1]), v1 = pack_bf16(v[2], v[3]);
-            const auto s0 = __builtin_amdgcn_permlane16_swap(u0, v0, false, false);
-            const auto s1 = __builtin_amdgcn_permlane16_swap(u1, v1, false, false);
-            const v4i d = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
-            if (col_ok) __builtin_amdgcn_raw_buffer_store_b128(d, rc, ((row0 + mb) * x.N + col) * 2, 0, 0);
-            if ((mb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
-    const int pair_of_lane = x.i >> 3;
-    const int nb_of_lane = 2 * pair_of_lane + (x.g & 1);
-    const int col = n0 + C::WN * x.w + 16 * nb_of_lane + 8 * (x.g >> 1);
-    const bool col_ok = n0 + C::WN * x.w + 16 * nb_of_lane < x.N;
-    const int row_lo = m0 + C::MB * (x.i & 7);
+    for (int pair = 0; pair < C::NBW / 2; ++pair) {
+        const int nb0 = 2 * pair, nb1 = 2 * pair + 1;
+        v4f u, v;
+        if constexpr (kDeferEpilogue<MODE>) {
+            // explicit reads, so that the register allocator keeps each
+            // accumulator where the next tile's matrix ops will write it
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) {
-        v4i d[2];
-#pragma unroll
-        for (int pair = 0; pair < 2; ++pair) {
-            const int nb0 = 2 * pair, nb1 = 2 * pair + 1;
-            v4f u = x.acc[mb][nb0], v = x.acc[mb][nb1];
-            if constexpr (MODE == MODE_PTPC) {
-                const float sa = eas[mb / 4][mb % 4];
-                u = u * sa * ebs[nb0];
-                v = v * sa * ebs[nb1];
+            for (int c = 0; c < 4; ++c) {
+                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(u[c]) : "a"(x.acc[mb][nb0][c]));
+                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[c]) : "a"(x.acc[mb][nb1][c]));
             }
-            const uint32_t u0 = pack_bf16(u[0], u[1]), u1 = pack_bf16(u[2], u[3]);
-            const uint32_t v0 = pack_bf16(v[0], v[1]), v1 = pack_bf16(v[2], v[3]);
-            const auto s0 = __builtin_amdgcn_permlane16_swap(u0, v0, false, false);
-            const auto s1 = __builtin_amdgcn_permlane16_swap(u1, v1, false, false);
-            d[pair] = (v4i){(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+        } else {
+            u = x.acc[mb][nb0];
+            v = x.acc[mb][nb1];
         }
+        if constexpr (MODE == MODE_PTPC) {
+            const float sa = e.eas[mb / 4][mb % 4];
+            u = u * sa * e.ebs[nb0];
+            v = v * sa * e.ebs[nb1];
+        }
+        const uint32_t u0 = pack_bf16(u[0], u[1]), u1 = pack_bf16(u[2], u[3]);
+        const uint32_t v0 = pack_bf16(v[0], v[1]), v1 = pack_bf16(v[2], v[3]);
+        const auto s0 = __builtin_amdgcn_permlane16_swap(u0, v0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(u1, v1, false, false);
+        d[pair] = (v4i){(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+    }
+    // rows at or past M fall outside the buffer and are dropped
+    if constexpr (C::NBW == 4) {
         v4i lo, hi;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             lo[q] = __builtin_amdgcn_update_dpp(d[0][q], d[1][q], kDppRowRor8, 0xF, 0xC, false);
             hi[q] = __builtin_amdgcn_update_dpp(d[1][q], d[0][q], kDppRowRor8, 0xF, 0x3, false);
         }
-        // rows at or past M fall outside the buffer and are dropped; C is
-        // written once and never read back, so the stores stream past the
-        // caches that hold the A and B panels
-        if (col_ok) {
-            __builtin_amdgcn_raw_buffer_store_b128(lo, rc, ((row_lo + mb) * x.N + col) * 2, 0, kStoreStream);
-            __builtin_amdgcn_raw_buffer_store_b128(hi, rc, ((row_lo + 8 * C::MB + mb) * x.N + col) * 2, 0,
+        // C is written once and never read back, so whole-line stores
+        // stream past the caches that hold the A and B panels
+        if (e.col_ok) {
+            __builtin_amdgcn_raw_buffer_store_b128(lo, rc, ((e.row + mb) * x.N + e.col) * 2, 0, kStoreStream);
+            __builtin_amdgcn_raw_buffer_store_b128(hi, rc, ((e.row + 8 * C::MB + mb) * x.N + e.col) * 2, 0,
                                                    kStoreStream);
         }
+    } else {
+        if (e.col_ok) __builtin_amdgcn_raw_buffer_store_b128(d[0], rc, ((e.row + mb) * x.N + e.col) * 2, 0, 0);
+    }
+}
+
+// The whole epilogue of a tile at once.
+template <int MODE, int mb = 0>
+__device__ __forceinline__ void epi_rows(Ctx<MODE>& x, Epi e) {
+    if constexpr (mb < Cfg<MODE>::MB) {
+        epi_row<MODE, mb>(x, e);
         // keep the scheduler from hoisting every accumulator read of the
         // epilogue at once (the next tile's loads are live here)
-        if ((mb & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+        if constexpr ((mb & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+        epi_rows<MODE, mb + 1>(x, e);
     }
-    }
+}
+
+template <int MODE>
+__device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
+    epi_rows<MODE>(x, epi_begin<MODE>(x, m0, n0));
 }
 
 template <int MODE>
@@ -607,8 +647,9 @@ __device__ __forceinline__ void mid_step(int s) {
 //   tile, the epilogue's scale DMAs); the wait + barrier sits at MB/2; the NA
 //   A DMAs of step s+3 follow it, spread evenly over the second half.  The
 //   order of the loads relative to the wait is the one sched::wait_at counts.
-template <int MODE, int S, bool FIRST, bool LAST, int mb>
-__device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, StepLoads L, v8i& f0, v8i& f1, v8i& f2) {
+template <int MODE, int S, bool FIRST, bool LAST, bool EPI, int mb>
+__device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, StepLoads L, Epi e, v8i& f0, v8i& f1,
+                                          v8i& f2) {
     using C = Cfg<MODE>;
     if constexpr (mb < C::MB) {
         constexpr int T = S & 1;
@@ -641,18 +682,28 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, Step
         } else {
             x.pre[nxt - C::MB] = read_a<MODE, SN>(x, nxt - C::MB);
         }
+        // the previous tile's row block mb, read out before this step's
+        // matrix ops overwrite its accumulators (the fences keep the reads
+        // ahead of them and this row block's work together)
+        if constexpr (EPI) {
+            __builtin_amdgcn_sched_barrier(0);
+            epi_row<MODE, mb>(x, e);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (mb % 3 == 0) mfma_row<MODE, T, mb, FIRST>(x, f0);
         else if constexpr (mb % 3 == 1) mfma_row<MODE, T, mb, FIRST>(x, f1);
         else mfma_row<MODE, T, mb, FIRST>(x, f2);
-        step_rows<MODE, S, FIRST, LAST, mb + 1>(x, s, cur, L, f0, f1, f2);
+        step_rows<MODE, S, FIRST, LAST, EPI, mb + 1>(x, s, cur, L, e, f0, f1, f2);
     }
 }
 
 // Stream step s = K tile k of tile j.  S = s % 4 is the LDS stage of the
 // tile, T = s % 2 the B register buffer.  FIRST / LAST: k == 0 / k == KI-1
 // (both for KI == 1).
-template <int MODE, int S, bool FIRST, bool LAST>
-__device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g) {
+// EPI: this first K step also runs the epilogue of the previous tile, prev.
+template <int MODE, int S, bool FIRST, bool LAST, bool EPI = false>
+__device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRef prev = TileRef{}) {
+    static_assert(!EPI || FIRST, "the previous tile's epilogue runs in the first K step");
     constexpr int T = S & 1;
     const int KI = x.KI;
     StepLoads L;
@@ -674,24 +725,27 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g) {
     akt = in0 ? kk : akt;
     L.ra = a_rsrc(x, a_m0 >= 0);
     L.abase = a_off + akt * BK;
+    Epi e{};
+    if constexpr (EPI) e = epi_begin<MODE>(x, prev.m0, prev.n0);
     realign_mx<MODE, T>(x);
     v8i f0 = x.pre[0], f1 = x.pre[1], f2;
-    step_rows<MODE, S, FIRST, LAST, 0>(x, s, g.t0, L, f0, f1, f2);
+    step_rows<MODE, S, FIRST, LAST, EPI, 0>(x, s, g.t0, L, e, f0, f1, f2);
 }
 
-// All K tiles of tile j, whose first K tile sits in stage P, then its
-// epilogue.  CASE = KI % 4 for KI >= 2, or 4 for KI == 1, is a compile-time
-// constant of the kernel: the first and last steps are peeled, the KI - 2
-// middle steps run as whole groups of four plus exactly (CASE - 2) & 3 more,
-// so every stage index and every wait count is a constant.
-template <int MODE, int P, int CASE>
-__device__ __forceinline__ void tile_body(Ctx<MODE>& x, int s0, Ring g) {
+// All K tiles of tile j, whose first K tile sits in stage P.  CASE = KI % 4
+// for KI >= 2, or 4 for KI == 1, is a compile-time constant of the kernel:
+// the first and last steps are peeled, the KI - 2 middle steps run as whole
+// groups of four plus exactly (CASE - 2) & 3 more, so every stage index and
+// every wait count is a constant.  PREV: the first step also stores tile
+// j - 1 (prev); without a deferred epilogue the tile stores itself at its end.
+template <int MODE, int P, int CASE, bool PREV>
+__device__ __forceinline__ void tile_body(Ctx<MODE>& x, int s0, Ring g, TileRef prev) {
     const int KI = x.KI;
     if constexpr (CASE == 4) {
-        kstep<MODE, P, true, true>(x, s0, 0, g);
+        kstep<MODE, P, true, true, PREV>(x, s0, 0, g, prev);
     } else {
         constexpr int REM = (CASE - 2) & 3;  // (KI - 2) % 4
-        kstep<MODE, P, true, false>(x, s0, 0, g);
+        kstep<MODE, P, true, false, PREV>(x, s0, 0, g, prev);
         int k = 1;
         for (; k + 4 <= KI - 1; k += 4) {
             kstep<MODE, (P + 1) & 3, false, false>(x, s0 + k, k, g);
@@ -704,13 +758,16 @@ __device__ __forceinline__ void tile_body(Ctx<MODE>& x, int s0, Ring g) {
         if constexpr (REM >= 3) kstep<MODE, (P + 3) & 3, false, false>(x, s0 + k + 2, k + 2, g);
         kstep<MODE, (P + CASE - 1) & 3, false, true>(x, s0 + KI - 1, KI - 1, g);
     }
-    mfma_drain<MODE>(x);
-    store_tile<MODE>(x, g.t0.m0, g.t0.n0);
+    if constexpr (!kDeferEpilogue<MODE>) {
+        mfma_drain<MODE>(x);
+        store_tile<MODE>(x, g.t0.m0, g.t0.n0);
+    }
 }
 
-template <int MODE, int P, int CASE>
-__device__ __forceinline__ void run_tile(Ctx<MODE>& x, int j, Ring& g) {
-    tile_body<MODE, P, CASE>(x, j * x.KI, g);
+template <int MODE, int P, int CASE, bool PREV>
+__device__ __forceinline__ void run_tile(Ctx<MODE>& x, int j, Ring& g, TileRef& prev) {
+    tile_body<MODE, P, CASE, PREV && kDeferEpilogue<MODE>>(x, j * x.KI, g, prev);
+    prev = g.t0;
     g = Ring{g.t1, g.t2, x.ref(j + 3)};
 }
 
@@ -784,15 +841,31 @@ __global__ void __launch_bounds__(Cfg<MODE>::NTHREADS, 1) gemm_a8w8_kernel(GemmA
 
     constexpr int R = CASE & 3;  // KI % 4
     constexpr int CYCLE = R == 0 ? 1 : R == 2 ? 2 : 4;
-    for (int j = 0; j < x.ntiles; j += CYCLE) {
-        run_tile<MODE, 0, CASE>(x, j, g);
+    // tile j's first K tile sits in stage (R j) % 4; the first cycle is
+    // peeled because its first tile has no predecessor to store
+    TileRef prev{};
+    run_tile<MODE, 0, CASE, false>(x, 0, g, prev);
+    if constexpr (CYCLE >= 2) {
+        if (1 < x.ntiles) run_tile<MODE, (R * 1) & 3, CASE, true>(x, 1, g, prev);
+    }
+    if constexpr (CYCLE == 4) {
+        if (2 < x.ntiles) run_tile<MODE, (R * 2) & 3, CASE, true>(x, 2, g, prev);
+        if (3 < x.ntiles) run_tile<MODE, (R * 3) & 3, CASE, true>(x, 3, g, prev);
+    }
+    for (int j = CYCLE; j < x.ntiles; j += CYCLE) {
+        run_tile<MODE, 0, CASE, true>(x, j, g, prev);
         if constexpr (CYCLE >= 2) {
-            if (j + 1 < x.ntiles) run_tile<MODE, (R * 1) & 3, CASE>(x, j + 1, g);
+            if (j + 1 < x.ntiles) run_tile<MODE, (R * 1) & 3, CASE, true>(x, j + 1, g, prev);
         }
         if constexpr (CYCLE == 4) {
-            if (j + 2 < x.ntiles) run_tile<MODE, (R * 2) & 3, CASE>(x, j + 2, g);
-            if (j + 3 < x.ntiles) run_tile<MODE, (R * 3) & 3, CASE>(x, j + 3, g);
+            if (j + 2 < x.ntiles) run_tile<MODE, (R * 2) & 3, CASE, true>(x, j + 2, g, prev);
+            if (j + 3 < x.ntiles) run_tile<MODE, (R * 3) & 3, CASE, true>(x, j + 3, g, prev);
         }
+    }
+    if constexpr (kDeferEpilogue<MODE>) {
+        // the last tile's epilogue
+        mfma_drain<MODE>(x);
+        store_tile<MODE>(x, prev.m0, prev.n0);
     }
 }
 

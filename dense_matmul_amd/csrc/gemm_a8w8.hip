@@ -713,16 +713,29 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRe
     L.rb = b_rsrc(x, L.bref.m0 >= 0);
     L.bbase = L.bref.b_off + L.bkt * 2048;
     // A DMA of stream step s+3: K tile k+3 of this tile or of one of the next
-    // two (selected without branches)
-    const int kk = k + 3;
-    const bool in0 = kk < KI, in1 = kk < 2 * KI;
-    int a_off = g.t2.a_off, a_m0 = g.t2.m0, akt = kk - 2 * KI;
-    a_off = in1 ? g.t1.a_off : a_off;
-    a_m0 = in1 ? g.t1.m0 : a_m0;
-    akt = in1 ? kk - KI : akt;
-    a_off = in0 ? g.t0.a_off : a_off;
-    a_m0 = in0 ? g.t0.m0 : a_m0;
-    akt = in0 ? kk : akt;
+    // two (selected without branches) -- or, when K = 128 (every step both
+    // the first and the last of its tile, s = j), K tile 0 of tile j + 3
+    int a_off, a_m0, akt;
+    if constexpr (FIRST && LAST) {
+        const TileRef t3 = x.ref(s + 3);
+        a_off = t3.a_off;
+        a_m0 = t3.m0;
+        akt = 0;
+    } else {
+        // sched::dma_ahead_tile(k, KI) (0, 1 or 2 for KI >= 2) and
+        // sched::dma_ahead_kt(k, KI), as two comparisons and selects
+        const int kk = k + 3;
+        const bool in0 = kk < KI, in1 = kk < 2 * KI;
+        a_off = g.t2.a_off;
+        a_m0 = g.t2.m0;
+        akt = kk - 2 * KI;
+        a_off = in1 ? g.t1.a_off : a_off;
+        a_m0 = in1 ? g.t1.m0 : a_m0;
+        akt = in1 ? kk - KI : akt;
+        a_off = in0 ? g.t0.a_off : a_off;
+        a_m0 = in0 ? g.t0.m0 : a_m0;
+        akt = in0 ? kk : akt;
+    }
     L.ra = a_rsrc(x, a_m0 >= 0);
     L.abase = a_off + akt * BK;
     Epi e{};
@@ -839,7 +852,7 @@ __global__ void __launch_bounds__(Cfg<MODE>::NTHREADS, 1) gemm_a8w8_kernel(GemmA
     x.pre[0] = read_a<MODE, 0>(x, 0);
     x.pre[1] = read_a<MODE, 0>(x, 1);
 
-    constexpr int R = CASE & 3;  // KI % 4
+    constexpr int R = sched::phase_advance(CASE);  // KI % 4
     constexpr int CYCLE = R == 0 ? 1 : R == 2 ? 2 : 4;
     // tile j's first K tile sits in stage (R j) % 4; the first cycle is
     // peeled because its first tile has no predecessor to store
@@ -890,7 +903,7 @@ static hipError_t launch_gemm(const GemmArgs& base, hipStream_t stream) {
     const int tiles = p.tiles_m * p.tiles_n;
     const int grid = tiles < device_cus() ? tiles : device_cus();
     const int ki = p.k / BK;
-    switch (ki == 1 ? 4 : ki & 3) {
+    switch (sched::case_of(ki)) {
         case 4: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 4>), dim3(grid), dim3(Cfg<MODE>::NTHREADS), 0, stream, p); break;
         case 0: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 0>), dim3(grid), dim3(Cfg<MODE>::NTHREADS), 0, stream, p); break;
         case 1: hipLaunchKernelGGL((gemm_a8w8_kernel<MODE, 1>), dim3(grid), dim3(Cfg<MODE>::NTHREADS), 0, stream, p); break;

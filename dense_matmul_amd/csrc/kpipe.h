@@ -65,6 +65,22 @@ constexpr int wait_at(int s, int k, int KI, int NA, int NB, int NSC) {
     return cap((s == 0 ? first_mid_wait(NA, NB) : mid_wait(NA, NB)) + extra * NSC);
 }
 
+// Target of the A DMA issued in K step k of a tile (KI K tiles per tile):
+// stream step s + 3, i.e. K tile dma_ahead_kt of the tile dma_ahead_tile
+// places further down the workgroup's list.  The kernel keeps the next two
+// tiles at hand; only K = 128 (KI = 1) reaches three tiles ahead.
+constexpr int dma_ahead_tile(int k, int KI) {
+    return k + 3 < KI ? 0 : k + 3 < 2 * KI ? 1 : k + 3 < 3 * KI ? 2 : 3;
+}
+constexpr int dma_ahead_kt(int k, int KI) { return k + 3 - KI * dma_ahead_tile(k, KI); }
+
+// The kernel is compiled per CASE = KI % 4 for KI >= 2 and CASE = 4 for
+// KI = 1 (every step both the first and the last of its tile).  Tile j's
+// first K tile is stream step j KI, in stage (j KI) % 4: the stage advances
+// by phase_advance(CASE) = KI % 4 per tile.
+constexpr int case_of(int KI) { return KI == 1 ? 4 : KI % 4; }
+constexpr int phase_advance(int CASE) { return CASE == 4 ? 1 : CASE; }
+
 // LDS stage holding stream K tile j, and the stage step s refills.
 constexpr int stage_of(int j) { return j % kStages; }
 constexpr int refill_stage(int s) { return (s + 3) % kStages; }

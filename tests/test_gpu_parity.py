@@ -290,3 +290,27 @@ def test_invalid_arguments_raise_value_error(dmm):
     with pytest.raises(ValueError):
         dmm.gemm_a8w8_ptpc(a[:, :200].contiguous(), b[:16, :200].contiguous(), s,
                            torch.ones(16, dtype=torch.float32, device=DEV))
+
+
+@pytest.mark.parametrize("mode", ["ptpc", "mxfp8", "blockscale"])
+@pytest.mark.parametrize("k", [128, 256, 384, 512, 640])
+def test_many_tiles_per_workgroup_every_k_phase(dmm, mode, k):
+    """More tiles than CUs, so every workgroup runs 2-3 tiles back to back,
+    for each K / 128 mod 4: the stage phase of a tile's first K tile cycles
+    through 1, 2 or 4 values and (ptpc, mxfp8) each tile's epilogue runs in
+    the next tile's first K step.  Exact-arithmetic inputs: sampled rows of
+    every tile row band must equal the oracle bitwise; two launches into a
+    NaN-poisoned C must be identical and leave no NaN."""
+    bm = 128 if mode == "blockscale" else 256
+    m, n = 18 * bm + 40, 8192 + 48  # partial last row and column tiles
+    announce("many tiles", mode, m, n, k)
+    qa, qb, sa, sb = exact_operands(mode, m, n, k, 7 * k + len(mode))
+    outs = run_poisoned(dmm, mode, qa, qb, sa, sb, 2)
+    diff = np.count_nonzero(outs[1] != outs[0])
+    assert diff == 0, f"launch 1 differs from launch 0 in {diff} elements"
+    assert not np.isnan(bits_to_f64(outs[0])).any(), "rows or columns left unwritten"
+    rows = np.unique(np.clip(np.concatenate([t * bm + np.array([0, 1, 15, 16, bm - 1]) for t in range(19)]), 0, m - 1))
+    ref = oracle.gemm_a8w8({"ptpc": 0, "blockscale": 1, "mxfp8": 2}[mode], qa, qb, sa, sb, rows=rows)
+    got = outs[0][rows]
+    mism = np.argwhere(got != ref)
+    assert mism.size == 0, f"{mode} {m}x{n}x{k}: {len(mism)} mismatches, first at {mism[:4].tolist()}"

@@ -37,6 +37,10 @@ int prologue_wait(int NA) { return sched::prologue_wait(NA); }
 int wait_at(int s, int k, int KI, int NA, int NB, int NSC) { return sched::wait_at(s, k, KI, NA, NB, NSC); }
 int stage_of(int j) { return sched::stage_of(j); }
 int refill_stage(int s) { return sched::refill_stage(s); }
+int dma_ahead_tile(int k, int KI) { return sched::dma_ahead_tile(k, KI); }
+int dma_ahead_kt(int k, int KI) { return sched::dma_ahead_kt(k, KI); }
+int case_of(int KI) { return sched::case_of(KI); }
+int phase_advance(int CASE) { return sched::phase_advance(CASE); }
 int dma_lds_byte(int b, int l) { return lds::dma_lds_byte(b, l); }
 int dma_row(int b, int l, int MB) { return lds::dma_row(b, l, MB); }
 int dma_chunk(int b, int l, int MB) { return lds::dma_chunk(b, l, MB); }
@@ -54,7 +58,7 @@ def shim(tmp_path_factory):
     subprocess.run(["g++", "-std=c++17", "-O1", "-shared", "-fPIC", "-I", CSRC, str(src), "-o", str(lib)], check=True)
     L = ctypes.CDLL(str(lib))
     for f in ("prologue_wait", "wait_at", "stage_of", "refill_stage", "dma_lds_byte", "dma_row", "dma_chunk",
-              "frag_byte"):
+              "frag_byte", "dma_ahead_tile", "dma_ahead_kt", "case_of", "phase_advance"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -158,6 +162,28 @@ def test_counts_are_exact(shim, mode):
         for ntiles in range(1, 4):
             for got, want in tight(shim, KI, ntiles, NA, NB, NSC):
                 assert got == want, f"{mode} KI={KI} tiles={ntiles}: wait {got}, loads after target {want}"
+
+
+def test_lookahead_dma_targets_stream_step_plus_three(shim):
+    """The A DMA of K step k lands on stream step s + 3: tile d ahead, K tile
+    kt, with d * KI + kt = k + 3.  The kernel holds the next two tiles; only
+    K = 128 (KI = 1, every step the first and last of its tile) reaches the
+    third, which the kernel computes separately."""
+    for KI in range(1, 41):
+        for k in range(KI):
+            d, kt = shim.dma_ahead_tile(k, KI), shim.dma_ahead_kt(k, KI)
+            assert 0 <= kt < KI and d * KI + kt == k + 3, (KI, k, d, kt)
+            assert (d == 3) == (KI == 1), (KI, k, d)
+
+
+def test_tile_phase_matches_stream_stage(shim):
+    """The kernel compiles one variant per CASE and gives tile j of a
+    workgroup the stage phase (phase_advance(CASE) * j) % 4; that must be the
+    stage of the tile's first K tile, stream step j * KI."""
+    for KI in range(1, 41):
+        adv = shim.phase_advance(shim.case_of(KI))
+        for j in range(12):
+            assert (adv * j) % 4 == shim.stage_of(j * KI), (KI, j)
 
 
 def test_k256_runs_the_tail_only_and_is_covered(shim):

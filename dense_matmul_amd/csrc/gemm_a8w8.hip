@@ -162,6 +162,16 @@ struct TileRef {
     int a_off, b_off;
 };
 
+// What the epilogue of one tile needs besides the accumulators.
+struct Epi {
+    v4f eas[4], ebs[4];  // ptpc: a_scale of this lane's rows, b_scale of its columns
+    int row;             // first row this lane writes
+    int col;             // column of this lane's 8 values
+    uint32_t cdrop;      // 0, or 2^31 when that column group lies at or past N: added to the
+                         // store offsets (all below 2^31), it puts them past the C descriptor,
+                         // so the hardware drops the stores without a branch
+};
+
 template <int MODE>
 struct Ctx {
     using C = Cfg<MODE>;
@@ -193,6 +203,8 @@ struct Ctx {
     v4f sfa[2][C::MB / 4];
     float sfb[2];
     v4f bp[2][C::NBW];
+    // the epilogue of the tile being stored (ptpc, mxfp8)
+    Epi ep;
 
     // Tile j of this workgroup's list with the buffer descriptors its loads
     // use (see TileRef).
@@ -284,14 +296,19 @@ __device__ __forceinline__ void issue_b(Ctx<MODE>& x, TileRef r, int kt) {
     b_scales<MODE, T>(x, r, kt);
 }
 
-// ptpc epilogue scales of the tile at (m0, n0): NSC = 2 DMAs per wave into
-// the wave's own 2 KiB of g_lds_scale (a_scale of rows m0 .. m0+255, then
-// b_scale of columns n0 .. n0+255; entries past M or N read as zero).
+// ptpc epilogue scales of tile t: NSC = 2 DMAs per wave into the wave's own
+// 2 KiB of g_lds_scale (a_scale of rows m0 .. m0+255, then b_scale of
+// columns n0 .. n0+255; entries past M or N read as zero, and a tile past
+// the end of the list moves nothing).
 template <int MODE>
-__device__ __forceinline__ void issue_epilogue_scales(Ctx<MODE>& x, int m0, int n0) {
+__device__ __forceinline__ void issue_epilogue_scales(Ctx<MODE>& x, TileRef t) {
     if constexpr (MODE == MODE_PTPC) {
-        const __amdgpu_buffer_rsrc_t rsa = make_rsrc((const float*)x.sa + m0, (uint32_t)(x.M - m0) * 4u);
-        const __amdgpu_buffer_rsrc_t rsb = make_rsrc((const float*)x.sb + n0, (uint32_t)(x.N - n0) * 4u);
+        const bool valid = t.m0 >= 0;
+        const int m0 = valid ? t.m0 : 0, n0 = valid ? t.n0 : 0;
+        const __amdgpu_buffer_rsrc_t rsa =
+            make_rsrc((const float*)x.sa + m0, valid ? (uint32_t)(x.M - m0) * 4u : 0u);
+        const __amdgpu_buffer_rsrc_t rsb =
+            make_rsrc((const float*)x.sb + n0, valid ? (uint32_t)(x.N - n0) * 4u : 0u);
         lds_char* dst = x.lds.scale + x.w * 2048;
         lds_dma16(rsa, dst, 16 * x.lane);
         lds_dma16(rsb, dst + 1024, 16 * x.lane);
@@ -378,21 +395,23 @@ __device__ __forceinline__ void fold_products(Ctx<MODE>& x) {
     }
 }
 
-template <int MODE, int T, int mb, bool FIRST>
-__device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
+// Block (mb, nb) of a K tile, ptpc / mxfp8 (AGPR accumulators).
+template <int MODE, int T, int mb, int nb, bool FIRST>
+__device__ __forceinline__ void mfma_block(Ctx<MODE>& x, const v8i& a) {
     if constexpr (MODE == MODE_PTPC) {
-        static_for<0, Cfg<MODE>::NBW>([&](auto NBc) {
-            constexpr int nb = decltype(NBc)::value;
-            mfma_acc<FIRST>(x.acc[mb][nb], x.bq[T][nb], a);
-        });
-    } else if constexpr (MODE == MODE_MXFP8) {
+        mfma_acc<FIRST>(x.acc[mb][nb], x.bq[T][nb], a);
+    } else {
+        static_assert(MODE == MODE_MXFP8, "blockscale issues its row blocks as a whole");
         // src1 (A) scale: byte mb % 4 of word mb / 4 of the realigned bytes;
         // src0 (B) scale: byte 0 of the block's register
-        const int sa_word = x.sxa[T][mb / 4];
-        static_for<0, Cfg<MODE>::NBW>([&](auto NBc) {
-            constexpr int nb = decltype(NBc)::value;
-            mfma_scaled_acc<FIRST, 0, mb % 4>(x.acc[mb][nb], x.bq[T][nb], a, x.sxb[nb], sa_word);
-        });
+        mfma_scaled_acc<FIRST, 0, mb % 4>(x.acc[mb][nb], x.bq[T][nb], a, x.sxb[nb], x.sxa[T][mb / 4]);
+    }
+}
+
+template <int MODE, int T, int mb, bool FIRST>
+__device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
+    if constexpr (MODE != MODE_BLOCKSCALE) {
+        static_for<0, Cfg<MODE>::NBW>([&](auto NBc) { mfma_block<MODE, T, mb, decltype(NBc)::value, FIRST>(x, a); });
     } else {
         // blockscale: one fp32 scale per (row, 128-wide K tile) times the
         // B block's scale multiplies each K tile's products before they are
@@ -457,28 +476,31 @@ __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
 // row segments: store 0 rows MB (i % 8) + mb, store 1 rows MB (i % 8 + 8) +
 // mb, lane i writing pair i / 8 of the row.
 //
-// ptpc and mxfp8 run a tile's epilogue inside the first K step of the
-// workgroup's next tile: row block mb is scaled, converted and stored just
-// before that step's first matrix ops overwrite its accumulators, so the
-// conversion overlaps matrix work and the stores spread over the step.  The
-// workgroup's last tile is stored after its loop; blockscale (accumulators
-// in VGPRs, written by the compiler) stores each tile at its end.
-
-// What the epilogue of one tile needs besides the accumulators.
-struct Epi {
-    v4f eas[4], ebs[4];  // ptpc: a_scale of this lane's rows, b_scale of its columns
-    int row;             // first row this lane writes
-    int col;             // column of this lane's 8 values
-    int col_ok;          // that column group lies below N
-};
+// ptpc and mxfp8 (accumulators in AGPRs) spread a tile's epilogue over two
+// K steps, so that its conversion work and its stores overlap matrix ops
+// instead of piling up between them.  With two or more K tiles per tile:
+//   * the tile's last K step stores row blocks 0..7, each as soon as its
+//     final matrix ops are done: row block r in eight phases, one after each
+//     matrix op of row blocks 2r+1 and 2r+2 (row block 7's second half after
+//     the step's last matrix op);
+//   * the next tile's first K step stores row blocks 8..15, each before
+//     that step's matrix ops overwrite its accumulators: row block r after
+//     the matrix ops of row blocks 2(r-8) and 2(r-8)+1.
+// With one K tile per tile both halves would land in the same step, so
+// there the whole tile is stored in the next tile's first step, each row
+// block just ahead of the matrix ops that overwrite it.  The workgroup's
+// last rows are stored after its loop.  Blockscale (accumulators in VGPRs,
+// written by the compiler) stores each tile at its end.
 
 // Start the epilogue of the tile at (m0, n0).  ptpc reads its scales from
-// this wave's LDS region: the scale DMAs (issue_epilogue_scales, in the
-// tile's last K step) were followed only by the NA A-tile DMAs of that step,
-// so vmcnt(NA) covers them; each wave reads only the region it filled.  The
-// reads are written out so that the compiler, which cannot tell the A-tile
-// DMAs still in flight from writes to this region, does not drain the whole
-// prefetch pipeline (vmcnt(0)) before them.
+// this wave's LDS region, where the scale DMAs (issue_epilogue_scales) put
+// them: with one K tile per tile in the previous step, before its last NA
+// A-tile DMAs; otherwise in the previous tile's last step (or the
+// prologue), again followed by at least the NA A-tile DMAs of the step
+// before this one.  So vmcnt(NA) covers them; each wave reads only the
+// region it filled.  The reads are written out so that the compiler, which
+// cannot tell the A-tile DMAs still in flight from writes to this region,
+// does not drain the whole prefetch pipeline (vmcnt(0)) before them.
 template <int MODE>
 __device__ __forceinline__ Epi epi_begin(Ctx<MODE>& x, int m0, int n0) {
     using C = Cfg<MODE>;
@@ -486,7 +508,7 @@ __device__ __forceinline__ Epi epi_begin(Ctx<MODE>& x, int m0, int n0) {
     if constexpr (C::NBW == 4) {
         const int nb_of_lane = 2 * (x.i >> 3) + (x.g & 1);
         e.col = n0 + C::WN * x.w + 16 * nb_of_lane + 8 * (x.g >> 1);
-        e.col_ok = n0 + C::WN * x.w + 16 * nb_of_lane < x.N;
+        e.cdrop = n0 + C::WN * x.w + 16 * nb_of_lane < x.N ? 0u : 0x80000000u;
         e.row = m0 + C::MB * (x.i & 7);
     } else {
         // one block pair per wave: the 4 lanes of row MB i + mb hold its
@@ -494,7 +516,7 @@ __device__ __forceinline__ Epi epi_begin(Ctx<MODE>& x, int m0, int n0) {
         // 128-byte segment, so these stores go through the L2, which merges
         // the halves
         e.col = n0 + C::WN * x.w + 16 * (x.g & 1) + 8 * (x.g >> 1);
-        e.col_ok = n0 + C::WN * x.w + 16 * (x.g & 1) < x.N;
+        e.cdrop = n0 + C::WN * x.w + 16 * (x.g & 1) < x.N ? 0u : 0x80000000u;
         e.row = m0 + C::MB * x.i;
     }
     if constexpr (MODE == MODE_PTPC) {
@@ -520,63 +542,97 @@ __device__ __forceinline__ Epi epi_begin(Ctx<MODE>& x, int m0, int n0) {
     return e;
 }
 
+// One row block's epilogue (ptpc, mxfp8) in eight phases, so that it can be
+// spread over eight matrix ops:
+//   0, 1  read the accumulators of column-block pair 0 / 1
+//   2..5  ptpc scaling, pair (PH - 2) / 2, first / second block of the pair
+//   6     bf16 conversion and permlane16 swaps of both pairs
+//   7     DPP exchange and the two stores
+struct EpiRow {
+    v4f u[2], v[2];
+    v4i d[2];
+};
+
+template <int MODE, int r, int PH>
+__device__ __forceinline__ void epi_phase(Ctx<MODE>& x, const Epi& e, EpiRow& q) {
+    using C = Cfg<MODE>;
+    static_assert(kDeferEpilogue<MODE> && C::NBW == 4, "AGPR accumulators, two block pairs per wave");
+    if constexpr (PH < 2) {
+        // explicit reads, so that the register allocator keeps each
+        // accumulator where the next tile's matrix ops will write it
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(q.u[PH][c]) : "a"(x.acc[r][2 * PH][c]));
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(q.v[PH][c]) : "a"(x.acc[r][2 * PH + 1][c]));
+        }
+    } else if constexpr (PH < 6) {
+        if constexpr (MODE == MODE_PTPC) {
+            constexpr int pair = (PH - 2) / 2;
+            const float sa = e.eas[r / 4][r % 4];
+            if constexpr (PH % 2 == 0) q.u[pair] = q.u[pair] * sa * e.ebs[2 * pair];
+            else q.v[pair] = q.v[pair] * sa * e.ebs[2 * pair + 1];
+        }
+    } else if constexpr (PH == 6) {
+#pragma unroll
+        for (int pair = 0; pair < 2; ++pair) {
+            const uint32_t u0 = pack_bf16(q.u[pair][0], q.u[pair][1]), u1 = pack_bf16(q.u[pair][2], q.u[pair][3]);
+            const uint32_t v0 = pack_bf16(q.v[pair][0], q.v[pair][1]), v1 = pack_bf16(q.v[pair][2], q.v[pair][3]);
+            const auto s0 = __builtin_amdgcn_permlane16_swap(u0, v0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(u1, v1, false, false);
+            q.d[pair] = (v4i){(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(x.c, (uint32_t)x.M * (uint32_t)x.N * 2u);
+        v4i lo, hi;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            lo[c] = __builtin_amdgcn_update_dpp(q.d[0][c], q.d[1][c], kDppRowRor8, 0xF, 0xC, false);
+            hi[c] = __builtin_amdgcn_update_dpp(q.d[1][c], q.d[0][c], kDppRowRor8, 0xF, 0x3, false);
+        }
+        // C is written once and never read back, so whole-line stores
+        // stream past the caches that hold the A and B panels; rows at or
+        // past M, and column groups at or past N (cdrop), fall outside the
+        // buffer and are dropped
+        const uint32_t o0 = (uint32_t)(((e.row + r) * x.N + e.col) * 2) + e.cdrop;
+        const uint32_t o1 = (uint32_t)(((e.row + 8 * C::MB + r) * x.N + e.col) * 2) + e.cdrop;
+        __builtin_amdgcn_raw_buffer_store_b128(lo, rc, o0, 0, kStoreStream);
+        __builtin_amdgcn_raw_buffer_store_b128(hi, rc, o1, 0, kStoreStream);
+    }
+}
+
+template <int MODE, int r, int PH = 0>
+__device__ __forceinline__ void epi_phases(Ctx<MODE>& x, const Epi& e, EpiRow& q) {
+    if constexpr (PH < 8) {
+        epi_phase<MODE, r, PH>(x, e, q);
+        epi_phases<MODE, r, PH + 1>(x, e, q);
+    }
+}
+
 // Scale, convert and store row block mb of the tile whose accumulators are
 // live.
 template <int MODE, int mb>
-__device__ __forceinline__ void epi_row(Ctx<MODE>& x, Epi e) {
+__device__ __forceinline__ void epi_row(Ctx<MODE>& x, const Epi& e) {
     using C = Cfg<MODE>;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(x.c, (uint32_t)x.M * (uint32_t)x.N * 2u);
-    v4i d[C::NBW / 2];
-#pragma unroll
-    for (int pair = 0; pair < C::NBW / 2; ++pair) {
-        const int nb0 = 2 * pair, nb1 = 2 * pair + 1;
-        v4f u, v;
-        if constexpr (kDeferEpilogue<MODE>) {
-            // explicit reads, so that the register allocator keeps each
-            // accumulator where the next tile's matrix ops will write it
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(u[c]) : "a"(x.acc[mb][nb0][c]));
-                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[c]) : "a"(x.acc[mb][nb1][c]));
-            }
-        } else {
-            u = x.acc[mb][nb0];
-            v = x.acc[mb][nb1];
-        }
-        if constexpr (MODE == MODE_PTPC) {
-            const float sa = e.eas[mb / 4][mb % 4];
-            u = u * sa * e.ebs[nb0];
-            v = v * sa * e.ebs[nb1];
-        }
+    if constexpr (kDeferEpilogue<MODE>) {
+        EpiRow q;
+        epi_phases<MODE, mb>(x, e, q);
+    } else {
+        // blockscale: one block pair per wave, accumulators in VGPRs
+        static_assert(C::NBW == 2, "one block pair per wave");
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(x.c, (uint32_t)x.M * (uint32_t)x.N * 2u);
+        const v4f u = x.acc[mb][0], v = x.acc[mb][1];
         const uint32_t u0 = pack_bf16(u[0], u[1]), u1 = pack_bf16(u[2], u[3]);
         const uint32_t v0 = pack_bf16(v[0], v[1]), v1 = pack_bf16(v[2], v[3]);
         const auto s0 = __builtin_amdgcn_permlane16_swap(u0, v0, false, false);
         const auto s1 = __builtin_amdgcn_permlane16_swap(u1, v1, false, false);
-        d[pair] = (v4i){(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
-    }
-    // rows at or past M fall outside the buffer and are dropped
-    if constexpr (C::NBW == 4) {
-        v4i lo, hi;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            lo[q] = __builtin_amdgcn_update_dpp(d[0][q], d[1][q], kDppRowRor8, 0xF, 0xC, false);
-            hi[q] = __builtin_amdgcn_update_dpp(d[1][q], d[0][q], kDppRowRor8, 0xF, 0x3, false);
-        }
-        // C is written once and never read back, so whole-line stores
-        // stream past the caches that hold the A and B panels
-        if (e.col_ok) {
-            __builtin_amdgcn_raw_buffer_store_b128(lo, rc, ((e.row + mb) * x.N + e.col) * 2, 0, kStoreStream);
-            __builtin_amdgcn_raw_buffer_store_b128(hi, rc, ((e.row + 8 * C::MB + mb) * x.N + e.col) * 2, 0,
-                                                   kStoreStream);
-        }
-    } else {
-        if (e.col_ok) __builtin_amdgcn_raw_buffer_store_b128(d[0], rc, ((e.row + mb) * x.N + e.col) * 2, 0, 0);
+        const v4i d = (v4i){(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+        __builtin_amdgcn_raw_buffer_store_b128(d, rc, (uint32_t)(((e.row + mb) * x.N + e.col) * 2) + e.cdrop, 0, 0);
     }
 }
 
 // The whole epilogue of a tile at once.
 template <int MODE, int mb = 0>
-__device__ __forceinline__ void epi_rows(Ctx<MODE>& x, Epi e) {
+__device__ __forceinline__ void epi_rows(Ctx<MODE>& x, const Epi& e) {
     if constexpr (mb < Cfg<MODE>::MB) {
         epi_row<MODE, mb>(x, e);
         // keep the scheduler from hoisting every accumulator read of the
@@ -613,25 +669,43 @@ struct StepLoads {
     int bbase, abase;  // byte offsets of the B event's and the A DMA's K tile
     int bkt;           // K tile of the B event (for the mode's scales)
     TileRef bref;
+    TileRef enext;     // the next tile, whose epilogue scales a tile's last step loads
 };
 
 // The middle of a step.  RAW: K tile s+1 has landed in every wave's share of
 // LDS.  WAR: every wave's reads of stage (S+3)%4 (stream step s-1) have
 // retired, so the A DMAs that follow may refill it.  The count is
-// sched::wait_at(s, k, KI, ...), specialised: only the stream's very first
-// step differs from the rest of its kind.
+// sched::wait_at(s, k, KI, ...), specialised (FIRST && LAST is KI == 1):
+// only the stream's very first step differs from the rest of its kind.
 template <int MODE, int S, bool FIRST, bool LAST>
 __device__ __forceinline__ void mid_step(int s) {
     using C = Cfg<MODE>;
     constexpr int NA = C::NA, NB = C::NB, NSC = C::NSC;
-    constexpr int XT = (LAST ? 1 : 0) + (FIRST ? 1 : 0);
+    constexpr int XT = FIRST && LAST ? 2 : FIRST ? 1 : 0;
     if constexpr (FIRST) {
         if (s == 0) wait_vm_lgkm0<sched::cap(sched::first_mid_wait(NA, NB) + (LAST ? NSC : 0))>();
         else wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB) + XT * NSC)>();
     } else {
-        wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB) + XT * NSC)>();
+        wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB))>();
     }
     __builtin_amdgcn_s_barrier();
+}
+
+// The four matrix ops of row block mb, each followed by one phase of the
+// epilogue of row block r (phases PH0 .. PH0+3).  With R0 (the first phase
+// of a row block whose final matrix ops ran earlier in this step) the
+// accumulator reads wait out the matrix-op result latency: the compiler
+// cannot see that hazard across the asm statements.
+template <int MODE, int T, int mb, bool FIRST, int r, int PH0, bool R0>
+__device__ __forceinline__ void mfma_row_epi(Ctx<MODE>& x, const v8i& a, EpiRow& q) {
+    static_for<0, 4>([&](auto NBc) {
+        constexpr int nb = decltype(NBc)::value;
+        mfma_block<MODE, T, mb, nb, FIRST>(x, a);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (R0 && nb == 0) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+        epi_phase<MODE, r, PH0 + nb>(x, x.ep, q);
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 // Row blocks mb .. MB-1 of a step; each row block's four matrix ops are
@@ -643,13 +717,19 @@ __device__ __forceinline__ void mid_step(int s) {
 //   fragments, read in the last two row blocks, come after this step's
 //   barrier.
 // - The next B event is spread over the first half (2 NBW / (MB/2) fragment
-//   loads per row block, then the mode's scales and, in the last K step of a
-//   tile, the epilogue's scale DMAs); the wait + barrier sits at MB/2; the NA
-//   A DMAs of step s+3 follow it, spread evenly over the second half.  The
-//   order of the loads relative to the wait is the one sched::wait_at counts.
-template <int MODE, int S, bool FIRST, bool LAST, bool EPI, int mb>
-__device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, StepLoads L, Epi e, v8i& f0, v8i& f1,
-                                          v8i& f2) {
+//   loads per row block, then the mode's scales and, with one K tile per
+//   tile, this tile's epilogue scale DMAs); the wait + barrier sits at MB/2,
+//   followed in a tile's last step (two or more K tiles per tile) by the
+//   next tile's epilogue scale DMAs; the NA A DMAs of step s+3 follow,
+//   spread evenly over the second half.  The order of the loads relative to
+//   the wait is the one sched::wait_at counts.
+// - EPM, the epilogue carried by the step (ptpc, mxfp8): 0 none; 1 the whole
+//   previous tile, each row block just ahead of its matrix ops (one K tile
+//   per tile); 2 row blocks 8..15 of the previous tile (first K step);
+//   3 row blocks 0..7 of this tile (last K step).
+template <int MODE, int S, bool FIRST, bool LAST, int EPM, int mb>
+__device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, StepLoads L, EpiRow& q, v8i& f0,
+                                          v8i& f1, v8i& f2) {
     using C = Cfg<MODE>;
     if constexpr (mb < C::MB) {
         constexpr int T = S & 1;
@@ -665,10 +745,13 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, Step
             if constexpr (BPR == 2) b_piece<MODE, T ^ 1, mb * BPR + 1>(x, L.rb, L.bbase);
             if constexpr (mb == HALF - 1) {
                 b_scales<MODE, T ^ 1>(x, L.bref, L.bkt);
-                if constexpr (LAST) issue_epilogue_scales<MODE>(x, cur.m0, cur.n0);
+                if constexpr (FIRST && LAST) issue_epilogue_scales<MODE>(x, cur);
             }
         }
-        if constexpr (mb == HALF) mid_step<MODE, S, FIRST, LAST>(s);
+        if constexpr (mb == HALF) {
+            mid_step<MODE, S, FIRST, LAST>(s);
+            if constexpr (LAST && !FIRST) issue_epilogue_scales<MODE>(x, L.enext);
+        }
         // NA DMAs spread over the second half, the first at mb = HALF
         static_assert(C::NA <= HALF && HALF % C::NA == 0, "A DMAs spread evenly over the second half");
         constexpr int DSTRIDE = HALF / C::NA;
@@ -682,28 +765,50 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, Step
         } else {
             x.pre[nxt - C::MB] = read_a<MODE, SN>(x, nxt - C::MB);
         }
-        // the previous tile's row block mb, read out before this step's
-        // matrix ops overwrite its accumulators (the fences keep the reads
-        // ahead of them and this row block's work together)
-        if constexpr (EPI) {
+        const v8i& fa = mb % 3 == 0 ? f0 : mb % 3 == 1 ? f1 : f2;
+        if constexpr (EPM == 1) {
+            // the previous tile's row block mb, read out before this step's
+            // matrix ops overwrite its accumulators (the fences keep the
+            // reads ahead of them and this row block's work together)
             __builtin_amdgcn_sched_barrier(0);
-            epi_row<MODE, mb>(x, e);
+            epi_row<MODE, mb>(x, x.ep);
             __builtin_amdgcn_sched_barrier(0);
+            mfma_row<MODE, T, mb, FIRST>(x, fa);
+        } else if constexpr (EPM == 2) {
+            // row block 8 + mb/2 of the previous tile: its reads (phases
+            // 0, 1) come before this step's matrix ops of that row block
+            mfma_row_epi<MODE, T, mb, FIRST, 8 + mb / 2, 4 * (mb % 2), false>(x, fa, q);
+        } else if constexpr (EPM == 3 && mb > 0) {
+            // row block (mb-1)/2 of this tile, final since row block
+            // (mb-1)/2's matrix ops earlier in this step
+            mfma_row_epi<MODE, T, mb, FIRST, (mb - 1) / 2, 4 * (1 - mb % 2), mb % 2 == 1>(x, fa, q);
+        } else {
+            mfma_row<MODE, T, mb, FIRST>(x, fa);
         }
-        if constexpr (mb % 3 == 0) mfma_row<MODE, T, mb, FIRST>(x, f0);
-        else if constexpr (mb % 3 == 1) mfma_row<MODE, T, mb, FIRST>(x, f1);
-        else mfma_row<MODE, T, mb, FIRST>(x, f2);
-        step_rows<MODE, S, FIRST, LAST, EPI, mb + 1>(x, s, cur, L, e, f0, f1, f2);
+        step_rows<MODE, S, FIRST, LAST, EPM, mb + 1>(x, s, cur, L, q, f0, f1, f2);
+    } else if constexpr (EPM == 3) {
+        // the second half of row block 7 (MB = 16)
+        static_assert(Cfg<MODE>::MB == 16, "row blocks 0..7 of 16 in the last K step");
+        __builtin_amdgcn_sched_barrier(0);
+        epi_phase<MODE, 7, 4>(x, x.ep, q);
+        epi_phase<MODE, 7, 5>(x, x.ep, q);
+        epi_phase<MODE, 7, 6>(x, x.ep, q);
+        epi_phase<MODE, 7, 7>(x, x.ep, q);
     }
 }
 
 // Stream step s = K tile k of tile j.  S = s % 4 is the LDS stage of the
 // tile, T = s % 2 the B register buffer.  FIRST / LAST: k == 0 / k == KI-1
-// (both for KI == 1).
-// EPI: this first K step also runs the epilogue of the previous tile, prev.
-template <int MODE, int S, bool FIRST, bool LAST, bool EPI = false>
+// (both for KI == 1).  PREV: a tile precedes this one in the workgroup's
+// list, so a first K step also stores (part of) it.
+template <int MODE, int S, bool FIRST, bool LAST, bool PREV = false>
 __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRef prev = TileRef{}) {
-    static_assert(!EPI || FIRST, "the previous tile's epilogue runs in the first K step");
+    static_assert(!PREV || FIRST, "the previous tile's epilogue runs in the first K step");
+    constexpr int EPM = !kDeferEpilogue<MODE> ? 0
+                        : FIRST && LAST       ? (PREV ? 1 : 0)
+                        : FIRST               ? (PREV ? 2 : 0)
+                        : LAST                ? 3
+                                              : 0;
     constexpr int T = S & 1;
     const int KI = x.KI;
     StepLoads L;
@@ -712,6 +817,7 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRe
     L.bkt = LAST ? 0 : k + 1;
     L.rb = b_rsrc(x, L.bref.m0 >= 0);
     L.bbase = L.bref.b_off + L.bkt * 2048;
+    L.enext = g.t1;
     // A DMA of stream step s+3: K tile k+3 of this tile or of one of the next
     // two (selected without branches) -- or, when K = 128 (every step both
     // the first and the last of its tile, s = j), K tile 0 of tile j + 3
@@ -738,11 +844,12 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRe
     }
     L.ra = a_rsrc(x, a_m0 >= 0);
     L.abase = a_off + akt * BK;
-    Epi e{};
-    if constexpr (EPI) e = epi_begin<MODE>(x, prev.m0, prev.n0);
+    if constexpr (EPM == 1) x.ep = epi_begin<MODE>(x, prev.m0, prev.n0);
+    if constexpr (EPM == 3) x.ep = epi_begin<MODE>(x, g.t0.m0, g.t0.n0);
     realign_mx<MODE, T>(x);
     v8i f0 = x.pre[0], f1 = x.pre[1], f2;
-    step_rows<MODE, S, FIRST, LAST, EPI, 0>(x, s, g.t0, L, e, f0, f1, f2);
+    EpiRow q;
+    step_rows<MODE, S, FIRST, LAST, EPM, 0>(x, s, g.t0, L, q, f0, f1, f2);
 }
 
 // All K tiles of tile j, whose first K tile sits in stage P.  CASE = KI % 4
@@ -831,10 +938,13 @@ __global__ void __launch_bounds__(Cfg<MODE>::NTHREADS, 1) gemm_a8w8_kernel(GemmA
 
     Ring g{x.ref(0), x.ref(1), x.ref(2)};
 
-    // prologue: Bev(0), A(0), A(1), A(2) of the stream
+    // prologue: Bev(0), [E(0),] A(0), A(1), A(2) of the stream
     {
         const int KI = x.KI;
         issue_b<MODE, 0>(x, g.t0, 0);
+        // with two or more K tiles per tile, the epilogue scales of a tile
+        // are loaded a tile ahead: tile 0's here
+        if constexpr (CASE != 4) issue_epilogue_scales<MODE>(x, g.t0);
         auto pos = [&](int sidx, int& kt) {
             if (sidx < KI) { kt = sidx; return g.t0; }
             if (sidx < 2 * KI) { kt = sidx - KI; return g.t1; }
@@ -876,9 +986,11 @@ __global__ void __launch_bounds__(Cfg<MODE>::NTHREADS, 1) gemm_a8w8_kernel(GemmA
         }
     }
     if constexpr (kDeferEpilogue<MODE>) {
-        // the last tile's epilogue
+        // the last tile's epilogue (its row blocks 8..15 with two or more K
+        // tiles per tile: the last K step stored the others)
         mfma_drain<MODE>(x);
-        store_tile<MODE>(x, prev.m0, prev.n0);
+        if constexpr (CASE == 4) store_tile<MODE>(x, prev.m0, prev.n0);
+        else epi_rows<MODE, 8>(x, x.ep);
     }
 }
 

@@ -11,15 +11,20 @@
 // A workgroup walks a stream of K tiles: all K tiles of its first output
 // tile, then all of the next, and so on (s = stream position, k = K tile
 // within the output tile, KI = K / 128).  Per wave, in issue order:
-//   prologue : Bev(0), A(0), A(1), A(2);
+//   prologue : Bev(0), [E(tile 0) if KI >= 2,] A(0), A(1), A(2);
 //              wait vmcnt(prologue_wait) lgkmcnt(0); s_barrier
-//   step s   : top : Bev(s+1) [, E if k == KI-1]
+//   step s   : top : Bev(s+1) [, E(this tile) if KI == 1]
 //              mid : wait vmcnt(c(s)) lgkmcnt(0); s_barrier;
+//                    [E(next tile) if k == KI-1 and KI >= 2;]
 //                    A(s+3) into LDS stage (s+3) % 4
-//              end : [stores of the output tile if k == KI-1]
+//              stores of an output tile are spread over its step k == KI-1
+//              and the next tile's step k == 0 (all in k == 0 if KI == 1)
 // A(j) is the global->LDS DMA of stream K tile j (NA loads per wave), Bev(j)
 // the direct-to-register loads of its B fragments plus any per-K-tile scales
-// (NB loads), E the ptpc epilogue's scale loads (NSC loads).  Every step
+// (NB loads), E the ptpc epilogue's scale loads (NSC loads).  E is read at
+// the top of the step that starts storing its tile, so with KI >= 2 a
+// tile's last step loads the next tile's (the prologue tile 0's); with
+// KI == 1 each step loads its own tile's and stores the previous one.  Every step
 // issues its loads unconditionally: a position past the end of the stream
 // goes through a zero-length buffer descriptor, moves no data and still
 // counts in vmcnt.  So the counts below depend only on where a step sits in
@@ -56,12 +61,14 @@ constexpr int first_mid_wait(int NA, int NB) { return NA + NB; }
 
 // Mid-step wait of step s >= 1: A(s+1) (issued at step s-2, or in the
 // prologue for s = 1) is followed by Bev(s), A(s+2) and Bev(s+1), plus NSC
-// for each of steps s-1 and s that closed its output tile.
+// for each E issued in between: KI == 1, the E of steps s-1 and s;
+// otherwise the one of step s-1 when it closed its output tile (k == 0) --
+// an E of step s-2 precedes that step's A DMAs.
 constexpr int mid_wait(int NA, int NB) { return 2 * NB + NA; }
 
 // The full rule, as the kernel applies it.
 constexpr int wait_at(int s, int k, int KI, int NA, int NB, int NSC) {
-    const int extra = (k == KI - 1 ? 1 : 0) + (s > 0 && k == 0 ? 1 : 0);
+    const int extra = KI == 1 ? 1 + (s > 0 ? 1 : 0) : (s > 0 && k == 0 ? 1 : 0);
     return cap((s == 0 ? first_mid_wait(NA, NB) : mid_wait(NA, NB)) + extra * NSC);
 }
 

@@ -73,21 +73,28 @@ def program(L, KI, ntiles, NA, NB, NSC, wait_fn=None):
     ("read", stream tile), ("read_done",) -- the same for every wave."""
     wait_fn = wait_fn or (lambda s, k: L.wait_at(s, k, KI, NA, NB, NSC))
     S = KI * ntiles
-    ev = [("load", "B", 0, NB), ("load", "A", 0, NA), ("load", "A", 1, NA), ("load", "A", 2, NA),
-          ("wait", L.prologue_wait(NA)), ("barrier",), ("read", 0)]
+    ev = [("load", "B", 0, NB)]
+    if KI > 1 and NSC:
+        ev.append(("load", "E", 0, NSC))  # tile 0's epilogue scales
+    ev += [("load", "A", 0, NA), ("load", "A", 1, NA), ("load", "A", 2, NA),
+           ("wait", L.prologue_wait(NA)), ("barrier",), ("read", 0)]
     for s in range(S):
         k = s % KI
+        if k == 0 and s > 0:
+            ev.append(("store", 16 if KI > 1 else 32))  # (part of) the previous tile
         ev.append(("load", "B", s + 1, NB))
-        if k == KI - 1 and NSC:
-            ev.append(("load", "E", s, NSC))
+        if KI == 1 and NSC:
+            ev.append(("load", "E", s, NSC))  # this tile's, before the wait
         ev.append(("read", s))  # first half of the row blocks
         ev.append(("wait", wait_fn(s, k)))
         ev.append(("barrier",))
+        if k == KI - 1 and KI > 1 and NSC:
+            ev.append(("load", "E", s // KI + 1, NSC))  # the next tile's, after the wait
         ev.append(("load", "A", s + 3, NA))
         ev.append(("read", s))  # second half
         ev.append(("read", s + 1))  # the next tile's first two fragments
-        if k == KI - 1:
-            ev.append(("store", 32))
+        if k == KI - 1 and KI > 1:
+            ev.append(("store", 16))  # row blocks 0..7 of this tile
     return ev
 
 

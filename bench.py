@@ -214,6 +214,7 @@ def extra_shapes(dmm, torch, args):
         ("ptpc_16384x7168x512", "ptpc", 16384, 7168, 512, 21, 22),
         ("ptpc_gathered_32768x6288x7168", "ptpc", 32768, 6288, 7168, tuple(range(500, 508)), 510),
         ("ptpc_gathered_32768x3648x7168", "ptpc", 32768, 3648, 7168, tuple(range(500, 508)), 511),
+        ("ptpc_2048x1168x1792", "ptpc", 2048, 1168, 1792, 61, 62),
     ]:
         qa, bs, sa, sb = headline_operands(dmm, torch, m, n, k, sa_seed, sb_seed, mode)
         out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")

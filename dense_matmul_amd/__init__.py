@@ -11,7 +11,8 @@ Functions (names as in the C ABI):
     quantize_blockscale_b(x)          -> (q, scale fp32 [ceil(N/128), K/128])
     quantize_mxfp8(x)                 -> (q, scale e8m0 uint8 [K/32, R])
     preshuffle_b(b)                   -> b_shuf (same shape, opaque order)
-    gemm_a8w8_ptpc(a, b_shuf, a_scale, b_scale, out=None)       -> bf16 [M,N]
+    gemm_a8w8_ptpc(a, b_shuf, a_scale, b_scale, out=None, tile="auto") -> bf16 [M,N]
+        (tile "256x256" / "128x256" calls gemm_a8w8_ptpc_tile)
     gemm_a8w8_blockscale(a, b_shuf, a_scale, b_scale, out=None) -> bf16 [M,N]
     gemm_a8w8_mxfp8(a, b_shuf, a_scale, b_scale, out=None)      -> bf16 [M,N]
     gemm_bf16(a, b, out=None)                                    -> bf16 [M,N]
@@ -31,7 +32,8 @@ DMM_OK, DMM_EINVAL, DMM_ENODEV, DMM_ELAUNCH = 0, 1, 2, 3
 
 EXPORTS = (
     "dmm_status_str", "dmm_last_error", "quantize_per_token", "quantize_blockscale_a", "quantize_blockscale_b",
-    "quantize_mxfp8", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8", "gemm_bf16",
+    "quantize_mxfp8", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8",
+    "gemm_bf16",
 )
 
 _lib = None
@@ -55,6 +57,7 @@ def lib():
         L.preshuffle_b.argtypes = [P, P, I64, I64, P]
         for name in ("gemm_a8w8_ptpc", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8"):
             getattr(L, name).argtypes = [P, P, P, P, P, I64, I64, I64, P]
+        L.gemm_a8w8_ptpc_tile.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
         L.gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
@@ -180,14 +183,25 @@ def _gemm_args(a, b_shuf, out):
     return _codes(a, "a"), _codes(b_shuf, "b_shuf"), out, m, n, k
 
 
-def gemm_a8w8_ptpc(a, b_shuf, a_scale, b_scale, out=None):
-    """C = bf16(a_scale[m] * b_scale[n] * sum_k A[m,k] B[n,k])."""
+PTPC_TILES = {"256x256": 1, "128x256": 2}
+
+
+def gemm_a8w8_ptpc(a, b_shuf, a_scale, b_scale, out=None, tile="auto"):
+    """C = bf16(a_scale[m] * b_scale[n] * sum_k A[m,k] B[n,k]).  tile: "auto"
+    (the library's choice), "256x256" or "128x256" (same result)."""
     au, bu, out, m, n, k = _gemm_args(a, b_shuf, out)
     _require(a_scale, "a_scale", torch.float32, 1)
     _require(b_scale, "b_scale", torch.float32, 1)
     _shape(a_scale, (m,), "a_scale")
     _shape(b_scale, (n,), "b_scale")
-    _check(lib().gemm_a8w8_ptpc(_ptr(au), _ptr(bu), _ptr(a_scale), _ptr(b_scale), _ptr(out), m, n, k, _stream()))
+    if tile == "auto":
+        _check(lib().gemm_a8w8_ptpc(_ptr(au), _ptr(bu), _ptr(a_scale), _ptr(b_scale), _ptr(out), m, n, k,
+                                    _stream()))
+    else:
+        if tile not in PTPC_TILES:
+            raise ValueError(f"tile must be 'auto' or one of {sorted(PTPC_TILES)} (got {tile!r})")
+        _check(lib().gemm_a8w8_ptpc_tile(_ptr(au), _ptr(bu), _ptr(a_scale), _ptr(b_scale), _ptr(out), m, n, k,
+                                         PTPC_TILES[tile], _stream()))
     return out
 
 

@@ -10,7 +10,7 @@
 #include "dmm.h"
 
 namespace dmm {
-hipError_t launch_gemm_a8w8(int mode, const uint8_t* a, const uint8_t* b, const void* sa, const void* sb, uint16_t* c,
+hipError_t launch_gemm_a8w8(int mode, int tile, const uint8_t* a, const uint8_t* b, const void* sa, const void* sb, uint16_t* c,
                             int m, int n, int k, hipStream_t stream);
 hipError_t launch_gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int m, int n, int k, hipStream_t st);
 hipError_t launch_quantize_rows(const float* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st);
@@ -73,8 +73,8 @@ dmm_status check_gemm_shape(int64_t m, int64_t n, int64_t k) {
     return DMM_OK;
 }
 
-dmm_status gemm_common(int mode, const uint8_t* a, const uint8_t* b, const void* sa, const void* sb, uint16_t* c,
-                       int64_t m, int64_t n, int64_t k, void* stream) {
+dmm_status gemm_common(int mode, int tile, const uint8_t* a, const uint8_t* b, const void* sa, const void* sb,
+                       uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream) {
     REQUIRE_PTR(a);
     REQUIRE_PTR(b);
     REQUIRE_PTR(sa);
@@ -85,7 +85,7 @@ dmm_status gemm_common(int mode, const uint8_t* a, const uint8_t* b, const void*
     if (mode == 1) REQUIRE((k / 128) * (m + 256) * 4 < kLimit, "a_scale is too large");
     if (mode == 2) REQUIRE((k / 32) * (m + 256) < kLimit && (k / 32) * (n + 256) < kLimit, "scales are too large");
     if ((s = check_device()) != DMM_OK) return s;
-    return launched(dmm::launch_gemm_a8w8(mode, a, b, sa, sb, c, (int)m, (int)n, (int)k, (hipStream_t)stream));
+    return launched(dmm::launch_gemm_a8w8(mode, tile, a, b, sa, sb, c, (int)m, (int)n, (int)k, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -168,17 +168,23 @@ dmm_status preshuffle_b(const uint8_t* b, uint8_t* b_shuf, int64_t n, int64_t k,
 
 dmm_status gemm_a8w8_ptpc(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale, const float* b_scale,
                           uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream) {
-    return gemm_common(0, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
+    return gemm_common(0, 0, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
+}
+
+dmm_status gemm_a8w8_ptpc_tile(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale, const float* b_scale,
+                               uint16_t* c, int64_t m, int64_t n, int64_t k, int tile, void* stream) {
+    REQUIRE(tile >= 0 && tile <= 2, "tile must be 0 (auto), 1 (256x256) or 2 (128x256) (got %d)", tile);
+    return gemm_common(0, tile, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
 }
 
 dmm_status gemm_a8w8_blockscale(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale, const float* b_scale,
                                 uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream) {
-    return gemm_common(1, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
+    return gemm_common(1, 0, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
 }
 
 dmm_status gemm_a8w8_mxfp8(const uint8_t* a, const uint8_t* b_shuf, const uint8_t* a_scale, const uint8_t* b_scale,
                            uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream) {
-    return gemm_common(2, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
+    return gemm_common(2, 0, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
 }
 
 dmm_status gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream) {

@@ -43,7 +43,11 @@
 
 namespace dmm {
 
-enum { MODE_PTPC = 0, MODE_BLOCKSCALE = 1, MODE_MXFP8 = 2 };
+// MODE_PTPC_N: ptpc on the 128 x 256 tile of eight waves (see Cfg).
+enum { MODE_PTPC = 0, MODE_BLOCKSCALE = 1, MODE_MXFP8 = 2, MODE_PTPC_N = 3 };
+
+template <int MODE>
+constexpr bool kPtpc = MODE == MODE_PTPC || MODE == MODE_PTPC_N;
 
 constexpr int BK = 128;
 
@@ -54,9 +58,9 @@ __shared__ __attribute__((aligned(1024))) char g_lds_a0[kMaxStageBytes];
 __shared__ __attribute__((aligned(1024))) char g_lds_a1[kMaxStageBytes];
 __shared__ __attribute__((aligned(1024))) char g_lds_a2[kMaxStageBytes];
 __shared__ __attribute__((aligned(1024))) char g_lds_a3[kMaxStageBytes];
-// ptpc epilogue scales: per wave 1 KiB of a_scale (the tile's 256 rows) and
-// 1 KiB of b_scale (the tile's 256 columns)
-__shared__ __attribute__((aligned(1024))) char g_lds_scale[4 * 2048];
+// ptpc epilogue scales: per wave (up to eight) 1 KiB of a_scale (the tile's
+// rows, up to 256) and 1 KiB of b_scale (the tile's 256 columns)
+__shared__ __attribute__((aligned(1024))) char g_lds_scale[8 * 2048];
 
 // The kernel body takes the four stage addresses and carries them in its
 // context (the host compilation pass only accepts references to the LDS
@@ -95,29 +99,32 @@ struct GemmArgs {
 // SIMD).  Blockscale folds every K tile's products into VGPR accumulators
 // with its scales, so each of its waves owns 128 x 32 (64 accumulators per
 // lane) and 8 waves, two per SIMD, share a 128 x 256 tile: each SIMD then
-// has a second wave to issue matrix ops while one waits.
+// has a second wave to issue matrix ops while one waits.  MODE_PTPC_N runs
+// ptpc on that narrow tile (matrix ops straight into VGPR accumulators),
+// which doubles the tile count of small problems.
 template <int MODE>
 struct Cfg {
-    static constexpr int MB = MODE == MODE_BLOCKSCALE ? 8 : 16;   // 16-row blocks per wave
-    static constexpr int NBW = MODE == MODE_BLOCKSCALE ? 2 : 4;   // 16-column blocks per wave
-    static constexpr int WAVES = MODE == MODE_BLOCKSCALE ? 8 : 4;  // waves per workgroup
+    static constexpr bool NARROW = MODE == MODE_BLOCKSCALE || MODE == MODE_PTPC_N;
+    static constexpr int MB = NARROW ? 8 : 16;   // 16-row blocks per wave
+    static constexpr int NBW = NARROW ? 2 : 4;   // 16-column blocks per wave
+    static constexpr int WAVES = NARROW ? 8 : 4;  // waves per workgroup
     static constexpr int NTHREADS = 64 * WAVES;
     static constexpr int BM = 16 * MB;                             // tile rows
     static constexpr int WN = 16 * NBW;                            // columns per wave
     static constexpr int BN = WAVES * WN;                          // tile columns
     static constexpr int NA = 2 * MB / WAVES;                      // DMA instructions per wave per K tile
     // vector-memory instructions of one B event: 2 NBW fragment loads plus scales
-    static constexpr int NB = MODE == MODE_PTPC ? 2 * NBW : 2 * NBW + 2 + 1;
+    static constexpr int NB = kPtpc<MODE> ? 2 * NBW : 2 * NBW + 2 + 1;
     // vector-memory instructions of the ptpc epilogue's scale loads (two
     // 1 KiB DMAs per wave)
-    static constexpr int NSC = MODE == MODE_PTPC ? 2 : 0;
+    static constexpr int NSC = kPtpc<MODE> ? 2 : 0;
     static_assert(2 * NB + NA <= 63, "vmcnt range");
 };
 
 // Whether a tile's epilogue is deferred into the next tile's first K step
 // (modes whose accumulators live in AGPRs).
 template <int MODE>
-constexpr bool kDeferEpilogue = MODE != MODE_BLOCKSCALE;
+constexpr bool kDeferEpilogue = !Cfg<MODE>::NARROW;
 
 // Per-workgroup tile list of the persistent grid.  Workgroup w runs on XCD
 // w % 8 (the dispatcher deals workgroups to the XCDs in turn); the XCD owns a
@@ -302,7 +309,7 @@ __device__ __forceinline__ void issue_b(Ctx<MODE>& x, TileRef r, int kt) {
 // the end of the list moves nothing).
 template <int MODE>
 __device__ __forceinline__ void issue_epilogue_scales(Ctx<MODE>& x, TileRef t) {
-    if constexpr (MODE == MODE_PTPC) {
+    if constexpr (kPtpc<MODE>) {
         const bool valid = t.m0 >= 0;
         const int m0 = valid ? t.m0 : 0, n0 = valid ? t.n0 : 0;
         const __amdgpu_buffer_rsrc_t rsa =
@@ -351,6 +358,13 @@ template <bool ZERO>
 __device__ __forceinline__ void mfma_acc(v4f& acc, const v8i& b, const v8i& a) {
     if constexpr (ZERO) asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "+a"(acc) : "v"(b), "v"(a));
     else asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
+// The same with the accumulator in VGPRs (MODE_PTPC_N).
+template <bool ZERO>
+__device__ __forceinline__ void mfma_vacc(v4f& acc, const v8i& b, const v8i& a) {
+    if constexpr (ZERO) asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(b), "v"(a));
+    else asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(b), "v"(a));
 }
 
 template <bool ZERO, int OA, int OB>
@@ -410,8 +424,13 @@ __device__ __forceinline__ void mfma_block(Ctx<MODE>& x, const v8i& a) {
 
 template <int MODE, int T, int mb, bool FIRST>
 __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
-    if constexpr (MODE != MODE_BLOCKSCALE) {
+    if constexpr (MODE == MODE_PTPC || MODE == MODE_MXFP8) {
         static_for<0, Cfg<MODE>::NBW>([&](auto NBc) { mfma_block<MODE, T, mb, decltype(NBc)::value, FIRST>(x, a); });
+    } else if constexpr (MODE == MODE_PTPC_N) {
+        // each accumulator is rewritten once per K tile, 2 MB - 1 matrix ops
+        // after its last write: far past the result latency
+        mfma_vacc<FIRST>(x.acc[mb][0], x.bq[T][0], a);
+        mfma_vacc<FIRST>(x.acc[mb][1], x.bq[T][1], a);
     } else {
         // blockscale: one fp32 scale per (row, 128-wide K tile) times the
         // B block's scale multiplies each K tile's products before they are
@@ -440,7 +459,10 @@ __device__ __forceinline__ void mfma_drain(Ctx<MODE>& x) {
 #pragma unroll
         for (int mb = 0; mb < Cfg<MODE>::MB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < Cfg<MODE>::NBW; ++nb) asm volatile("" : "+a"(x.acc[mb][nb]));
+            for (int nb = 0; nb < Cfg<MODE>::NBW; ++nb) {
+                if constexpr (kDeferEpilogue<MODE>) asm volatile("" : "+a"(x.acc[mb][nb]));
+                else asm volatile("" : "+v"(x.acc[mb][nb]));
+            }
     }
 }
 
@@ -518,6 +540,22 @@ __device__ __forceinline__ Epi epi_begin(Ctx<MODE>& x, int m0, int n0) {
         e.col = n0 + C::WN * x.w + 16 * (x.g & 1) + 8 * (x.g >> 1);
         e.cdrop = n0 + C::WN * x.w + 16 * (x.g & 1) < x.N ? 0u : 0x80000000u;
         e.row = m0 + C::MB * x.i;
+    }
+    if constexpr (MODE == MODE_PTPC_N) {
+        // rows MB i .. MB i + 7 and, per block, columns WN w + 16 nb + 4 g + v
+        static_assert(C::MB == 8 && C::NBW == 2, "two A- and two B-scale vectors");
+        wait_vm<C::NA>();
+        const uint32_t sc = (uint32_t)(uintptr_t)(x.lds.scale + x.w * 2048);
+        const uint32_t pa = sc + C::MB * x.i * 4, pb = sc + 1024 + (C::WN * x.w + 4 * x.g) * 4;
+        asm volatile(
+            "ds_read_b128 %0, %4\n"
+            "ds_read_b128 %1, %4 offset:16\n"
+            "ds_read_b128 %2, %5\n"
+            "ds_read_b128 %3, %5 offset:64\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(e.eas[0]), "=&v"(e.eas[1]), "=&v"(e.ebs[0]), "=&v"(e.ebs[1])
+            : "v"(pa), "v"(pb)
+            : "memory");
     }
     if constexpr (MODE == MODE_PTPC) {
         static_assert(C::MB == 16 && C::NBW == 4, "ptpc epilogue reads four A- and four B-scale vectors");
@@ -617,10 +655,16 @@ __device__ __forceinline__ void epi_row(Ctx<MODE>& x, const Epi& e) {
         EpiRow q;
         epi_phases<MODE, mb>(x, e, q);
     } else {
-        // blockscale: one block pair per wave, accumulators in VGPRs
+        // blockscale, narrow ptpc: one block pair per wave, accumulators
+        // in VGPRs
         static_assert(C::NBW == 2, "one block pair per wave");
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(x.c, (uint32_t)x.M * (uint32_t)x.N * 2u);
-        const v4f u = x.acc[mb][0], v = x.acc[mb][1];
+        v4f u = x.acc[mb][0], v = x.acc[mb][1];
+        if constexpr (MODE == MODE_PTPC_N) {
+            const float sa = e.eas[mb / 4][mb % 4];
+            u = u * sa * e.ebs[0];
+            v = v * sa * e.ebs[1];
+        }
         const uint32_t u0 = pack_bf16(u[0], u[1]), u1 = pack_bf16(u[2], u[3]);
         const uint32_t v0 = pack_bf16(v[0], v[1]), v1 = pack_bf16(v[2], v[3]);
         const auto s0 = __builtin_amdgcn_permlane16_swap(u0, v0, false, false);
@@ -845,7 +889,9 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRe
     L.ra = a_rsrc(x, a_m0 >= 0);
     L.abase = a_off + akt * BK;
     if constexpr (EPM == 1) x.ep = epi_begin<MODE>(x, prev.m0, prev.n0);
-    if constexpr (EPM == 3) x.ep = epi_begin<MODE>(x, g.t0.m0, g.t0.n0);
+    // the tile's scales leave LDS before this step's wait lets the next
+    // tile's scale DMAs in (the narrow tile stores at the end of the step)
+    if constexpr (EPM == 3 || (MODE == MODE_PTPC_N && LAST && !FIRST)) x.ep = epi_begin<MODE>(x, g.t0.m0, g.t0.n0);
     realign_mx<MODE, T>(x);
     v8i f0 = x.pre[0], f1 = x.pre[1], f2;
     EpiRow q;
@@ -880,7 +926,8 @@ __device__ __forceinline__ void tile_body(Ctx<MODE>& x, int s0, Ring g, TileRef 
     }
     if constexpr (!kDeferEpilogue<MODE>) {
         mfma_drain<MODE>(x);
-        store_tile<MODE>(x, g.t0.m0, g.t0.n0);
+        if constexpr (MODE == MODE_PTPC_N && CASE != 4) epi_rows<MODE>(x, x.ep);
+        else store_tile<MODE>(x, g.t0.m0, g.t0.n0);
     }
 }
 
@@ -1025,10 +1072,22 @@ static hipError_t launch_gemm(const GemmArgs& base, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_a8w8(int mode, const uint8_t* a, const uint8_t* b, const void* sa, const void* sb,
+// ptpc tile choice: the 256 x 256 tile moves the fewest bytes per matrix op
+// and wins wherever it fills the chip.  When it would leave at least half
+// the CUs idle, the 128 x 256 tile of eight waves puts twice as many CUs to
+// work (each narrow tile runs at about 0.8 of the wide tile's rate, so the
+// trade pays only there).
+int ptpc_tile_for(int m, int n) {
+    const long wide = (long)((m + 255) / 256) * ((n + 255) / 256);
+    return 2 * wide <= device_cus() ? 2 : 1;
+}
+
+hipError_t launch_gemm_a8w8(int mode, int tile, const uint8_t* a, const uint8_t* b, const void* sa, const void* sb,
                             uint16_t* c, int m, int n, int k, hipStream_t stream) {
     GemmArgs p{a, b, sa, sb, c, m, n, k, 0, 0};
+    if (mode == MODE_PTPC && (tile == 0 ? ptpc_tile_for(m, n) : tile) == 2) mode = MODE_PTPC_N;
     if (mode == MODE_PTPC) return launch_gemm<MODE_PTPC>(p, stream);
+    if (mode == MODE_PTPC_N) return launch_gemm<MODE_PTPC_N>(p, stream);
     if (mode == MODE_MXFP8) return launch_gemm<MODE_MXFP8>(p, stream);
     return launch_gemm<MODE_BLOCKSCALE>(p, stream);
 }

@@ -110,6 +110,17 @@ dmm_status preshuffle_b(const uint8_t* b, uint8_t* b_shuf, int64_t n, int64_t k,
 dmm_status gemm_a8w8_ptpc(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale, const float* b_scale,
                           uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream);
 
+/* ptpc with an explicit output-tile shape, the same result as
+ * gemm_a8w8_ptpc: tile 1 = 256 x 256 (four waves), 2 = 128 x 256 (eight
+ * waves), 0 = the choice gemm_a8w8_ptpc makes (128 x 256 when the problem
+ * has at most one 256 x 256 tile per two compute units).  The pages size the
+ * tile to the problem in the same spirit (mori PR 785, Cost: the table's
+ * shapes; aiter PR 6539, Benchmark: the tuned shapes).  Other values of
+ * tile return DMM_EINVAL. */
+dmm_status gemm_a8w8_ptpc_tile(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale,
+                               const float* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k, int tile,
+                               void* stream);
+
 /* blockscale: a_scale [k/128][m] fp32 (1x128 blocks, K-block major),
  * b_scale [ceil(n/128)][k/128] fp32 (128x128 blocks).
  *   C[m, n] = bf16(sum_kb a_scale[kb][m] b_scale[n/128][kb] sum_{k in kb} A B). */

@@ -30,7 +30,8 @@ def L():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for f in ("quantize_per_token", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8",
+    for f in ("quantize_per_token", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_blockscale",
+              "gemm_a8w8_mxfp8",
               "gemm_bf16", "quantize_blockscale_a", "quantize_blockscale_b", "quantize_mxfp8", "dmm_status_str",
               "dmm_last_error"):
         assert f in names, f
@@ -58,6 +59,18 @@ def test_gemm_shape_rules(L, m, n, k, why):
     for fn in (L.gemm_a8w8_ptpc, L.gemm_a8w8_blockscale, L.gemm_a8w8_mxfp8):
         assert fn(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, m, n, k, None) == 1
         assert why in L.dmm_last_error().decode()
+
+
+def test_ptpc_tile_rule(L):
+    """tile is 0 (auto), 1 (256x256) or 2 (128x256); anything else is an
+    argument error, reported before any HIP call."""
+    f = L.gemm_a8w8_ptpc_tile
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_void_p]
+    for tile in (-1, 3, 256):
+        assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 64, 256, 256, tile, None) == 1
+        assert b"tile must be" in L.dmm_last_error()
+    # shape rules apply as for gemm_a8w8_ptpc
+    assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 64, 24, 256, 2, None) == 1
 
 
 def test_gemm_pointer_rules(L):

@@ -131,8 +131,30 @@ def test_preshuffle_is_the_documented_permutation(dmm, n, k):
 
 
 # ------------------------------------------------------------------ GEMM
+# ptpc runs on two tile shapes; "ptpc" is the library's own choice, the
+# other two force one shape (same data, same oracle).
+PTPC_TILE = {"ptpc": "auto", "ptpc_w": "256x256", "ptpc_n": "128x256"}
+MODE_ID = {"ptpc": 0, "blockscale": 1, "mxfp8": 2}
+GEMM_MODES = ["ptpc_w", "ptpc_n", "blockscale", "mxfp8"]
+
+
+def base_mode(mode):
+    return "ptpc" if mode in PTPC_TILE else mode
+
+
+def gemm_fn(dmm, mode):
+    if mode in PTPC_TILE:
+        return lambda *args, **kw: dmm.gemm_a8w8_ptpc(*args, tile=PTPC_TILE[mode], **kw)
+    return {"blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
+
+
+def tile_rows(mode):
+    return 128 if mode in ("blockscale", "ptpc_n") else 256
+
+
 def quantised_operands(mode, m, n, k, seed_a, seed_b):
     """fp32 N(0,1) operands quantised by the oracle's quantisers."""
+    mode = base_mode(mode)
     a = inputs.operand_a(m, k, seed_a)
     b = inputs.normal((n, k), seed_b)
     if mode == "ptpc":
@@ -149,11 +171,11 @@ def quantised_operands(mode, m, n, k, seed_a, seed_b):
 
 def gpu_gemm(dmm, mode, qa, qb, sa, sb, out=None):
     b_shuf = dmm.preshuffle_b(to_dev(qb))
-    fn = {"ptpc": dmm.gemm_a8w8_ptpc, "blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
-    return fn(to_dev(qa), b_shuf, to_dev(sa), to_dev(sb), out=out)
+    return gemm_fn(dmm, mode)(to_dev(qa), b_shuf, to_dev(sa), to_dev(sb), out=out)
 
 
 def exact_operands(mode, m, n, k, seed):
+    mode = base_mode(mode)
     vals = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0], np.float32)
     codes = oracle.enc_e4m3(vals)
     qa = inputs.choice((m, k), codes, seed)
@@ -173,7 +195,7 @@ def exact_operands(mode, m, n, k, seed):
 EXACT_SHAPES = [(1, 16, 128), (17, 272, 256), (300, 1168, 384), (256, 256, 512), (513, 528, 640), (64, 48, 1792)]
 
 
-@pytest.mark.parametrize("mode", ["ptpc", "blockscale", "mxfp8"])
+@pytest.mark.parametrize("mode", GEMM_MODES)
 @pytest.mark.parametrize("m,n,k", EXACT_SHAPES)
 def test_gemm_exact_regime_bitwise(dmm, mode, m, n, k):
     """Every partial sum exact in fp32: the GPU must equal the oracle bitwise,
@@ -181,21 +203,21 @@ def test_gemm_exact_regime_bitwise(dmm, mode, m, n, k):
     announce("exact", mode, m, n, k)
     qa, qb, sa, sb = exact_operands(mode, m, n, k, m + n + k)
     c = gpu_gemm(dmm, mode, qa, qb, sa, sb)
-    ref = oracle.gemm_a8w8({"ptpc": 0, "blockscale": 1, "mxfp8": 2}[mode], qa, qb, sa, sb)
+    ref = oracle.gemm_a8w8(MODE_ID[base_mode(mode)], qa, qb, sa, sb)
     got = bf16_bits(c)
     mism = np.argwhere(got != ref)
     assert mism.size == 0, f"{mode} {m}x{n}x{k}: {len(mism)} mismatches, first at {mism[:4].tolist()}"
 
 
-@pytest.mark.parametrize("mode", ["ptpc", "blockscale", "mxfp8"])
+@pytest.mark.parametrize("mode", GEMM_MODES)
 @pytest.mark.parametrize("m,n,k,sa_seed,sb_seed", [(512, 1024, 256, 1, 2), (300, 1168, 1792, 61, 62),
                                                    (17, 16, 128, 3, 4), (1000, 3648, 512, 5, 6)])
 def test_gemm_normal_inputs_within_tolerance(dmm, mode, m, n, k, sa_seed, sb_seed):
     announce("normal", mode, m, n, k)
     qa, qb, sa, sb = quantised_operands(mode, m, n, k, sa_seed, sb_seed)
     c = gpu_gemm(dmm, mode, qa, qb, sa, sb)
-    ref = oracle.gemm_a8w8({"ptpc": 0, "blockscale": 1, "mxfp8": 2}[mode], qa, qb, sa, sb)
-    check_close(bf16_bits(c), ref, f"{mode} {m}x{n}x{k}", mode, (qa, qb, sa, sb))
+    ref = oracle.gemm_a8w8(MODE_ID[base_mode(mode)], qa, qb, sa, sb)
+    check_close(bf16_bits(c), ref, f"{mode} {m}x{n}x{k}", base_mode(mode), (qa, qb, sa, sb))
 
 
 def run_poisoned(dmm, mode, qa, qb, sa, sb, launches, hog=False):
@@ -204,7 +226,7 @@ def run_poisoned(dmm, mode, qa, qb, sa, sb, launches, hog=False):
     m, n = qa.shape[0], qb.shape[0]
     b_shuf = dmm.preshuffle_b(to_dev(qb))
     a, s_a, s_b = to_dev(qa), to_dev(sa), to_dev(sb)
-    fn = {"ptpc": dmm.gemm_a8w8_ptpc, "blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
+    fn = gemm_fn(dmm, mode)
     buf = torch.empty(m * n + 2048, dtype=torch.bfloat16, device=DEV)
     c = buf[: m * n].view(m, n)
     canary = buf[m * n:]
@@ -227,25 +249,26 @@ def run_poisoned(dmm, mode, qa, qb, sa, sb, launches, hog=False):
     return outs
 
 
+@pytest.mark.parametrize("mode", ["ptpc", "ptpc_w", "ptpc_n"])
 @pytest.mark.parametrize("m,n,k,seed_a,seed_b", [(4096, 7168, 256, 11, 12), (16384, 7168, 512, 21, 22)])
-def test_race_shapes_bit_stable_and_correct(dmm, m, n, k, seed_a, seed_b):
+def test_race_shapes_bit_stable_and_correct(dmm, mode, m, n, k, seed_a, seed_b):
     """The pages' race shapes (mori PR 785, Test table): 20 launches into a
     NaN-poisoned C must be bitwise identical, leave no NaN, and match the
     oracle on sampled rows (every row of the first and last 256-row tiles
     plus one per 64-row band)."""
-    announce("race", m, n, k)
+    announce("race", mode, m, n, k)
     qa, qb, sa, sb = quantised_operands("ptpc", m, n, k, seed_a, seed_b)
-    outs = run_poisoned(dmm, "ptpc", qa, qb, sa, sb, 20)
+    outs = run_poisoned(dmm, mode, qa, qb, sa, sb, 20)
     for i, o in enumerate(outs[1:], 1):
         diff = np.count_nonzero(o != outs[0])
         assert diff == 0, f"launch {i} differs from launch 0 in {diff} elements"
     assert not np.isnan(bits_to_f64(outs[0])).any()
     rows = inputs.rows_sample(m, seed=m)
     ref = oracle.gemm_ptpc(qa, qb, sa, sb, rows=rows)
-    check_close(outs[0][rows], ref, f"ptpc {m}x{n}x{k} sampled rows", "ptpc", (qa, qb, sa, sb), rows)
+    check_close(outs[0][rows], ref, f"{mode} {m}x{n}x{k} sampled rows", "ptpc", (qa, qb, sa, sb), rows)
 
 
-@pytest.mark.parametrize("mode", ["ptpc", "mxfp8", "blockscale"])
+@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "blockscale"])
 def test_bit_stable_under_concurrent_copy(dmm, mode):
     """Same 20-launch identity with an HBM copy loop on a second stream."""
     m, n, k = 4096, 7168, 256
@@ -292,7 +315,7 @@ def test_invalid_arguments_raise_value_error(dmm):
                            torch.ones(16, dtype=torch.float32, device=DEV))
 
 
-@pytest.mark.parametrize("mode", ["ptpc", "mxfp8", "blockscale"])
+@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "blockscale"])
 @pytest.mark.parametrize("k", [128, 256, 384, 512, 640])
 def test_many_tiles_per_workgroup_every_k_phase(dmm, mode, k):
     """More tiles than CUs, so every workgroup runs 2-3 tiles back to back,
@@ -301,7 +324,7 @@ def test_many_tiles_per_workgroup_every_k_phase(dmm, mode, k):
     the next tile's first K step.  Exact-arithmetic inputs: sampled rows of
     every tile row band must equal the oracle bitwise; two launches into a
     NaN-poisoned C must be identical and leave no NaN."""
-    bm = 128 if mode == "blockscale" else 256
+    bm = tile_rows(mode)
     m, n = 18 * bm + 40, 8192 + 48  # partial last row and column tiles
     announce("many tiles", mode, m, n, k)
     qa, qb, sa, sb = exact_operands(mode, m, n, k, 7 * k + len(mode))
@@ -310,7 +333,7 @@ def test_many_tiles_per_workgroup_every_k_phase(dmm, mode, k):
     assert diff == 0, f"launch 1 differs from launch 0 in {diff} elements"
     assert not np.isnan(bits_to_f64(outs[0])).any(), "rows or columns left unwritten"
     rows = np.unique(np.clip(np.concatenate([t * bm + np.array([0, 1, 15, 16, bm - 1]) for t in range(19)]), 0, m - 1))
-    ref = oracle.gemm_a8w8({"ptpc": 0, "blockscale": 1, "mxfp8": 2}[mode], qa, qb, sa, sb, rows=rows)
+    ref = oracle.gemm_a8w8(MODE_ID[base_mode(mode)], qa, qb, sa, sb, rows=rows)
     got = outs[0][rows]
     mism = np.argwhere(got != ref)
     assert mism.size == 0, f"{mode} {m}x{n}x{k}: {len(mism)} mismatches, first at {mism[:4].tolist()}"

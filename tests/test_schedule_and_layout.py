@@ -64,7 +64,7 @@ def shim(tmp_path_factory):
 
 
 # ---------------------------------------------------------------- schedule
-MODES = {"ptpc": (8, 8, 2), "mxfp8": (8, 11, 0), "blockscale": (2, 7, 0)}  # NA, NB, NSC per wave
+MODES = {"ptpc": (8, 8, 2), "mxfp8": (8, 11, 0), "blockscale": (2, 7, 0), "ptpc_128x256": (2, 4, 2)}  # NA, NB, NSC per wave
 
 
 def program(L, KI, ntiles, NA, NB, NSC, wait_fn=None):

@@ -13,6 +13,8 @@ Functions (names as in the C ABI):
     preshuffle_b(b)                   -> b_shuf (same shape, opaque order)
     gemm_a8w8_ptpc(a, b_shuf, a_scale, b_scale, out=None, tile="auto") -> bf16 [M,N]
         (tile "256x256" / "128x256" calls gemm_a8w8_ptpc_tile)
+    gemm_a8w8_ptpc_gathered(a, b_shuf, a_scale, b_scale, flags, src_rows, nchunks, own, epoch,
+                            spin_limit=1 << 22, status=None, out=None) -> (bf16 [M,N], status)
     gemm_a8w8_blockscale(a, b_shuf, a_scale, b_scale, out=None) -> bf16 [M,N]
     gemm_a8w8_mxfp8(a, b_shuf, a_scale, b_scale, out=None)      -> bf16 [M,N]
     gemm_bf16(a, b, out=None)                                    -> bf16 [M,N]
@@ -32,7 +34,8 @@ DMM_OK, DMM_EINVAL, DMM_ENODEV, DMM_ELAUNCH = 0, 1, 2, 3
 
 EXPORTS = (
     "dmm_status_str", "dmm_last_error", "quantize_per_token", "quantize_blockscale_a", "quantize_blockscale_b",
-    "quantize_mxfp8", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8",
+    "quantize_mxfp8", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_ptpc_gathered", "gemm_a8w8_blockscale",
+    "gemm_a8w8_mxfp8",
     "gemm_bf16",
 )
 
@@ -58,6 +61,8 @@ def lib():
         for name in ("gemm_a8w8_ptpc", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8"):
             getattr(L, name).argtypes = [P, P, P, P, P, I64, I64, I64, P]
         L.gemm_a8w8_ptpc_tile.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
+        L.gemm_a8w8_ptpc_gathered.argtypes = [P, P, P, P, P, I64, I64, I64, P, I64, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_uint32, I64, P, P]
         L.gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
@@ -203,6 +208,34 @@ def gemm_a8w8_ptpc(a, b_shuf, a_scale, b_scale, out=None, tile="auto"):
         _check(lib().gemm_a8w8_ptpc_tile(_ptr(au), _ptr(bu), _ptr(a_scale), _ptr(b_scale), _ptr(out), m, n, k,
                                          PTPC_TILES[tile], _stream()))
     return out
+
+
+def gemm_a8w8_ptpc_gathered(a, b_shuf, a_scale, b_scale, flags, src_rows, nchunks, own, epoch,
+                            spin_limit=1 << 22, status=None, out=None):
+    """ptpc GEMM over a gathered A whose source slabs arrive in bands (see
+    include/dmm.h).  flags: int32 [m // src_rows * nchunks], on the GPU or in
+    pinned host memory (a host thread may write it while the kernel runs);
+    band s * nchunks + c is read once (int32)(flags[band] - epoch) >= 0.
+    Returns (out, status): status is a GPU int32 [1], 0 unless a band's wait
+    gave up after spin_limit polls (then 1 + that band, the largest)."""
+    au, bu, out, m, n, k = _gemm_args(a, b_shuf, out)
+    _require(a_scale, "a_scale", torch.float32, 1)
+    _require(b_scale, "b_scale", torch.float32, 1)
+    _shape(a_scale, (m,), "a_scale")
+    _shape(b_scale, (n,), "b_scale")
+    _require(flags, "flags", torch.int32, 1, cuda=False)
+    if not flags.is_cuda and not flags.is_pinned():
+        raise ValueError("flags: expected a GPU tensor or pinned host memory")
+    if src_rows < 1 or m % src_rows:
+        raise ValueError(f"m={m} is not a multiple of src_rows={src_rows}")
+    _shape(flags, (m // src_rows * nchunks,), "flags")
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=a.device)
+    _require(status, "status", torch.int32, 1)
+    _check(lib().gemm_a8w8_ptpc_gathered(_ptr(au), _ptr(bu), _ptr(a_scale), _ptr(b_scale), _ptr(out), m, n, k,
+                                         _ptr(flags), src_rows, nchunks, own, epoch & 0xFFFFFFFF, spin_limit,
+                                         _ptr(status), _stream()))
+    return out, status
 
 
 def gemm_a8w8_blockscale(a, b_shuf, a_scale, b_scale, out=None):

@@ -12,6 +12,10 @@
 namespace dmm {
 hipError_t launch_gemm_a8w8(int mode, int tile, const uint8_t* a, const uint8_t* b, const void* sa, const void* sb, uint16_t* c,
                             int m, int n, int k, hipStream_t stream);
+hipError_t launch_gemm_a8w8_gathered(const uint8_t* a, const uint8_t* b, const float* sa, const float* sb,
+                                     uint16_t* c, int m, int n, int k, const uint32_t* flags, int src_rows,
+                                     int nchunks, int own, uint32_t epoch, long long spin_limit, int* status,
+                                     hipStream_t stream);
 hipError_t launch_gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int m, int n, int k, hipStream_t st);
 hipError_t launch_quantize_rows(const float* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st);
 hipError_t launch_quantize_blockscale_a(const float* x, uint8_t* q, float* s, int m, int k, hipStream_t st);
@@ -175,6 +179,33 @@ dmm_status gemm_a8w8_ptpc_tile(const uint8_t* a, const uint8_t* b_shuf, const fl
                                uint16_t* c, int64_t m, int64_t n, int64_t k, int tile, void* stream) {
     REQUIRE(tile >= 0 && tile <= 2, "tile must be 0 (auto), 1 (256x256) or 2 (128x256) (got %d)", tile);
     return gemm_common(0, tile, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
+}
+
+dmm_status gemm_a8w8_ptpc_gathered(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale,
+                                   const float* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k,
+                                   const uint32_t* flags, int64_t src_rows, int nchunks, int own, uint32_t epoch,
+                                   int64_t spin_limit, int* status, void* stream) {
+    REQUIRE_PTR(a);
+    REQUIRE_PTR(b_shuf);
+    REQUIRE_PTR(a_scale);
+    REQUIRE_PTR(b_scale);
+    REQUIRE_PTR(c);
+    dmm_status s = check_gemm_shape(m, n, k);
+    if (s != DMM_OK) return s;
+    REQUIRE(flags != nullptr && (uintptr_t)flags % 4 == 0, "flags: null or not 4-byte aligned");
+    REQUIRE(status != nullptr && (uintptr_t)status % 4 == 0, "status: null or not 4-byte aligned");
+    REQUIRE(nchunks >= 1, "nchunks must be >= 1 (got %d)", nchunks);
+    REQUIRE(src_rows >= 256 && src_rows % (256 * (int64_t)nchunks) == 0,
+            "src_rows must be a positive multiple of 256 * nchunks (got %lld)", (long long)src_rows);
+    REQUIRE(m % src_rows == 0, "m must be a multiple of src_rows (got m %lld, src_rows %lld)", (long long)m,
+            (long long)src_rows);
+    REQUIRE((m / src_rows) * nchunks <= 64, "at most 64 bands (sources x nchunks)");
+    REQUIRE(own >= 0 && own < m / src_rows, "own must name a source slab (got %d)", own);
+    REQUIRE(spin_limit >= 0, "spin_limit must be >= 0");
+    if ((s = check_device()) != DMM_OK) return s;
+    return launched(dmm::launch_gemm_a8w8_gathered(a, b_shuf, a_scale, b_scale, c, (int)m, (int)n, (int)k, flags,
+                                                   (int)src_rows, nchunks, own, epoch, (long long)spin_limit,
+                                                   status, (hipStream_t)stream));
 }
 
 dmm_status gemm_a8w8_blockscale(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale, const float* b_scale,

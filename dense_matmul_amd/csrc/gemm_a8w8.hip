@@ -38,16 +38,20 @@
 #include "common.h"
 #include "kpipe.h"
 #include "lds_layout.h"
+#include "tile_order.h"
 
 #include <type_traits>
 
 namespace dmm {
 
-// MODE_PTPC_N: ptpc on the 128 x 256 tile of eight waves (see Cfg).
-enum { MODE_PTPC = 0, MODE_BLOCKSCALE = 1, MODE_MXFP8 = 2, MODE_PTPC_N = 3 };
+// MODE_PTPC_N: ptpc on the 128 x 256 tile of eight waves (see Cfg);
+// MODE_PTPC_G: ptpc over a gathered A (Gather), 256 x 256 tiles.
+enum { MODE_PTPC = 0, MODE_BLOCKSCALE = 1, MODE_MXFP8 = 2, MODE_PTPC_N = 3, MODE_PTPC_G = 4 };
 
 template <int MODE>
-constexpr bool kPtpc = MODE == MODE_PTPC || MODE == MODE_PTPC_N;
+constexpr bool kWidePtpc = MODE == MODE_PTPC || MODE == MODE_PTPC_G;
+template <int MODE>
+constexpr bool kPtpc = kWidePtpc<MODE> || MODE == MODE_PTPC_N;
 
 constexpr int BK = 128;
 
@@ -83,6 +87,16 @@ __device__ __forceinline__ void static_for(F&& f) {
 constexpr int kDppRowRor8 = 0x128;
 constexpr int kStoreStream = 2;
 
+// Gathered operand (order::gathered_coords): band b's rows of A and
+// a_scale may be read once flags[b] has reached epoch (wrap-safe compare).
+struct Gather {
+    const uint32_t* flags;  // null: A is resident, default order
+    int bt, nsrc, nchunks, own;
+    uint32_t epoch;
+    long long spin_limit;   // polls per band before giving up
+    int* status;            // set to 1 + band (the largest) when a wait gave up
+};
+
 struct GemmArgs {
     const uint8_t* a;
     const uint8_t* b;
@@ -91,6 +105,7 @@ struct GemmArgs {
     uint16_t* c;
     int m, n, k;
     int tiles_m, tiles_n;
+    Gather gather;  // MODE_PTPC_G only
 };
 
 // Tile shape per mode.  Each of the WAVES waves owns NBW 16-column blocks
@@ -126,38 +141,8 @@ struct Cfg {
 template <int MODE>
 constexpr bool kDeferEpilogue = !Cfg<MODE>::NARROW;
 
-// Per-workgroup tile list of the persistent grid.  Workgroup w runs on XCD
-// w % 8 (the dispatcher deals workgroups to the XCDs in turn); the XCD owns a
-// contiguous range of the tile order and its workgroups stride through it, so
-// the tiles in flight on one XCD at any time are neighbours in that order.
-struct TileList {
-    int start, count, slot, slots;  // XCD range, this workgroup's slot, slots on the XCD
-    __device__ __forceinline__ int ntiles() const { return slot < count ? (count - slot + slots - 1) / slots : 0; }
-    __device__ __forceinline__ int tile(int j) const { return start + slot + j * slots; }
-};
-
-__device__ __forceinline__ TileList tile_list(int wg, int grid, int T) {
-    TileList L;
-    const int x = wg & 7, per = T >> 3, rem = T & 7;
-    L.start = x * per + (x < rem ? x : rem);
-    L.count = per + (x < rem ? 1 : 0);
-    L.slot = wg >> 3;
-    L.slots = (grid - x + 7) >> 3;
-    return L;
-}
-
-// Linear tile index -> (row tile, column tile): GROUP row tiles sweep all
-// column tiles, so the tiles an XCD runs together share A rows and B columns
-// in its L2.
-__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
-    constexpr int GROUP = 4;
-    const int group = t / (GROUP * tiles_n);
-    const int first = group * GROUP;
-    const int gsize = tiles_m - first < GROUP ? tiles_m - first : GROUP;
-    const int within = t - group * GROUP * tiles_n;
-    tm = first + within % gsize;
-    tn = within / gsize;
-}
+// Tile order of the persistent grid: tile_order.h (order::xcd_list, or
+// order::round_list with the gathered order).
 
 // One output tile of a workgroup's list: its origin and the byte offsets of
 // its A rows and preshuffled B blocks.  Loads go through descriptors over the
@@ -189,8 +174,10 @@ struct Ctx {
     const void* sb;
     uint16_t* c;
     int M, N, K, KI, tiles_m, tiles_n;
-    TileList tl;
+    order::List tl;
     int ntiles;
+    Gather gather;             // MODE_PTPC_G only
+    unsigned long long ready;  // MODE_PTPC_G: bands seen complete
     int w, lane, i, g;
     int dma_lds;        // byte offset of this wave's DMA slots in a stage
     int voff_a[C::NA];  // per-lane byte offsets of the DMA rows, relative to the tile's first row
@@ -215,14 +202,45 @@ struct Ctx {
 
     // Tile j of this workgroup's list with the buffer descriptors its loads
     // use (see TileRef).
-    __device__ __forceinline__ TileRef ref(int j) const;
+    __device__ __forceinline__ TileRef ref(int j);
 };
 
+// Wait until band b of a gathered A has arrived: poll its flag with
+// system-scope loads (every wave of the workgroup polls for itself, before
+// any of its loads of the band's rows), then an acquire fence, so that the
+// loads that follow see the band's rows and scales.  After spin_limit polls
+// the wait gives up, records the band in status and goes on: the kernel
+// always finishes.
+__device__ __forceinline__ void await_band(const Gather& gth, int b) {
+    long long polls = 0;
+    for (;;) {
+        const uint32_t f = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(gth.flags + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
+        if ((int32_t)(f - gth.epoch) >= 0) break;
+        if (++polls > gth.spin_limit) {
+            if (threadIdx.x == 0) atomicMax(gth.status, b + 1);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+}
+
 template <int MODE>
-__device__ __forceinline__ TileRef Ctx<MODE>::ref(int j) const {
+__device__ __forceinline__ TileRef Ctx<MODE>::ref(int j) {
     if (j >= ntiles) return TileRef{-1, -1, 0, 0};
+    const int u = tl.first + j * tl.stride;
     int tm, tn;
-    tile_coords(tl.tile(j), tiles_m, tiles_n, tm, tn);
+    if constexpr (MODE == MODE_PTPC_G) {
+        int band;
+        order::gathered_coords(u, gather.bt, gather.nsrc, gather.nchunks, gather.own, tiles_n, tm, tn, band);
+        if (band >= 0 && !((ready >> band) & 1ull)) {
+            await_band(gather, band);
+            ready |= 1ull << band;
+        }
+    } else {
+        order::coords(u, tiles_m, tiles_n, tm, tn);
+    }
     const int m0 = tm * C::BM, n0 = tn * C::BN;
     return TileRef{m0, n0, m0 * K, (n0 / 16) * KI * 2048};
 }
@@ -412,7 +430,7 @@ __device__ __forceinline__ void fold_products(Ctx<MODE>& x) {
 // Block (mb, nb) of a K tile, ptpc / mxfp8 (AGPR accumulators).
 template <int MODE, int T, int mb, int nb, bool FIRST>
 __device__ __forceinline__ void mfma_block(Ctx<MODE>& x, const v8i& a) {
-    if constexpr (MODE == MODE_PTPC) {
+    if constexpr (kWidePtpc<MODE>) {
         mfma_acc<FIRST>(x.acc[mb][nb], x.bq[T][nb], a);
     } else {
         static_assert(MODE == MODE_MXFP8, "blockscale issues its row blocks as a whole");
@@ -424,7 +442,7 @@ __device__ __forceinline__ void mfma_block(Ctx<MODE>& x, const v8i& a) {
 
 template <int MODE, int T, int mb, bool FIRST>
 __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
-    if constexpr (MODE == MODE_PTPC || MODE == MODE_MXFP8) {
+    if constexpr (kWidePtpc<MODE> || MODE == MODE_MXFP8) {
         static_for<0, Cfg<MODE>::NBW>([&](auto NBc) { mfma_block<MODE, T, mb, decltype(NBc)::value, FIRST>(x, a); });
     } else if constexpr (MODE == MODE_PTPC_N) {
         // each accumulator is rewritten once per K tile, 2 MB - 1 matrix ops
@@ -557,7 +575,7 @@ __device__ __forceinline__ Epi epi_begin(Ctx<MODE>& x, int m0, int n0) {
             : "v"(pa), "v"(pb)
             : "memory");
     }
-    if constexpr (MODE == MODE_PTPC) {
+    if constexpr (kWidePtpc<MODE>) {
         static_assert(C::MB == 16 && C::NBW == 4, "ptpc epilogue reads four A- and four B-scale vectors");
         wait_vm<C::NA>();
         const uint32_t sc = (uint32_t)(uintptr_t)(x.lds.scale + x.w * 2048);
@@ -604,7 +622,7 @@ __device__ __forceinline__ void epi_phase(Ctx<MODE>& x, const Epi& e, EpiRow& q)
             asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(q.v[PH][c]) : "a"(x.acc[r][2 * PH + 1][c]));
         }
     } else if constexpr (PH < 6) {
-        if constexpr (MODE == MODE_PTPC) {
+        if constexpr (kWidePtpc<MODE>) {
             constexpr int pair = (PH - 2) / 2;
             const float sa = e.eas[r / 4][r % 4];
             if constexpr (PH % 2 == 0) q.u[pair] = q.u[pair] * sa * e.ebs[2 * pair];
@@ -959,8 +977,14 @@ __global__ void __launch_bounds__(Cfg<MODE>::NTHREADS, 1) gemm_a8w8_kernel(GemmA
     x.KI = p.k / BK;
     x.tiles_m = p.tiles_m;
     x.tiles_n = p.tiles_n;
-    x.tl = tile_list(blockIdx.x, gridDim.x, p.tiles_m * p.tiles_n);
-    x.ntiles = x.tl.ntiles();
+    if constexpr (MODE == MODE_PTPC_G) {
+        x.gather = p.gather;
+        x.ready = 0;
+        x.tl = order::round_list(blockIdx.x, gridDim.x, p.tiles_m * p.tiles_n);
+    } else {
+        x.tl = order::xcd_list(blockIdx.x, gridDim.x, p.tiles_m * p.tiles_n);
+    }
+    x.ntiles = x.tl.n;
     if (x.ntiles == 0) return;
     x.w = wave_id();
     x.lane = lane_id();
@@ -1090,6 +1114,18 @@ hipError_t launch_gemm_a8w8(int mode, int tile, const uint8_t* a, const uint8_t*
     if (mode == MODE_PTPC_N) return launch_gemm<MODE_PTPC_N>(p, stream);
     if (mode == MODE_MXFP8) return launch_gemm<MODE_MXFP8>(p, stream);
     return launch_gemm<MODE_BLOCKSCALE>(p, stream);
+}
+
+// ptpc over a gathered A (256 x 256 tiles, time-ordered grid): src_rows rows
+// per source slab, nchunks arrival bands per slab (the host checks that
+// every band is a whole number of 256-row tiles).
+hipError_t launch_gemm_a8w8_gathered(const uint8_t* a, const uint8_t* b, const float* sa, const float* sb,
+                                     uint16_t* c, int m, int n, int k, const uint32_t* flags, int src_rows,
+                                     int nchunks, int own, uint32_t epoch, long long spin_limit, int* status,
+                                     hipStream_t stream) {
+    GemmArgs p{a, b, sa, sb, c, m, n, k, 0, 0};
+    p.gather = Gather{flags, src_rows / 256, m / src_rows, nchunks, own, epoch, spin_limit, status};
+    return launch_gemm<MODE_PTPC_G>(p, stream);
 }
 
 }  // namespace dmm

@@ -121,6 +121,31 @@ dmm_status gemm_a8w8_ptpc_tile(const uint8_t* a, const uint8_t* b_shuf, const fl
                                const float* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k, int tile,
                                void* stream);
 
+/* ptpc over a gathered A: the GEMM half of an all-gather + GEMM (mori PR
+ * 809, How it works: the tile order and the wait), on one GPU.  A [m, k] and
+ * a_scale [m] are m / src_rows source slabs of src_rows rows; slab `own` is
+ * resident when the call starts, and every other slab arrives in nchunks
+ * row bands of src_rows / nchunks rows: band s * nchunks + c (rows
+ * s * src_rows + c * src_rows / nchunks ...) may be read once
+ * flags[s * nchunks + c] has reached epoch, compared wrap-safe as
+ * (int32_t)(flags[band] - epoch) >= 0, so a caller advances epoch per call
+ * and never resets the flags.  Tiles of the own slab run first, never
+ * waiting; then, for each chunk c, the sources own+1, own+2, ... (mod the
+ * source count).  A workgroup polls a band's flag with system-scope loads
+ * before any load of its rows and fences (acquire) after seeing it; flags
+ * may live in device memory or in pinned host memory that a host thread
+ * writes.  After spin_limit polls (each about 0.3 us) for one band the wait
+ * gives up: *status (device int, zeroed by the caller) becomes the largest
+ * 1 + band that timed out and the result is undefined; the kernel still
+ * finishes.  The result is otherwise bitwise that of gemm_a8w8_ptpc.
+ * Rules beyond gemm_a8w8_ptpc's: src_rows a positive multiple of
+ * 256 * nchunks; m a multiple of src_rows; at most 64 bands; 0 <= own <
+ * m / src_rows; spin_limit >= 0; flags and status non-null, 4-byte aligned. */
+dmm_status gemm_a8w8_ptpc_gathered(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale,
+                                   const float* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k,
+                                   const uint32_t* flags, int64_t src_rows, int nchunks, int own, uint32_t epoch,
+                                   int64_t spin_limit, int* status, void* stream);
+
 /* blockscale: a_scale [k/128][m] fp32 (1x128 blocks, K-block major),
  * b_scale [ceil(n/128)][k/128] fp32 (128x128 blocks).
  *   C[m, n] = bf16(sum_kb a_scale[kb][m] b_scale[n/128][kb] sum_{k in kb} A B). */

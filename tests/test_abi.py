@@ -30,7 +30,8 @@ def L():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for f in ("quantize_per_token", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_blockscale",
+    for f in ("quantize_per_token", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_ptpc_gathered",
+              "gemm_a8w8_blockscale",
               "gemm_a8w8_mxfp8",
               "gemm_bf16", "quantize_blockscale_a", "quantize_blockscale_b", "quantize_mxfp8", "dmm_status_str",
               "dmm_last_error"):
@@ -71,6 +72,30 @@ def test_ptpc_tile_rule(L):
         assert b"tile must be" in L.dmm_last_error()
     # shape rules apply as for gemm_a8w8_ptpc
     assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 64, 24, 256, 2, None) == 1
+
+
+@pytest.mark.parametrize("m,src_rows,nchunks,own,spin,why", [
+    (4096, 1000, 1, 0, 10, "src_rows must be"),       # not a multiple of 256
+    (4096, 1024, 3, 0, 10, "src_rows must be"),       # 1024 rows do not split into 3 chunks of whole tiles
+    (4096, 1536, 1, 0, 10, "m must be a multiple"),
+    (4096, 1024, 1, 4, 10, "own must name"),
+    (4096, 1024, 1, -1, 10, "own must name"),
+    (65 * 256, 256, 1, 0, 10, "at most 64 bands"),
+    (4096, 1024, 0, 0, 10, "nchunks must be"),
+    (4096, 1024, 1, 0, -1, "spin_limit"),
+])
+def test_gathered_rules(L, m, src_rows, nchunks, own, spin, why):
+    f = L.gemm_a8w8_ptpc_gathered
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 3 + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                                                 ctypes.c_int, ctypes.c_uint32, ctypes.c_int64,
+                                                                 ctypes.c_void_p, ctypes.c_void_p]
+    assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, m, 256, 256, ALIGNED, src_rows, nchunks, own, 7, spin,
+             ALIGNED, None) == 1
+    assert why in L.dmm_last_error().decode()
+    # flags and status must be given
+    assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 4096, 256, 256, None, 1024, 1, 0, 7, 10, ALIGNED,
+             None) == 1
+    assert b"flags" in L.dmm_last_error()
 
 
 def test_gemm_pointer_rules(L):

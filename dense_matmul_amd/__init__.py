@@ -6,7 +6,7 @@ current stream; there is no CPU fallback, and every call raises if the
 library is not built or the device is not a gfx950.
 
 Functions (names as in the C ABI):
-    quantize_per_token(x)             -> (q e4m3 [R,C], scale fp32 [R])
+    quantize_per_token(x)             -> (q e4m3 [R,C], scale fp32 [R]); x fp32 or bf16
     quantize_blockscale_a(x)          -> (q, scale fp32 [K/128, M])
     quantize_blockscale_b(x)          -> (q, scale fp32 [ceil(N/128), K/128])
     quantize_mxfp8(x)                 -> (q, scale e8m0 uint8 [K/32, R])
@@ -33,10 +33,9 @@ LIB_PATH = os.path.join(_HERE, "libdmm.so")
 DMM_OK, DMM_EINVAL, DMM_ENODEV, DMM_ELAUNCH = 0, 1, 2, 3
 
 EXPORTS = (
-    "dmm_status_str", "dmm_last_error", "quantize_per_token", "quantize_blockscale_a", "quantize_blockscale_b",
-    "quantize_mxfp8", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_ptpc_gathered", "gemm_a8w8_blockscale",
-    "gemm_a8w8_mxfp8",
-    "gemm_bf16",
+    "dmm_status_str", "dmm_last_error", "quantize_per_token", "quantize_per_token_bf16", "quantize_blockscale_a",
+    "quantize_blockscale_b", "quantize_mxfp8", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile",
+    "gemm_a8w8_ptpc_gathered", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8", "gemm_bf16",
 )
 
 _lib = None
@@ -55,7 +54,8 @@ def lib():
         L.dmm_status_str.restype = ctypes.c_char_p
         L.dmm_last_error.argtypes = []
         L.dmm_last_error.restype = ctypes.c_char_p
-        for name in ("quantize_per_token", "quantize_blockscale_a", "quantize_blockscale_b", "quantize_mxfp8"):
+        for name in ("quantize_per_token", "quantize_per_token_bf16", "quantize_blockscale_a", "quantize_blockscale_b",
+                     "quantize_mxfp8"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, P]
         L.preshuffle_b.argtypes = [P, P, I64, I64, P]
         for name in ("gemm_a8w8_ptpc", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8"):
@@ -118,8 +118,11 @@ def _shape(t, shape, name):
 
 # ------------------------------------------------------------ quantisers
 def quantize_per_token(x, q=None, scale=None):
-    """Per-row E4M3 quantisation (scale = amax/448) of fp32 x [R, C]."""
-    _require(x, "x", torch.float32, 2)
+    """Per-row E4M3 quantisation (scale = amax/448) of fp32 or bf16 x [R, C]
+    (bf16 calls quantize_per_token_bf16)."""
+    _require(x, "x", None, 2)
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"x: expected float32 or bfloat16, got {x.dtype}")
     r, c = x.shape
     q = torch.empty((r, c), dtype=torch.float8_e4m3fn, device=x.device) if q is None else q
     scale = torch.empty(r, dtype=torch.float32, device=x.device) if scale is None else scale
@@ -127,7 +130,8 @@ def quantize_per_token(x, q=None, scale=None):
     _require(scale, "scale", torch.float32, 1)
     _shape(q, (r, c), "q")
     _shape(scale, (r,), "scale")
-    _check(lib().quantize_per_token(_ptr(x), _ptr(_codes(q, "q")), _ptr(scale), r, c, _stream()))
+    fn = lib().quantize_per_token if x.dtype == torch.float32 else lib().quantize_per_token_bf16
+    _check(fn(_ptr(x), _ptr(_codes(q, "q")), _ptr(scale), r, c, _stream()))
     return q, scale
 
 

@@ -18,6 +18,7 @@ hipError_t launch_gemm_a8w8_gathered(const uint8_t* a, const uint8_t* b, const f
                                      hipStream_t stream);
 hipError_t launch_gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int m, int n, int k, hipStream_t st);
 hipError_t launch_quantize_rows(const float* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st);
+hipError_t launch_quantize_rows_bf16(const uint16_t* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st);
 hipError_t launch_quantize_blockscale_a(const float* x, uint8_t* q, float* s, int m, int k, hipStream_t st);
 hipError_t launch_quantize_blockscale_b(const float* x, uint8_t* q, float* s, int n, int k, hipStream_t st);
 hipError_t launch_quantize_mxfp8(const float* x, uint8_t* q, uint8_t* s, int rows, int k, hipStream_t st);
@@ -119,6 +120,20 @@ dmm_status quantize_per_token(const float* x, uint8_t* q, float* scale, int64_t 
     dmm_status s = check_device();
     if (s != DMM_OK) return s;
     return launched(dmm::launch_quantize_rows(x, q, scale, (int)rows, (int)cols, (hipStream_t)stream));
+}
+
+dmm_status quantize_per_token_bf16(const uint16_t* x, uint8_t* q, float* scale, int64_t rows, int64_t cols,
+                                   void* stream) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(scale);
+    REQUIRE(rows >= 1, "rows must be >= 1");
+    REQUIRE(cols >= 16 && cols % 16 == 0, "cols must be a positive multiple of 16 (got %lld)", (long long)cols);
+    REQUIRE(rows * cols * 2 < ((int64_t)1 << 40), "x is too large");
+    REQUIRE(rows < kLimit && cols < kLimit, "rows and cols must be < 2^31");
+    dmm_status s = check_device();
+    if (s != DMM_OK) return s;
+    return launched(dmm::launch_quantize_rows_bf16(x, q, scale, (int)rows, (int)cols, (hipStream_t)stream));
 }
 
 dmm_status quantize_blockscale_a(const float* x, uint8_t* q, float* scale, int64_t m, int64_t k, void* stream) {

@@ -49,21 +49,32 @@ __device__ __forceinline__ uint32_t pack4(v4f v, float s) {
 
 // ------------------------------------------------------------- per token
 // One wave per row; 4 rows per workgroup.  cols % 16 == 0.
-__global__ void __launch_bounds__(256) quantize_rows_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
+// Four consecutive values of a row as fp32: fp32 rows load 16 bytes, bf16
+// rows 8 bytes, widened exactly (a bf16 value is the high half of an fp32).
+__device__ __forceinline__ v4f load4(const float* xr, int c) { return ((const v4f*)xr)[c]; }
+__device__ __forceinline__ v4f load4(const uint16_t* xr, int c) {
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    const v2u w = ((const v2u*)xr)[c];
+    return (v4f){__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xFFFF0000u),
+                 __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xFFFF0000u)};
+}
+
+template <typename In>
+__global__ void __launch_bounds__(256) quantize_rows_kernel(const In* __restrict__ x, uint8_t* __restrict__ q,
                                                             float* __restrict__ scale, int rows, int cols) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
-    const v4f* xr = (const v4f*)(x + (size_t)row * cols);
+    const In* xr = x + (size_t)row * cols;
     uint32_t* qr = (uint32_t*)(q + (size_t)row * cols);
     const int n4 = cols / 4;
     float amax = 0.0f;
     for (int c = lane; c < n4; c += 64) {
-        const v4f v = xr[c];
+        const v4f v = load4(xr, c);
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     }
     const float s = amax_to_scale(wave_max(amax));
-    for (int c = lane; c < n4; c += 64) qr[c] = pack4(xr[c], s);
+    for (int c = lane; c < n4; c += 64) qr[c] = pack4(load4(xr, c), s);
     if (lane == 0) scale[row] = s;
 }
 
@@ -180,7 +191,12 @@ __global__ void __launch_bounds__(256) preshuffle_b_kernel(const uint8_t* __rest
 
 // -------------------------------------------------------------- launch
 hipError_t launch_quantize_rows(const float* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st) {
-    hipLaunchKernelGGL(quantize_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, x, q, s, rows, cols);
+    hipLaunchKernelGGL(quantize_rows_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, st, x, q, s, rows, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows_bf16(const uint16_t* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st) {
+    hipLaunchKernelGGL(quantize_rows_kernel<uint16_t>, dim3((rows + 3) / 4), dim3(256), 0, st, x, q, s, rows, cols);
     return hipGetLastError();
 }
 

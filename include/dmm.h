@@ -66,6 +66,12 @@ const char* dmm_last_error(void);
 dmm_status quantize_per_token(const float* x, uint8_t* q, float* scale, int64_t rows, int64_t cols,
                               void* stream);
 
+/* The same for bf16 activations: x [rows, cols] bf16 (uint16_t bit
+ * patterns), each value widened exactly to fp32, then the rule above.
+ * Same rules and outputs. */
+dmm_status quantize_per_token_bf16(const uint16_t* x, uint8_t* q, float* scale, int64_t rows, int64_t cols,
+                                   void* stream);
+
 /* Blockscale A: one fp32 scale per row per 128-wide K block (mori PR 785,
  * Cost: blockscale; the A scale is K-block major, mori PR 809, Not done yet).
  *   scale[kb * m + r] = amax(x[r, 128kb .. 128kb+127]) / 448 (1.0 if zero),

@@ -30,7 +30,7 @@ def L():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for f in ("quantize_per_token", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_ptpc_gathered",
+    for f in ("quantize_per_token", "quantize_per_token_bf16", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_ptpc_gathered",
               "gemm_a8w8_blockscale",
               "gemm_a8w8_mxfp8",
               "gemm_bf16", "quantize_blockscale_a", "quantize_blockscale_b", "quantize_mxfp8", "dmm_status_str",
@@ -110,6 +110,9 @@ def test_gemm_pointer_rules(L):
 def test_quantiser_and_preshuffle_rules(L):
     assert L.quantize_per_token(ALIGNED, ALIGNED, ALIGNED, 0, 256, None) == 1
     assert L.quantize_per_token(ALIGNED, ALIGNED, ALIGNED, 4, 17, None) == 1
+    L.quantize_per_token_bf16.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 2 + [ctypes.c_void_p]
+    assert L.quantize_per_token_bf16(ALIGNED, ALIGNED, ALIGNED, 4, 24, None) == 1
+    assert L.quantize_per_token_bf16(ALIGNED, ALIGNED, ALIGNED, 0, 32, None) == 1
     assert L.quantize_blockscale_a(ALIGNED, ALIGNED, ALIGNED, 4, 100, None) == 1
     assert L.quantize_blockscale_b(ALIGNED, ALIGNED, ALIGNED, 20, 128, None) == 1
     assert L.quantize_mxfp8(ALIGNED, ALIGNED, ALIGNED, 4, 96, None) == 1

@@ -76,6 +76,20 @@ def test_quantize_per_token_bitexact(dmm, rows, cols, seed):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
 
 
+@pytest.mark.parametrize("rows,cols,seed", [(512, 256, 21), (300, 1792, 22), (5, 7168, 23)])
+def test_quantize_per_token_bf16_input_bitexact(dmm, rows, cols, seed):
+    """bf16 activations: the oracle quantises the same values widened to fp32
+    (bf16 -> fp32 is exact), so codes and scales must match bitwise."""
+    announce("quantize_per_token bf16", rows, cols, seed)
+    x = torch.from_numpy(inputs.normal((rows, cols), seed)).to(torch.bfloat16)  # RNE on the CPU
+    x[0] = 0.0
+    x[1, 3] = 448.0 * 3.0
+    q, s = dmm.quantize_per_token(x.to(DEV))
+    oq, os_ = oracle.quantize_per_token(x.to(torch.float32).numpy())
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), oq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
 @pytest.mark.parametrize("m,k,seed", [(300, 384, 5), (64, 128, 6), (33, 2048, 7)])
 def test_quantize_blockscale_a_bitexact(dmm, m, k, seed):
     announce("quantize_blockscale_a", m, k, seed)

@@ -397,12 +397,13 @@ __device__ __forceinline__ void mfma_scaled_acc(v4f& acc, const v8i& b, const v8
                      : "v"(b), "v"(a), "v"(sb), "v"(sa), "n"(OA & 1), "n"(OB & 1), "n"(OA >> 1), "n"(OB >> 1));
 }
 
-// blockscale: acc[r] (+)= bp[r % 2] * sa(row, kt) * sb(block, kt).  The
-// products come from the matrix ops issued just before (at the latest two of
-// them earlier); the 20 wait states ahead of the first read cover the result
-// latency of the longest (16-pass) form of the instruction whatever the
-// compiler schedules in between, since the compiler cannot see the hazard
-// across the asm statements.
+// blockscale: acc[r] (+)= bp[r % 2] * sa(row, kt) * sb(block, kt).  The fp8
+// 16x16x128 matrix op has 8 passes, so a VALU read of its result needs 11
+// wait states, which the compiler cannot see across the asm statements.
+// Row block r's products are folded after row block r + 1's two matrix ops
+// and the 10 wait states of the s_nop pair: 12 whatever the compiler
+// schedules in between.  The last row block's come after the previous
+// fold (10 nops, 8 VALU) and its own 10 nops.
 template <int MODE, int T, int r, bool FIRST>
 __device__ __forceinline__ void fold_products(Ctx<MODE>& x) {
     const float s = x.sfa[T][r / 4][r % 4] * x.sfb[T];
@@ -411,7 +412,7 @@ __device__ __forceinline__ void fold_products(Ctx<MODE>& x) {
     const v4f p0 = x.bp[r & 1][0], p1 = x.bp[r & 1][1];
     if constexpr (FIRST) {
         asm volatile(
-            "s_nop 7\n\ts_nop 7\n\ts_nop 3\n\t"
+            "s_nop 7\n\ts_nop 1\n\t"
             "v_mul_f32 %0, %8, %16\n\tv_mul_f32 %1, %9, %16\n\tv_mul_f32 %2, %10, %16\n\tv_mul_f32 %3, %11, %16\n\t"
             "v_mul_f32 %4, %12, %16\n\tv_mul_f32 %5, %13, %16\n\tv_mul_f32 %6, %14, %16\n\tv_mul_f32 %7, %15, %16"
             : "=&v"(c0[0]), "=&v"(c0[1]), "=&v"(c0[2]), "=&v"(c0[3]), "=&v"(c1[0]), "=&v"(c1[1]), "=&v"(c1[2]),
@@ -419,7 +420,7 @@ __device__ __forceinline__ void fold_products(Ctx<MODE>& x) {
             : "v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(p1[0]), "v"(p1[1]), "v"(p1[2]), "v"(p1[3]), "v"(s));
     } else {
         asm volatile(
-            "s_nop 7\n\ts_nop 7\n\ts_nop 3\n\t"
+            "s_nop 7\n\ts_nop 1\n\t"
             "v_fmac_f32 %0, %8, %16\n\tv_fmac_f32 %1, %9, %16\n\tv_fmac_f32 %2, %10, %16\n\tv_fmac_f32 %3, %11, %16\n\t"
             "v_fmac_f32 %4, %12, %16\n\tv_fmac_f32 %5, %13, %16\n\tv_fmac_f32 %6, %14, %16\n\tv_fmac_f32 %7, %15, %16"
             : "+v"(c0[0]), "+v"(c0[1]), "+v"(c0[2]), "+v"(c0[3]), "+v"(c1[0]), "+v"(c1[1]), "+v"(c1[2]), "+v"(c1[3])

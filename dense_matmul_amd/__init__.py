@@ -17,7 +17,7 @@ Functions (names as in the C ABI):
                             spin_limit=1 << 22, status=None, out=None) -> (bf16 [M,N], status)
     gemm_a8w8_blockscale(a, b_shuf, a_scale, b_scale, out=None) -> bf16 [M,N]
     gemm_a8w8_mxfp8(a, b_shuf, a_scale, b_scale, out=None)      -> bf16 [M,N]
-    gemm_bf16(a, b, out=None)                                    -> bf16 [M,N]
+    gemm_bf16(a, b, out=None, tile="auto")                       -> bf16 [M,N]
 
 Argument errors (status DMM_EINVAL) raise ValueError; everything else raises
 RuntimeError.
@@ -35,7 +35,7 @@ DMM_OK, DMM_EINVAL, DMM_ENODEV, DMM_ELAUNCH = 0, 1, 2, 3
 EXPORTS = (
     "dmm_status_str", "dmm_last_error", "quantize_per_token", "quantize_per_token_bf16", "quantize_blockscale_a",
     "quantize_blockscale_b", "quantize_mxfp8", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile",
-    "gemm_a8w8_ptpc_gathered", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8", "gemm_bf16",
+    "gemm_a8w8_ptpc_gathered", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8", "gemm_bf16", "gemm_bf16_tile",
 )
 
 _lib = None
@@ -64,6 +64,7 @@ def lib():
         L.gemm_a8w8_ptpc_gathered.argtypes = [P, P, P, P, P, I64, I64, I64, P, I64, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_uint32, I64, P, P]
         L.gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
+        L.gemm_bf16_tile.argtypes = [P, P, P, I64, I64, I64, ctypes.c_int, P]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -267,8 +268,12 @@ def gemm_a8w8_mxfp8(a, b_shuf, a_scale, b_scale, out=None):
     return out
 
 
-def gemm_bf16(a, b, out=None):
-    """C = bf16(sum_k a[m,k] b[n,k]) with fp32 accumulation; a [M,K], b [N,K] bf16."""
+BF16_TILES = {"128x128": 1, "64x64": 2}
+
+
+def gemm_bf16(a, b, out=None, tile="auto"):
+    """C = bf16(sum_k a[m,k] b[n,k]) with fp32 accumulation; a [M,K], b [N,K] bf16.
+    tile: "auto", "128x128" or "64x64" (same result)."""
     _require(a, "a", torch.bfloat16, 2)
     _require(b, "b", torch.bfloat16, 2)
     m, k = a.shape
@@ -278,5 +283,10 @@ def gemm_bf16(a, b, out=None):
     out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device) if out is None else out
     _require(out, "out", torch.bfloat16, 2)
     _shape(out, (m, n), "out")
-    _check(lib().gemm_bf16(_ptr(a), _ptr(b), _ptr(out), m, n, k, _stream()))
+    if tile == "auto":
+        _check(lib().gemm_bf16(_ptr(a), _ptr(b), _ptr(out), m, n, k, _stream()))
+    else:
+        if tile not in BF16_TILES:
+            raise ValueError(f"tile must be 'auto' or one of {sorted(BF16_TILES)} (got {tile!r})")
+        _check(lib().gemm_bf16_tile(_ptr(a), _ptr(b), _ptr(out), m, n, k, BF16_TILES[tile], _stream()))
     return out

@@ -16,7 +16,8 @@ hipError_t launch_gemm_a8w8_gathered(const uint8_t* a, const uint8_t* b, const f
                                      uint16_t* c, int m, int n, int k, const uint32_t* flags, int src_rows,
                                      int nchunks, int own, uint32_t epoch, long long spin_limit, int* status,
                                      hipStream_t stream);
-hipError_t launch_gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int m, int n, int k, hipStream_t st);
+hipError_t launch_gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int m, int n, int k, int tile,
+                            hipStream_t st);
 hipError_t launch_quantize_rows(const float* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st);
 hipError_t launch_quantize_rows_bf16(const uint16_t* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st);
 hipError_t launch_quantize_blockscale_a(const float* x, uint8_t* q, float* s, int m, int k, hipStream_t st);
@@ -233,10 +234,12 @@ dmm_status gemm_a8w8_mxfp8(const uint8_t* a, const uint8_t* b_shuf, const uint8_
     return gemm_common(2, 0, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
 }
 
-dmm_status gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream) {
+dmm_status gemm_bf16_tile(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t m, int64_t n, int64_t k,
+                          int tile, void* stream) {
     REQUIRE_PTR(a);
     REQUIRE_PTR(b);
     REQUIRE_PTR(c);
+    REQUIRE(tile >= 0 && tile <= 2, "tile must be 0 (auto), 1 (128x128) or 2 (64x64) (got %d)", tile);
     REQUIRE(m >= 1, "m must be >= 1 (got %lld)", (long long)m);
     REQUIRE(n >= 16 && n % 16 == 0, "n must be a positive multiple of 16 (got %lld)", (long long)n);
     REQUIRE(k >= 64 && k % 64 == 0, "k must be a positive multiple of 64 (got %lld)", (long long)k);
@@ -244,7 +247,11 @@ dmm_status gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t 
             "operands are too large (each must be < 2^31 bytes with a 256-row margin)");
     dmm_status s = check_device();
     if (s != DMM_OK) return s;
-    return launched(dmm::launch_gemm_bf16(a, b, c, (int)m, (int)n, (int)k, (hipStream_t)stream));
+    return launched(dmm::launch_gemm_bf16(a, b, c, (int)m, (int)n, (int)k, tile, (hipStream_t)stream));
+}
+
+dmm_status gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream) {
+    return gemm_bf16_tile(a, b, c, m, n, k, 0, stream);
 }
 
 }  // extern "C"

@@ -3,16 +3,23 @@
 // DeepGEMM PR 453 ("Fix SM120 BF16 GEMM shared-memory reuse ordering",
 // Reproduction and validation): [4096, 1024] x [1024, 896].
 //
-// 128 x 128 output tile per 256-thread workgroup, 2 x 2 waves of 64 x 64.
-// Both operands stream global -> LDS by direct-to-LDS buffer loads into a
-// 3-stage ring of separate arrays (K tile 64 = 128 B per row, 16-byte chunks
-// XOR-swizzled by row & 7); v_mfma_f32_16x16x32_bf16 with src0 = B rows
-// (output columns) and src1 = A rows (output rows), so each lane ends with 4
-// consecutive output columns of one row.  The stage written by a refill was
-// last read one step earlier; the barrier that ends that step (after
-// lgkmcnt(0)) orders the reads before the refill, and the wait before it
-// (vmcnt) makes the next stage complete in every wave before anyone reads it.
+// BM x BN output tile per 256-thread workgroup, 2 x 2 waves of BM/2 x BN/2.
+// Both operands stream global -> LDS by direct-to-LDS buffer loads into an
+// NS-stage ring of separate arrays (K tile 64 = 128 B per row, 16-byte chunks
+// placed by lds::bf16_chunk_pos, conflict-free for the fragment reads),
+// refilled NS - 1 K tiles ahead;
+// v_mfma_f32_16x16x32_bf16 with src0 = B rows (output columns) and src1 =
+// A rows (output rows), so each lane ends with 4 consecutive output columns
+// of one row.  The stage written by a refill was last read one step
+// earlier; the barrier that ends that step (after lgkmcnt(0)) orders the
+// reads before the refill, and the wait before it (vmcnt) makes the next
+// stage complete in every wave before anyone reads it.
+//
+// Two tile sizes: 128 x 128 with 4 stages (one workgroup per CU, 128 KiB of
+// LDS) in general, and 64 x 64 with 3 stages (48 KiB, three workgroups per
+// CU) for grids too small to occupy half the CUs with 128 x 128 tiles.
 #include "common.h"
+#include "lds_layout.h"
 
 #include <type_traits>
 
@@ -21,87 +28,111 @@ namespace dmm {
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 
 namespace bf16k {
-constexpr int BM = 128, BN = 128, BK = 64, NT = 256, STAGE = BM * BK * 2;  // 16 KiB per operand per stage
-constexpr int NL = STAGE / 1024 / 4;  // DMA instructions per wave per operand per stage (4)
+constexpr int BK = 64, NT = 256;
 
-__shared__ __attribute__((aligned(1024))) char g_a0[STAGE];
-__shared__ __attribute__((aligned(1024))) char g_a1[STAGE];
-__shared__ __attribute__((aligned(1024))) char g_a2[STAGE];
-__shared__ __attribute__((aligned(1024))) char g_b0[STAGE];
-__shared__ __attribute__((aligned(1024))) char g_b1[STAGE];
-__shared__ __attribute__((aligned(1024))) char g_b2[STAGE];
+template <int BM, int BN>
+struct Cfg {
+    static constexpr int NS = BM == 128 ? 4 : 3;              // LDS stages
+    static constexpr int SA = BM * BK * 2, SB = BN * BK * 2;  // bytes per stage
+    static constexpr int NLA = SA / 1024 / 4, NLB = SB / 1024 / 4;  // 1 KiB DMAs per wave per stage
+    static constexpr int MBW = BM / 32, NBW = BN / 32;  // 16 x 16 blocks per wave
+    static_assert(NLA >= 1 && NLB >= 1, "at least one DMA per wave per operand");
+};
 
-template <int S>
-__device__ __forceinline__ char* sa() {
-    if constexpr (S == 0) return g_a0;
-    else if constexpr (S == 1) return g_a1;
-    else return g_a2;
-}
-template <int S>
-__device__ __forceinline__ char* sb() {
-    if constexpr (S == 0) return g_b0;
-    else if constexpr (S == 1) return g_b1;
-    else return g_b2;
-}
+// The LDS ring: the kernel declares the arrays (one object per stage, so the
+// compiler's LDS-DMA dependency tracking tells them apart) and carries their
+// addresses here; after inlining they are constants again.
+struct Ring {
+    lds_char* a[4];
+    lds_char* b[4];
+};
 
+template <int BM, int BN>
 struct Ctx {
+    using C = Cfg<BM, BN>;
+    Ring lds;
     const void *pa, *pb;
     uint32_t na, nb;
     int KT, wm, wn, lane, i, g;
-    int dma_lds;
-    int voff_a[NL], voff_b[NL];
+    int voff_a[C::NLA], voff_b[C::NLB];
     int rd[2];  // LDS byte offset of this lane's 16-byte chunk for MFMA k-half 0 / 1
-    v4f acc[4][4];
+    v4f acc[C::MBW][C::NBW];
 };
 
 // Tile kt into stage S.  Tiles past the end go through zero-length
 // descriptors: no data moves, the instructions still count in vmcnt, so every
 // wait below is a constant.
-template <int S>
-__device__ __forceinline__ void issue(Ctx& x, int kt) {
+template <int BM, int BN, int S>
+__device__ __forceinline__ void issue(Ctx<BM, BN>& x, int kt) {
+    using C = Cfg<BM, BN>;
     const bool valid = kt < x.KT;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(x.pa, valid ? x.na : 0u);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(x.pb, valid ? x.nb : 0u);
+    const int w = wave_id();
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-        lds_dma16(ra, (lds_char*)(sa<S>() + x.dma_lds + j * 1024), x.voff_a[j] + kt * BK * 2);
-        lds_dma16(rb, (lds_char*)(sb<S>() + x.dma_lds + j * 1024), x.voff_b[j] + kt * BK * 2);
-    }
+    for (int j = 0; j < C::NLA; ++j)
+        lds_dma16(ra, x.lds.a[S] + (C::NLA * w + j) * 1024, x.voff_a[j] + kt * BK * 2);
+#pragma unroll
+    for (int j = 0; j < C::NLB; ++j)
+        lds_dma16(rb, x.lds.b[S] + (C::NLB * w + j) * 1024, x.voff_b[j] + kt * BK * 2);
 }
 
-template <int S>
-__device__ __forceinline__ void compute(Ctx& x) {
+template <int BM, int BN, int S, int KK>
+__device__ __forceinline__ void read_frags(const Ctx<BM, BN>& x, bf8 (&af)[Cfg<BM, BN>::MBW],
+                                           bf8 (&bfr)[Cfg<BM, BN>::NBW]) {
+    using C = Cfg<BM, BN>;
+    typedef __attribute__((address_space(3))) const bf8 lds_bf8;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        bf8 af[4], bfr[4];
+    for (int q = 0; q < C::MBW; ++q) af[q] = *(lds_bf8*)(x.lds.a[S] + ((BM / 2) * x.wm + 16 * q) * 128 + x.rd[KK]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            af[q] = *(const bf8*)(sa<S>() + (64 * x.wm + 16 * q) * 128 + x.rd[kk]);
-            bfr[q] = *(const bf8*)(sb<S>() + (64 * x.wn + 16 * q) * 128 + x.rd[kk]);
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-                x.acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nb], af[mb], x.acc[mb][nb], 0, 0, 0);
-    }
+    for (int q = 0; q < C::NBW; ++q) bfr[q] = *(lds_bf8*)(x.lds.b[S] + ((BN / 2) * x.wn + 16 * q) * 128 + x.rd[KK]);
 }
 
-// Step kt computes stage S = kt % 3 and refills stage (kt + 2) % 3.
-template <int S>
-__device__ __forceinline__ void step(Ctx& x, int kt) {
-    issue<(S + 2) % 3>(x, kt + 2);
-    compute<S>(x);
-    // tile kt+1 was issued one step (2 NL instructions) before tile kt+2
-    wait_vm_lgkm0<2 * NL>();
+// The two 32-wide k-halves of stage S: the second half's fragments are read
+// while the first half's matrix ops run.
+template <int BM, int BN, int S>
+__device__ __forceinline__ void compute(Ctx<BM, BN>& x) {
+    using C = Cfg<BM, BN>;
+    bf8 a0[C::MBW], b0[C::NBW], a1[C::MBW], b1[C::NBW];
+    read_frags<BM, BN, S, 0>(x, a0, b0);
+    read_frags<BM, BN, S, 1>(x, a1, b1);
+#pragma unroll
+    for (int mb = 0; mb < C::MBW; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NBW; ++nb)
+            x.acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[nb], a0[mb], x.acc[mb][nb], 0, 0, 0);
+#pragma unroll
+    for (int mb = 0; mb < C::MBW; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NBW; ++nb)
+            x.acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[nb], a1[mb], x.acc[mb][nb], 0, 0, 0);
+}
+
+// Step kt computes stage S = kt % NS and refills stage (kt + NS - 1) % NS
+// (the one step kt - 1 read).
+template <int BM, int BN, int S>
+__device__ __forceinline__ void step(Ctx<BM, BN>& x, int kt) {
+    using C = Cfg<BM, BN>;
+    constexpr int NS = C::NS;
+    issue<BM, BN, (S + NS - 1) % NS>(x, kt + NS - 1);
+    compute<BM, BN, S>(x);
+    // tile kt+1 was followed by the NS - 2 later tiles' loads
+    wait_vm_lgkm0<(NS - 2) * (C::NLA + C::NLB)>();
     __builtin_amdgcn_s_barrier();
 }
 }  // namespace bf16k
 
-__global__ void __launch_bounds__(bf16k::NT, 1) gemm_bf16_kernel(const uint16_t* a, const uint16_t* b, uint16_t* c, int m,
-                                                                 int n, int k, int tiles_n) {
+template <int BM, int BN>
+__global__ void __launch_bounds__(bf16k::NT) gemm_bf16_kernel(const uint16_t* a, const uint16_t* b, uint16_t* c, int m,
+                                                              int n, int k, int tiles_n) {
     using namespace bf16k;
-    Ctx x;
+    using C = Cfg<BM, BN>;
+    constexpr int NS = C::NS;
+    __shared__ __attribute__((aligned(1024))) char a0[C::SA], a1[C::SA], a2[C::SA], a3[NS == 4 ? C::SA : 16];
+    __shared__ __attribute__((aligned(1024))) char b0[C::SB], b1[C::SB], b2[C::SB], b3[NS == 4 ? C::SB : 16];
+    Ctx<BM, BN> x;
+    x.lds = Ring{{(lds_char*)a0, (lds_char*)a1, (lds_char*)a2, (lds_char*)a3},
+                 {(lds_char*)b0, (lds_char*)b1, (lds_char*)b2, (lds_char*)b3}};
     const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
     const int w = wave_id();
@@ -115,42 +146,52 @@ __global__ void __launch_bounds__(bf16k::NT, 1) gemm_bf16_kernel(const uint16_t*
     x.na = (uint32_t)m * (uint32_t)k * 2u;
     x.pb = b;
     x.nb = (uint32_t)n * (uint32_t)k * 2u;
-    x.dma_lds = w * NL * 1024;
+    // DMA j of wave w moves rows 8 (NL w + j) .. + 7 (128 bytes each); lane l
+    // fetches row 8 (NL w + j) + l / 8, the chunk that belongs at byte 16 l
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-        const int r = 8 * (NL * w + j) + (x.lane >> 3);
-        const int chunk = (x.lane & 7) ^ (r & 7);
-        x.voff_a[j] = ((m0 + r) * k) * 2 + chunk * 16;
-        x.voff_b[j] = ((n0 + r) * k) * 2 + chunk * 16;
+    for (int j = 0; j < C::NLA; ++j) {
+        const int r = 8 * (C::NLA * w + j) + (x.lane >> 3);
+        x.voff_a[j] = ((m0 + r) * k) * 2 + lds::bf16_chunk_pos(r, x.lane & 7) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < C::NLB; ++j) {
+        const int r = 8 * (C::NLB * w + j) + (x.lane >> 3);
+        x.voff_b[j] = ((n0 + r) * k) * 2 + lds::bf16_chunk_pos(r, x.lane & 7) * 16;
     }
     // MFMA k-half kk: lane (i, g) reads row 16 q + i, 16-byte chunk 4 kk + g
+    // (the position depends on (row >> 1) & 7, the same for every q)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) x.rd[kk] = x.i * 128 + (((4 * kk + x.g) ^ (x.i & 7)) * 16);
+    for (int kk = 0; kk < 2; ++kk) x.rd[kk] = x.i * 128 + lds::bf16_chunk_pos(x.i, 4 * kk + x.g) * 16;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < C::MBW; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) x.acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < C::NBW; ++nb) x.acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    issue<0>(x, 0);
-    issue<1>(x, 1);
-    wait_vm_lgkm0<2 * NL>();
+    // prologue: tiles 0 .. NS-2; wait for tile 0
+    issue<BM, BN, 0>(x, 0);
+    issue<BM, BN, 1>(x, 1);
+    if constexpr (NS == 4) issue<BM, BN, 2>(x, 2);
+    wait_vm_lgkm0<(NS - 2) * (C::NLA + C::NLB)>();
     __builtin_amdgcn_s_barrier();
-    for (int kt = 0; kt < x.KT; kt += 3) {
-        step<0>(x, kt);
-        if (kt + 1 < x.KT) step<1>(x, kt + 1);
-        if (kt + 2 < x.KT) step<2>(x, kt + 2);
+    for (int kt = 0; kt < x.KT; kt += NS) {
+        step<BM, BN, 0>(x, kt);
+        if (kt + 1 < x.KT) step<BM, BN, 1>(x, kt + 1);
+        if (kt + 2 < x.KT) step<BM, BN, 2>(x, kt + 2);
+        if constexpr (NS == 4)
+            if (kt + 3 < x.KT) step<BM, BN, 3>(x, kt + 3);
     }
 
-    // lane (i, g), block (mb, nb): row m0 + 64 wm + 16 mb + i, columns
-    // n0 + 64 wn + 16 nb + 4 g + [0, 4)
+    // lane (i, g), block (mb, nb): row m0 + BM/2 wm + 16 mb + i, columns
+    // n0 + BN/2 wn + 16 nb + 4 g + [0, 4); rows past M fall outside the
+    // descriptor, column blocks past N are skipped
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(c, (uint32_t)m * (uint32_t)n * 2u);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int col = n0 + 64 * x.wn + 16 * nb;
+    for (int nb = 0; nb < C::NBW; ++nb) {
+        const int col = n0 + (BN / 2) * x.wn + 16 * nb;
         if (col >= n) continue;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            const int row = m0 + 64 * x.wm + 16 * mb + x.i;
+        for (int mb = 0; mb < C::MBW; ++mb) {
+            const int row = m0 + (BM / 2) * x.wm + 16 * mb + x.i;
             const v4f v = x.acc[mb][nb];
             v2i packed = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
             __builtin_amdgcn_raw_buffer_store_b64(packed, rc, (row * n + col + 4 * x.g) * 2, 0, 0);
@@ -158,10 +199,36 @@ __global__ void __launch_bounds__(bf16k::NT, 1) gemm_bf16_kernel(const uint16_t*
     }
 }
 
-hipError_t launch_gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int m, int n, int k, hipStream_t st) {
-    const int tiles_m = (m + bf16k::BM - 1) / bf16k::BM, tiles_n = (n + bf16k::BN - 1) / bf16k::BN;
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tiles_m * tiles_n), dim3(bf16k::NT), 0, st, a, b, c, m, n, k, tiles_n);
+template <int BM, int BN>
+static hipError_t launch_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int m, int n, int k, hipStream_t st) {
+    const int tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN>), dim3(tiles_m * tiles_n), dim3(bf16k::NT), 0, st, a, b, c, m, n, k,
+                       tiles_n);
     return hipGetLastError();
+}
+
+static int bf16_device_cus() {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+// tile 0: the library's choice (64 x 64 when the 128 x 128 grid would leave
+// at least half the CUs idle), 1: 128 x 128, 2: 64 x 64.
+hipError_t launch_gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int m, int n, int k, int tile,
+                            hipStream_t st) {
+    if (tile == 0) {
+        const long big = (long)((m + 127) / 128) * ((n + 127) / 128);
+        tile = 2 * big <= bf16_device_cus() ? 2 : 1;
+    }
+    if (tile == 2) return launch_bf16<64, 64>(a, b, c, m, n, k, st);
+    return launch_bf16<128, 128>(a, b, c, m, n, k, st);
 }
 
 }  // namespace dmm

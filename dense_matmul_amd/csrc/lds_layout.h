@@ -48,5 +48,16 @@ constexpr int frag_base(int i, int g, int odd_mb, int half, int MB) {
 }
 constexpr int frag_byte(int i, int g, int mb, int half, int MB) { return frag_base(i, g, mb & 1, half, MB) + 128 * mb; }
 
+// The bf16 GEMM's stages: rows of 128 bytes (64 bf16 of one K tile), 16-byte
+// chunk c of row r at position c ^ ((r >> 1) & 7).  Its fragment reads take
+// rows 16 q + i (i = 0..15) and one chunk for all 16 lanes of a phase; rows
+// i and i + 1 differ in 128-byte parity (the two halves of the 256 bytes of
+// bank space) and, within a parity, (i >> 1) & 7 takes all eight values, so
+// the phase touches 16 distinct 16-byte bank groups.  (Swizzling by r & 7
+// would put rows i and i + 8 on the same banks.)  The DMA writes lane l of
+// a 1 KiB instruction at row 8 q + l / 8, position l % 8, and fetches the
+// chunk that belongs there.
+constexpr int bf16_chunk_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
+
 }  // namespace lds
 }  // namespace dmm

@@ -174,6 +174,13 @@ dmm_status gemm_a8w8_mxfp8(const uint8_t* a, const uint8_t* b_shuf, const uint8_
 dmm_status gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t m, int64_t n, int64_t k,
                      void* stream);
 
+/* gemm_bf16 with an explicit output-tile shape, the same result: tile 1 =
+ * 128 x 128, 2 = 64 x 64, 0 = gemm_bf16's choice (64 x 64 when the problem
+ * has at most one 128 x 128 tile per two compute units).  Other values
+ * return DMM_EINVAL. */
+dmm_status gemm_bf16_tile(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t m, int64_t n, int64_t k,
+                          int tile, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     for f in ("quantize_per_token", "quantize_per_token_bf16", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_ptpc_gathered",
               "gemm_a8w8_blockscale",
               "gemm_a8w8_mxfp8",
-              "gemm_bf16", "quantize_blockscale_a", "quantize_blockscale_b", "quantize_mxfp8", "dmm_status_str",
+              "gemm_bf16", "gemm_bf16_tile", "quantize_blockscale_a", "quantize_blockscale_b", "quantize_mxfp8", "dmm_status_str",
               "dmm_last_error"):
         assert f in names, f
 
@@ -96,6 +96,15 @@ def test_gathered_rules(L, m, src_rows, nchunks, own, spin, why):
     assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 4096, 256, 256, None, 1024, 1, 0, 7, 10, ALIGNED,
              None) == 1
     assert b"flags" in L.dmm_last_error()
+
+
+def test_bf16_tile_rule(L):
+    f = L.gemm_bf16_tile
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_void_p]
+    for tile in (-1, 3):
+        assert f(ALIGNED, ALIGNED, ALIGNED, 64, 256, 256, tile, None) == 1
+        assert b"tile must be" in L.dmm_last_error()
+    assert f(ALIGNED, ALIGNED, ALIGNED, 64, 24, 256, 2, None) == 1
 
 
 def test_gemm_pointer_rules(L):

@@ -294,26 +294,31 @@ def test_bit_stable_under_concurrent_copy(dmm, mode):
     assert not np.isnan(bits_to_f64(outs[0])).any()
 
 
-def test_bf16_gemm(dmm):
+@pytest.mark.parametrize("tile", ["auto", "128x128", "64x64"])
+def test_bf16_gemm(dmm, tile):
     m, k, n = GOLD["bf16_shape_mkn"]["value"]
-    announce("bf16", m, k, n)
+    announce("bf16", m, k, n, tile)
     a32, b_kn = inputs.bf16_operands(m, k, n, GOLD["bf16_seed"]["value"])
     a = torch.from_numpy(a32).to(torch.bfloat16)
     b = torch.from_numpy(np.ascontiguousarray(b_kn.T)).to(torch.bfloat16)  # [N, K]
-    c = dmm.gemm_bf16(a.to(DEV), b.to(DEV))
+    c = dmm.gemm_bf16(a.to(DEV), b.to(DEV), tile=tile)
     ref = oracle.gemm_bf16(a.view(torch.int16).numpy().view(np.uint16), b.view(torch.int16).numpy().view(np.uint16))
-    check_close(bf16_bits(c), ref, "bf16 4096x1024x896")
-    outs = [bf16_bits(dmm.gemm_bf16(a.to(DEV), b.to(DEV))) for _ in range(20)]
+    check_close(bf16_bits(c), ref, f"bf16 4096x1024x896 {tile}")
+    outs = [bf16_bits(dmm.gemm_bf16(a.to(DEV), b.to(DEV), tile=tile)) for _ in range(20)]
     assert all(np.array_equal(o, outs[0]) for o in outs)
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 16, 64), (200, 272, 192), (129, 144, 1024)])
-def test_bf16_gemm_edges(dmm, m, n, k):
-    announce("bf16 edge", m, n, k)
+@pytest.mark.parametrize("tile", ["128x128", "64x64"])
+@pytest.mark.parametrize("m,n,k", [(1, 16, 64), (200, 272, 192), (129, 144, 1024), (300, 1040, 320)])
+def test_bf16_gemm_edges(dmm, m, n, k, tile):
+    """Exact inputs (small integers and halves, sums far below 2^24): bitwise
+    equal to the oracle on both tile shapes, with partial row and column
+    tiles and K tile counts that end mid-way through the 3-stage ring."""
+    announce("bf16 edge", m, n, k, tile)
     vals = np.array([0, 1, -1, 2, -2, 0.5], np.float32)
     a = torch.from_numpy(inputs.choice((m, k), vals, m)).to(torch.bfloat16)
     b = torch.from_numpy(inputs.choice((n, k), vals, n)).to(torch.bfloat16)
-    c = dmm.gemm_bf16(a.to(DEV), b.to(DEV))
+    c = dmm.gemm_bf16(a.to(DEV), b.to(DEV), tile=tile)
     ref = oracle.gemm_bf16(a.view(torch.int16).numpy().view(np.uint16), b.view(torch.int16).numpy().view(np.uint16))
     assert np.array_equal(bf16_bits(c), ref)
 

@@ -45,6 +45,7 @@ int dma_lds_byte(int b, int l) { return lds::dma_lds_byte(b, l); }
 int dma_row(int b, int l, int MB) { return lds::dma_row(b, l, MB); }
 int dma_chunk(int b, int l, int MB) { return lds::dma_chunk(b, l, MB); }
 int frag_byte(int i, int g, int mb, int half, int MB) { return lds::frag_byte(i, g, mb, half, MB); }
+int bf16_chunk_pos(int r, int c) { return lds::bf16_chunk_pos(r, c); }
 }
 """
 
@@ -58,7 +59,7 @@ def shim(tmp_path_factory):
     subprocess.run(["g++", "-std=c++17", "-O1", "-shared", "-fPIC", "-I", CSRC, str(src), "-o", str(lib)], check=True)
     L = ctypes.CDLL(str(lib))
     for f in ("prologue_wait", "wait_at", "stage_of", "refill_stage", "dma_lds_byte", "dma_row", "dma_chunk",
-              "frag_byte", "dma_ahead_tile", "dma_ahead_kt", "case_of", "phase_advance"):
+              "frag_byte", "dma_ahead_tile", "dma_ahead_kt", "case_of", "phase_advance", "bf16_chunk_pos"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -287,3 +288,23 @@ def test_fragment_reads_are_bank_conflict_free(shim, MB):
             for phase in range(4):
                 groups = {(shim.frag_byte(l % 16, l // 16, mb, half, MB) // 16) % 16 for l in range(16 * phase, 16 * phase + 16)}
                 assert len(groups) == 16, (MB, mb, half, phase, sorted(groups))
+
+
+# ------------------------------------------------------------ bf16 layout
+def test_bf16_layout_is_a_permutation_and_conflict_free(shim):
+    """bf16 GEMM stages (lds::bf16_chunk_pos): every row's 8 chunks land on 8
+    distinct positions, and each 16-lane phase of a fragment read (rows
+    16 q + i, one chunk) hits 16 distinct 16-byte bank groups."""
+    for r in range(128):
+        assert sorted(shim.bf16_chunk_pos(r, c) for c in range(8)) == list(range(8))
+    for q in range(8):
+        for c in range(8):
+            groups = {((16 * q + i) * 128 + shim.bf16_chunk_pos(16 * q + i, c) * 16) // 16 % 16 for i in range(16)}
+            assert len(groups) == 16, (q, c, sorted(groups))
+
+
+def test_bf16_old_swizzle_would_conflict():
+    """The r & 7 swizzle puts rows i and i + 8 on the same bank group: the
+    check above would reject it."""
+    groups = {(i * 128 + ((0 ^ (i & 7)) * 16)) // 16 % 16 for i in range(16)}
+    assert len(groups) == 8

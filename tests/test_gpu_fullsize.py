@@ -1,0 +1,69 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+bench times (the library's own tile choice, one call per GEMM).
+
+The inputs are the workloads' seeded N(0,1) operands quantised on the host
+by the oracle's quantisers (the GPU quantisers are tested bitwise against
+the same functions elsewhere), so no expected value comes from the GPU.
+Each GEMM runs twice into a NaN-poisoned C: the two results must be
+bitwise identical with no NaN left, and sampled rows (every row of the
+first and last 256-row tiles plus one per 64-row band) must meet the
+acceptance rule against the oracle, which computes only those rows.  The
+smaller workloads (512x1024x256, 4096x7168x256, 16384x7168x512,
+2048x1168x1792, the bf16 GEMM) are tested in full elsewhere."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dense_matmul_amd import inputs
+from oracle import tolerance
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+FULL = ["ptpc_32768x7168x1792", "blockscale_16384x7168x2048", "mxfp8_32768x7168x1792", "mxfp8_16384x7168x2048",
+        "ptpc_gathered_32768x6288x7168", "ptpc_gathered_32768x3648x7168"]
+MODE_ID = {"ptpc": 0, "blockscale": 1, "mxfp8": 2}
+
+
+@pytest.fixture(scope="module")
+def dmm():
+    import dense_matmul_amd as d
+
+    d.lib()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return d
+
+
+def quantise(mode, x, side):
+    if mode == "ptpc":
+        return oracle.quantize_per_token(x)
+    if mode == "blockscale":
+        return oracle.quantize_blockscale_a(x) if side == "a" else oracle.quantize_blockscale_b(x)
+    return oracle.quantize_mxfp8(x)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(dmm, name):
+    mode, m, n, k, seed_a, seed_b = inputs.WORKLOADS[name]
+    print("[case] full size", name, flush=True)
+    qa, sa = quantise(mode, inputs.operand_a(m, k, seed_a), "a")
+    qb, sb = quantise(mode, inputs.normal((n, k), seed_b), "b")
+    a, s_a, s_b = (torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for v in (qa, sa, sb))
+    b_shuf = dmm.preshuffle_b(torch.from_numpy(qb).to(DEV))
+    fn = {"ptpc": dmm.gemm_a8w8_ptpc, "blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
+    c = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    outs = []
+    for _ in range(2):
+        c.fill_(float("nan"))
+        fn(a, b_shuf, s_a, s_b, out=c)
+        torch.cuda.synchronize()
+        outs.append(c.view(torch.int16).cpu().numpy().view(np.uint16))
+    diff = np.count_nonzero(outs[1] != outs[0])
+    assert diff == 0, f"{name}: launch 1 differs from launch 0 in {diff} elements"
+    assert not np.isnan((outs[0].astype(np.uint32) << 16).view(np.float32)).any(), f"{name}: unwritten elements"
+    rows = inputs.rows_sample(m, seed=m + n + k)
+    ref = oracle.gemm_a8w8(MODE_ID[mode], qa, qb, sa, sb, rows=rows)
+    stats = tolerance.check(outs[0][rows], ref, f"{name} sampled rows", mode=mode, operands=(qa, qb, sa, sb),
+                            rows=rows)
+    print("[stats]", name, stats, flush=True)

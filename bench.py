@@ -11,7 +11,9 @@ algorithmic FLOPs per launch over its average launch time (HIP events on the
 launch stream) against the fp8 dense MFMA peak; traffic comes from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE summaries under profiles/ when they were
 taken for the current kernel, else null.  cpu_baseline is the CPU oracle
-timed on a bounded row sample of the same workload.
+timed on a bounded row sample of the same workload; its result is also
+compared with the GPU output of the timed run (the acceptance rule of
+oracle.tolerance) and the statistics reported as cpu_baseline.parity.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
 """
@@ -129,10 +131,12 @@ def traffic_from_profiles(kernel_tag):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(m, n, k, rows_n):
+def cpu_baseline(m, n, k, rows_n, gpu_c=None):
     """The oracle, untouched, on ``rows_n`` evenly spaced rows of the headline
     workload (all of it by default) with every thread of this process's CPU
-    share; returns TFLOP/s and the sample used."""
+    share; returns TFLOP/s and the sample used.  With gpu_c (the GPU's bf16
+    bits of the same workload), the oracle's rows are checked against it
+    after the timing."""
     import numpy as np
 
     import oracle
@@ -148,12 +152,24 @@ def cpu_baseline(m, n, k, rows_n):
     # where the machine's count is larger than the share)
     threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "0")) or 1 << 30)
     t0 = time.perf_counter()
-    oracle.gemm_ptpc(qa, qb, sa, sb, rows=rows, threads=threads)
+    ref = oracle.gemm_ptpc(qa, qb, sa, sb, rows=rows, threads=threads)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows_n * n * k
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": (f"{rows_n} evenly spaced rows of {m}" if rows_n < m else f"all {m} rows") +
-                      f" (all {n} columns, K={k}), GEMM only, {dt:.1f} s"}
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": (f"{rows_n} evenly spaced rows of {m}" if rows_n < m else f"all {m} rows") +
+                     f" (all {n} columns, K={k}), GEMM only, {dt:.1f} s"}
+    if gpu_c is not None:
+        from oracle import tolerance
+
+        got = gpu_c if rows is None else gpu_c[rows]
+        try:
+            st = tolerance.check(got, ref, "bench headline vs oracle", mode="ptpc", operands=(qa, qb, sa, sb),
+                                 rows=rows)
+            res["parity"] = {"rel_l2": st["rel_l2"], "elements": st["elements"], "max_err": st["max_err"],
+                             "secondary": st["primary_fail"], "ok": True}
+        except AssertionError as e:
+            res["parity"] = {"ok": False, "error": str(e)[:200]}
+    return res
 
 
 def main():
@@ -173,6 +189,7 @@ def main():
     qa, bs, sa, sb = headline_operands(dmm, torch, m, n, k, 31, 32)
     out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
     ms = timed(lambda: dmm.gemm_a8w8_ptpc(qa, bs, sa, sb, out=out), args.steps, args.warmup)
+    gpu_c = None if args.no_cpu else out.view(torch.int16).cpu().numpy().view("uint16")
     flops = 2.0 * m * n * k
     tflops = flops / (ms * 1e-3) / 1e12
     rec = {
@@ -197,7 +214,7 @@ def main():
     if args.extra:
         rec["extra"] = extra_shapes(dmm, torch, args)
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(m, n, k, args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(m, n, k, args.cpu_rows, gpu_c)
     print(json.dumps(rec), flush=True)
 
 

@@ -10,7 +10,11 @@ Prints ONE JSON line.  The roofline object reports the GEMM kernel's
 algorithmic FLOPs per launch over its average launch time (HIP events on the
 launch stream) against the fp8 dense MFMA peak; traffic comes from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE summaries under profiles/ when they were
-taken for the current kernel, else null.  cpu_baseline is the CPU oracle
+taken for the current kernel, else null.  Two context objects follow the
+timed run: mfma_ceiling, what the part sustains issuing nothing but the
+GEMM's matrix instruction (one and two waves per SIMD, dmm_mfma_ceiling_fp8),
+and vendor_baseline, the vendor library (hipBLASLt through torch._scaled_mm)
+on the same codes and scales.  cpu_baseline is the CPU oracle
 timed on a bounded row sample of the same workload; its result is also
 compared with the GPU output of the timed run (the acceptance rule of
 oracle.tolerance) and the statistics reported as cpu_baseline.parity.
@@ -64,7 +68,9 @@ def timed(fn, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
-def headline_operands(dmm, torch, m, n, k, seed_a, seed_b, mode="ptpc"):
+def headline_operands(dmm, torch, m, n, k, seed_a, seed_b, mode="ptpc", keep_b=False):
+    """Quantised operands on the GPU: (a codes, preshuffled b codes, a scale,
+    b scale[, b codes in plain order when keep_b])."""
     from dense_matmul_amd import inputs
 
     a32 = torch.from_numpy(inputs.operand_a(m, k, seed_a)).to("cuda:0")
@@ -81,7 +87,7 @@ def headline_operands(dmm, torch, m, n, k, seed_a, seed_b, mode="ptpc"):
     bs = dmm.preshuffle_b(qb)
     del a32, b32
     torch.cuda.synchronize()
-    return qa, bs, sa, sb
+    return (qa, bs, sa, sb, qb) if keep_b else (qa, bs, sa, sb)
 
 
 COPY_BYTES = 1 << 30
@@ -186,9 +192,12 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
     m, n, k = 32768, 7168, 1792
-    qa, bs, sa, sb = headline_operands(dmm, torch, m, n, k, 31, 32)
+    qa, bs, sa, sb, qb = headline_operands(dmm, torch, m, n, k, 31, 32, keep_b=True)
     out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
     ms = timed(lambda: dmm.gemm_a8w8_ptpc(qa, bs, sa, sb, out=out), args.steps, args.warmup)
+    # context, measured right after the timed run (the part as warm as it was)
+    ceiling = mfma_ceiling(dmm, torch, qa)
+    vendor = vendor_baseline(torch, qa, qb, sa, sb, out, args.steps, args.warmup)
     gpu_c = None if args.no_cpu else out.view(torch.int16).cpu().numpy().view("uint16")
     flops = 2.0 * m * n * k
     tflops = flops / (ms * 1e-3) / 1e12
@@ -209,13 +218,56 @@ def main():
                    "pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic_from_profiles("gemm_a8w8_ptpc")},
+        "mfma_ceiling": dict(ceiling, value_over_one_wave_ceiling=round(
+            tflops / ceiling["one_wave_per_simd_TFLOP/s"], 4)),
+        "vendor_baseline": vendor,
     }
-    del out
+    del out, qb
     if args.extra:
         rec["extra"] = extra_shapes(dmm, torch, args)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(m, n, k, args.cpu_rows, gpu_c)
     print(json.dumps(rec), flush=True)
+
+
+def mfma_ceiling(dmm, torch, frag, iters=1200, launches=40):
+    """What the part sustains issuing nothing but the GEMM's matrix op:
+    back-to-back independent fp8 16x16x128 ops on every SIMD, one and two
+    waves per SIMD, operands taken from the headline's own A codes
+    (dmm_mfma_ceiling_fp8).  TFLOP/s over HIP events on the launch stream."""
+    out = torch.empty(1 << 20, dtype=torch.float32, device="cuda:0")
+    res = {"kind": "back-to-back independent fp8 16x16x128 matrix ops (calibration kernel)"}
+    for wps, key in ((1, "one_wave_per_simd_TFLOP/s"), (2, "two_waves_per_simd_TFLOP/s")):
+        flops = dmm.mfma_ceiling_fp8(frag, iters, wps, out=out)[1]
+        ms = timed(lambda: dmm.mfma_ceiling_fp8(frag, iters, wps, out=out), launches, 10)
+        res[key] = round(flops / (ms * 1e-3) / 1e12, 1)
+    del out
+    return res
+
+
+def vendor_baseline(torch, qa, qb, sa, sb, ours, steps, warmup):
+    """The vendor library on the same codes and scales: torch._scaled_mm
+    (hipBLASLt on ROCm) with per-row A and per-column B fp32 scales, bf16
+    out, timed like the headline; its output is compared with this
+    library's (relative L2 distance)."""
+    lib = "hipBLASLt via torch._scaled_mm (per-row A / per-column B fp32 scales)"
+    try:
+        a8, b8 = qa.view(torch.float8_e4m3fn), qb.view(torch.float8_e4m3fn)
+        sa2, sb2 = sa.view(-1, 1), sb.view(1, -1)
+
+        def f():
+            return torch._scaled_mm(a8, b8.t(), scale_a=sa2, scale_b=sb2, out_dtype=torch.bfloat16)
+
+        ms = timed(f, steps, warmup)
+        c = f()
+        m, k = qa.shape
+        n = qb.shape[0]
+        rel = ((c.float() - ours.float()).norm() / ours.float().norm()).item()
+        del c
+        return {"library": lib, "us": round(ms * 1e3, 1), "TFLOP/s": round(2.0 * m * n * k / (ms * 1e-3) / 1e12, 1),
+                "rel_l2_vs_this_library": rel}
+    except Exception as e:  # an unsupported _scaled_mm form leaves only the error in the line
+        return {"library": lib, "error": f"{type(e).__name__}: {str(e)[:160]}"}
 
 
 def extra_shapes(dmm, torch, args):

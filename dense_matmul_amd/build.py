@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdmm.so")
-SOURCES = ["gemm_a8w8.hip", "gemm_bf16.hip", "quant.hip", "api.cpp"]
+SOURCES = ["gemm_a8w8.hip", "gemm_bf16.hip", "quant.hip", "calib.hip", "api.cpp"]
 ARCH = "gfx950"
 # packed-fp32 instructions are kept out of every kernel (-packed-fp32-ops)
 FLAGS = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

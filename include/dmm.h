@@ -181,6 +181,26 @@ dmm_status gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t 
 dmm_status gemm_bf16_tile(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t m, int64_t n, int64_t k,
                           int tile, void* stream);
 
+/* ------------------------------------------------------------ calibration */
+
+/* Matrix-core issue ceiling, for reading a GEMM's measured rate against what
+ * the part sustains rather than only against the published peak (mori PR
+ * 785, Cost, and the scope's target are stated as a fraction of the dense
+ * fp8 peak); not a step of the GEMM.  One workgroup per compute unit, with
+ * waves_per_simd (1 or 2) waves on each of its four SIMDs; every wave loads
+ * four A and four B fragments (32 bytes per lane each) from frag and issues
+ * iters x 16 back-to-back independent v_mfma_f32_16x16x128_f8f6f4 ops on
+ * them, then writes the sum of its accumulators to out[thread] for threads
+ * below out_len.  One launch does
+ *     2 * 16 * 16 * 128 * 16 * iters * (*workgroups) * 4 * waves_per_simd
+ * FLOPs; *workgroups (host pointer, may be NULL) receives the grid size (the
+ * device's compute-unit count).  frag: device, at least 2 MiB of e4m3 codes
+ * (the operand bytes change the power the part draws, so pass real codes);
+ * out: device fp32 [out_len].  Rules: 1 <= iters <= 2^20; waves_per_simd 1
+ * or 2; frag_bytes >= 2 MiB; 1 <= out_len < 2^31. */
+dmm_status dmm_mfma_ceiling_fp8(const uint8_t* frag, int64_t frag_bytes, float* out, int64_t out_len, int iters,
+                                int waves_per_simd, int* workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--extra", action="store_true", help="also time the other modes and shapes")
     p.add_argument("--cpu-rows", type=int, default=32768,
                    help="rows of the headline the oracle computes (default: all of them)")
+    p.add_argument("--calibrate", action="store_true",
+                   help="also time every variant of the matrix-op calibration kernel (what each kind of "
+                        "instruction interleaved with the matrix ops costs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 1 GiB HBM copy kernel 3 times (the reference dispatch for "
                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -196,7 +199,7 @@ def main():
     out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
     ms = timed(lambda: dmm.gemm_a8w8_ptpc(qa, bs, sa, sb, out=out), args.steps, args.warmup)
     # context, measured right after the timed run (the part as warm as it was)
-    ceiling = mfma_ceiling(dmm, torch, qa)
+    ceiling = mfma_ceiling(dmm, torch, qa, all_variants=args.calibrate)
     vendor = vendor_baseline(torch, qa, qb, sa, sb, out, args.steps, args.warmup)
     gpu_c = None if args.no_cpu else out.view(torch.int16).cpu().numpy().view("uint16")
     flops = 2.0 * m * n * k
@@ -230,17 +233,31 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def mfma_ceiling(dmm, torch, frag, iters=1200, launches=40):
+def mfma_ceiling(dmm, torch, frag, all_variants=False, iters=1200, launches=100):
     """What the part sustains issuing nothing but the GEMM's matrix op:
     back-to-back independent fp8 16x16x128 ops on every SIMD, one and two
     waves per SIMD, operands taken from the headline's own A codes
-    (dmm_mfma_ceiling_fp8).  TFLOP/s over HIP events on the launch stream."""
+    (dmm_mfma_ceiling_fp8).  With all_variants, also the mxfp8 form and the
+    same stream with one kind of instruction interleaved after each op, one
+    wave per SIMD.  TFLOP/s over HIP events on the launch stream."""
     out = torch.empty(1 << 20, dtype=torch.float32, device="cuda:0")
-    res = {"kind": "back-to-back independent fp8 16x16x128 matrix ops (calibration kernel)"}
-    for wps, key in ((1, "one_wave_per_simd_TFLOP/s"), (2, "two_waves_per_simd_TFLOP/s")):
-        flops = dmm.mfma_ceiling_fp8(frag, iters, wps, out=out)[1]
-        ms = timed(lambda: dmm.mfma_ceiling_fp8(frag, iters, wps, out=out), launches, 10)
-        res[key] = round(flops / (ms * 1e-3) / 1e12, 1)
+
+    def rate(wps, variant):
+        flops = dmm.mfma_ceiling_fp8(frag, iters, wps, variant, out=out)[1]
+        ms = timed(lambda: dmm.mfma_ceiling_fp8(frag, iters, wps, variant, out=out), launches, 10)
+        return round(flops / (ms * 1e-3) / 1e12, 1)
+
+    # the part's clock settles to a new load within a fraction of a second:
+    # run the plain stream ~0.3 s before the first figure
+    timed(lambda: dmm.mfma_ceiling_fp8(frag, iters, 1, "plain", out=out), 1000, 0)
+
+    res = {"kind": "back-to-back independent fp8 16x16x128 matrix ops (calibration kernel)",
+           "one_wave_per_simd_TFLOP/s": rate(1, "plain"), "two_waves_per_simd_TFLOP/s": rate(2, "plain")}
+    if all_variants:
+        res["one_wave_per_simd_variants_TFLOP/s"] = {
+            v: rate(1, v) for v in ("plain", "scaled", "lds_read", "valu2", "acc_read", "acc_read16")}
+        res["two_waves_per_simd_variants_TFLOP/s"] = {
+            v: rate(2, v) for v in ("plain", "lds_read", "valu2", "acc_read", "acc_read16")}
     del out
     return res
 

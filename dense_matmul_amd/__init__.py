@@ -18,7 +18,7 @@ Functions (names as in the C ABI):
     gemm_a8w8_blockscale(a, b_shuf, a_scale, b_scale, out=None) -> bf16 [M,N]
     gemm_a8w8_mxfp8(a, b_shuf, a_scale, b_scale, out=None)      -> bf16 [M,N]
     gemm_bf16(a, b, out=None, tile="auto")                       -> bf16 [M,N]
-    mfma_ceiling_fp8(frag, iters, waves_per_simd, out=None)      -> (out, FLOPs of the launch)
+    mfma_ceiling_fp8(frag, iters, waves_per_simd, variant=0, out=None) -> (out, FLOPs of the launch)
         (calibration: back-to-back fp8 matrix ops, not a step of the GEMM)
 
 Argument errors (status DMM_EINVAL) raise ValueError; everything else raises
@@ -68,7 +68,8 @@ def lib():
                                               ctypes.c_uint32, I64, P, P]
         L.gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
         L.gemm_bf16_tile.argtypes = [P, P, P, I64, I64, I64, ctypes.c_int, P]
-        L.dmm_mfma_ceiling_fp8.argtypes = [P, I64, P, I64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int), P]
+        L.dmm_mfma_ceiling_fp8.argtypes = [P, I64, P, I64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_int), P]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -297,9 +298,15 @@ def gemm_bf16(a, b, out=None, tile="auto"):
 
 
 # ------------------------------------------------------------ calibration
-def mfma_ceiling_fp8(frag, iters, waves_per_simd=1, out=None):
+MFMA_CEILING_VARIANTS = {"plain": 0, "scaled": 1, "lds_read": 2, "valu2": 3, "acc_read": 4, "acc_read16": 5}
+
+
+def mfma_ceiling_fp8(frag, iters, waves_per_simd=1, variant="plain", out=None):
     """One launch of the matrix-core issue-ceiling kernel (dmm_mfma_ceiling_fp8)
-    on e4m3 codes frag (at least 2 MiB, any shape); returns (out, FLOPs)."""
+    on e4m3 codes frag (at least 2 MiB, any shape); variant is a name of
+    MFMA_CEILING_VARIANTS; returns (out, FLOPs)."""
+    if variant not in MFMA_CEILING_VARIANTS:
+        raise ValueError(f"variant must be one of {sorted(MFMA_CEILING_VARIANTS)} (got {variant!r})")
     _require(frag, "frag", None, None)
     fb = _codes(frag, "frag")
     if out is None:
@@ -307,6 +314,6 @@ def mfma_ceiling_fp8(frag, iters, waves_per_simd=1, out=None):
     _require(out, "out", torch.float32, 1)
     wg = ctypes.c_int(0)
     _check(lib().dmm_mfma_ceiling_fp8(_ptr(fb), fb.numel(), _ptr(out), out.numel(), int(iters), int(waves_per_simd),
-                                      ctypes.byref(wg), _stream()))
+                                      MFMA_CEILING_VARIANTS[variant], ctypes.byref(wg), _stream()))
     flops = 2.0 * 16 * 16 * 128 * 16 * int(iters) * wg.value * 4 * int(waves_per_simd)
     return out, flops

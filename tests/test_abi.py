@@ -132,14 +132,16 @@ def test_quantiser_and_preshuffle_rules(L):
     assert L.gemm_bf16(ALIGNED, ALIGNED, ALIGNED, 4, 16, 96, None) == 1
 
 
-@pytest.mark.parametrize("frag,frag_bytes,out_len,iters,wps,why", [
-    (ALIGNED, 1 << 20, 16, 1, 1, "frag must hold"), (ALIGNED, 1 << 21, 0, 1, 1, "out_len"),
-    (ALIGNED, 1 << 21, 16, 0, 1, "iters"), (ALIGNED, 1 << 21, 16, (1 << 20) + 1, 1, "iters"),
-    (ALIGNED, 1 << 21, 16, 1, 3, "waves_per_simd"), (ALIGNED, 1 << 21, 16, 1, 0, "waves_per_simd"),
-    (ctypes.c_void_p((1 << 20) + 4), 1 << 21, 16, 1, 1, "frag: pointer"), (None, 1 << 21, 16, 1, 1, "frag: pointer"),
+@pytest.mark.parametrize("frag,frag_bytes,out_len,iters,wps,var,why", [
+    (ALIGNED, 1 << 20, 16, 1, 1, 0, "frag must hold"), (ALIGNED, 1 << 21, 0, 1, 1, 0, "out_len"),
+    (ALIGNED, 1 << 21, 16, 0, 1, 0, "iters"), (ALIGNED, 1 << 21, 16, (1 << 20) + 1, 1, 0, "iters"),
+    (ALIGNED, 1 << 21, 16, 1, 3, 0, "waves_per_simd"), (ALIGNED, 1 << 21, 16, 1, 0, 0, "waves_per_simd"),
+    (ALIGNED, 1 << 21, 16, 1, 1, 6, "variant"), (ALIGNED, 1 << 21, 16, 1, 1, -1, "variant"),
+    (ctypes.c_void_p((1 << 20) + 4), 1 << 21, 16, 1, 1, 0, "frag: pointer"),
+    (None, 1 << 21, 16, 1, 1, 0, "frag: pointer"),
 ])
-def test_mfma_ceiling_rules(L, frag, frag_bytes, out_len, iters, wps, why):
+def test_mfma_ceiling_rules(L, frag, frag_bytes, out_len, iters, wps, var, why):
     """The calibration entry point checks its arguments before any HIP call."""
-    st = L.dmm_mfma_ceiling_fp8(frag, frag_bytes, ALIGNED, out_len, iters, wps, None, None)
+    st = L.dmm_mfma_ceiling_fp8(frag, frag_bytes, ALIGNED, out_len, iters, wps, var, None, None)
     assert st == 1, st
     assert why in L.dmm_last_error().decode()

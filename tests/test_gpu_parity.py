@@ -358,20 +358,24 @@ def test_many_tiles_per_workgroup_every_k_phase(dmm, mode, k):
     assert mism.size == 0, f"{mode} {m}x{n}x{k}: {len(mism)} mismatches, first at {mism[:4].tolist()}"
 
 
+@pytest.mark.parametrize("variant", ["plain", "scaled", "lds_read", "valu2", "acc_read", "acc_read16"])
 @pytest.mark.parametrize("wps", [1, 2])
-def test_mfma_ceiling_calibration(dmm, wps):
+def test_mfma_ceiling_calibration(dmm, wps, variant):
     """The calibration kernel runs on every compute unit, reports the FLOPs of
     its launch, and is deterministic (its accumulators are finite and equal
-    across two launches)."""
-    announce("mfma ceiling calibration, waves per SIMD", wps)
+    across two launches, and the same for every variant: the extra
+    instructions never feed the matrix ops)."""
+    announce("mfma ceiling calibration, waves per SIMD", wps, "variant", variant)
     g = torch.Generator().manual_seed(5)
     frag = torch.randint(0, 0x7F, (1 << 21,), dtype=torch.uint8, generator=g).to(DEV)  # finite e4m3 codes
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    out1, flops = dmm.mfma_ceiling_fp8(frag, 3, wps)
-    out2, _ = dmm.mfma_ceiling_fp8(frag, 3, wps)
+    out1, flops = dmm.mfma_ceiling_fp8(frag, 3, wps, variant)
+    out2, _ = dmm.mfma_ceiling_fp8(frag, 3, wps, variant)
+    ref, _ = dmm.mfma_ceiling_fp8(frag, 3, wps, "plain")
     torch.cuda.synchronize()
     assert flops == 2.0 * 16 * 16 * 128 * 16 * 3 * cus * 4 * wps
     used = cus * 256 * wps
     assert torch.isfinite(out1[:used]).all()
     assert torch.equal(out1[:used], out2[:used])
+    assert torch.equal(out1[:used], ref[:used])
     assert (out1[:used] != 0).any()

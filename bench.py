@@ -302,7 +302,7 @@ def extra_shapes(dmm, torch, args):
         ("ptpc_gathered_32768x3648x7168", "ptpc", 32768, 3648, 7168, tuple(range(500, 508)), 511),
         ("ptpc_2048x1168x1792", "ptpc", 2048, 1168, 1792, 61, 62),
     ]:
-        qa, bs, sa, sb = headline_operands(dmm, torch, m, n, k, sa_seed, sb_seed, mode)
+        qa, bs, sa, sb, qb = headline_operands(dmm, torch, m, n, k, sa_seed, sb_seed, mode, keep_b=True)
         out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
         fn = {"ptpc": dmm.gemm_a8w8_ptpc, "blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
         ms = timed(lambda: fn(qa, bs, sa, sb, out=out), steps, warm)
@@ -310,7 +310,10 @@ def extra_shapes(dmm, torch, args):
         hbm = (m * k + n * k + 2 * m * n) / (ms * 1e-3) / 1e9
         res[name] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1), "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 1),
                      "alg_GB/s": round(hbm, 0)}
-        del qa, bs, sa, sb, out
+        if mode == "ptpc":  # the vendor library has the per-row / per-column form only
+            v = vendor_baseline(torch, qa, qb, sa, sb, out, steps, warm)
+            res[name]["vendor_us"] = v.get("us")
+        del qa, bs, sa, sb, qb, out
         torch.cuda.empty_cache()
     from dense_matmul_amd import inputs
 

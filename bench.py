@@ -255,9 +255,10 @@ def mfma_ceiling(dmm, torch, frag, all_variants=False, iters=1200, launches=100)
            "one_wave_per_simd_TFLOP/s": rate(1, "plain"), "two_waves_per_simd_TFLOP/s": rate(2, "plain")}
     if all_variants:
         res["one_wave_per_simd_variants_TFLOP/s"] = {
-            v: rate(1, v) for v in ("plain", "scaled", "lds_read", "valu2", "acc_read", "acc_read16")}
+            v: rate(1, v) for v in ("plain", "scaled", "lds_read", "valu2", "acc_read", "acc_read16", "vmem_load",
+                                    "lds_dma")}
         res["two_waves_per_simd_variants_TFLOP/s"] = {
-            v: rate(2, v) for v in ("plain", "lds_read", "valu2", "acc_read", "acc_read16")}
+            v: rate(2, v) for v in ("plain", "lds_read", "valu2", "acc_read", "acc_read16", "vmem_load", "lds_dma")}
     del out
     return res
 

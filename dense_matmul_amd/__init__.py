@@ -298,7 +298,8 @@ def gemm_bf16(a, b, out=None, tile="auto"):
 
 
 # ------------------------------------------------------------ calibration
-MFMA_CEILING_VARIANTS = {"plain": 0, "scaled": 1, "lds_read": 2, "valu2": 3, "acc_read": 4, "acc_read16": 5}
+MFMA_CEILING_VARIANTS = {"plain": 0, "scaled": 1, "lds_read": 2, "valu2": 3, "acc_read": 4, "acc_read16": 5,
+                         "vmem_load": 6, "lds_dma": 7}
 
 
 def mfma_ceiling_fp8(frag, iters, waves_per_simd=1, variant="plain", out=None):

@@ -264,7 +264,7 @@ dmm_status dmm_mfma_ceiling_fp8(const uint8_t* frag, int64_t frag_bytes, float* 
     REQUIRE(out_len >= 1 && out_len < kLimit, "out_len must be in [1, 2^31)");
     REQUIRE(iters >= 1 && iters <= (1 << 20), "iters must be in [1, 2^20] (got %d)", iters);
     REQUIRE(waves_per_simd == 1 || waves_per_simd == 2, "waves_per_simd must be 1 or 2 (got %d)", waves_per_simd);
-    REQUIRE(variant >= 0 && variant <= 5, "variant must be in [0, 5] (got %d)", variant);
+    REQUIRE(variant >= 0 && variant <= 7, "variant must be in [0, 7] (got %d)", variant);
     dmm_status s = check_device();
     if (s != DMM_OK) return s;
     int grid = 0;

@@ -198,13 +198,16 @@ dmm_status gemm_bf16_tile(const uint16_t* a, const uint16_t* b, uint16_t* c, int
  *   3  variant 0 + two v_mul_f32 per op
  *   4  variant 0 + one v_accvgpr_read_b32 per op
  *   5  variant 0 + sixteen v_accvgpr_read_b32 after every sixteenth op
+ *   6  variant 0 + one 16-byte-per-lane buffer load into VGPRs per four ops
+ *   7  variant 0 + one 16-byte-per-lane buffer load into LDS per four ops
+ *      (6 and 7 read frag's first 2 MiB, 1 KiB per instruction)
  * One launch does
  *     2 * 16 * 16 * 128 * 16 * iters * (*workgroups) * 4 * waves_per_simd
  * FLOPs; *workgroups (host pointer, may be NULL) receives the grid size (the
  * device's compute-unit count).  frag: device, at least 2 MiB of e4m3 codes
  * (the operand bytes change the power the part draws, so pass real codes);
  * out: device fp32 [out_len].  Rules: 1 <= iters <= 2^20; waves_per_simd 1
- * or 2; 0 <= variant <= 5; frag_bytes >= 2 MiB; 1 <= out_len < 2^31. */
+ * or 2; 0 <= variant <= 7; frag_bytes >= 2 MiB; 1 <= out_len < 2^31. */
 dmm_status dmm_mfma_ceiling_fp8(const uint8_t* frag, int64_t frag_bytes, float* out, int64_t out_len, int iters,
                                 int waves_per_simd, int variant, int* workgroups, void* stream);
 

@@ -136,7 +136,7 @@ def test_quantiser_and_preshuffle_rules(L):
     (ALIGNED, 1 << 20, 16, 1, 1, 0, "frag must hold"), (ALIGNED, 1 << 21, 0, 1, 1, 0, "out_len"),
     (ALIGNED, 1 << 21, 16, 0, 1, 0, "iters"), (ALIGNED, 1 << 21, 16, (1 << 20) + 1, 1, 0, "iters"),
     (ALIGNED, 1 << 21, 16, 1, 3, 0, "waves_per_simd"), (ALIGNED, 1 << 21, 16, 1, 0, 0, "waves_per_simd"),
-    (ALIGNED, 1 << 21, 16, 1, 1, 6, "variant"), (ALIGNED, 1 << 21, 16, 1, 1, -1, "variant"),
+    (ALIGNED, 1 << 21, 16, 1, 1, 8, "variant"), (ALIGNED, 1 << 21, 16, 1, 1, -1, "variant"),
     (ctypes.c_void_p((1 << 20) + 4), 1 << 21, 16, 1, 1, 0, "frag: pointer"),
     (None, 1 << 21, 16, 1, 1, 0, "frag: pointer"),
 ])

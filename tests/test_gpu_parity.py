@@ -358,7 +358,8 @@ def test_many_tiles_per_workgroup_every_k_phase(dmm, mode, k):
     assert mism.size == 0, f"{mode} {m}x{n}x{k}: {len(mism)} mismatches, first at {mism[:4].tolist()}"
 
 
-@pytest.mark.parametrize("variant", ["plain", "scaled", "lds_read", "valu2", "acc_read", "acc_read16"])
+@pytest.mark.parametrize("variant", ["plain", "scaled", "lds_read", "valu2", "acc_read", "acc_read16", "vmem_load",
+                                     "lds_dma"])
 @pytest.mark.parametrize("wps", [1, 2])
 def test_mfma_ceiling_calibration(dmm, wps, variant):
     """The calibration kernel runs on every compute unit, reports the FLOPs of

@@ -40,7 +40,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=100)
+    # the part needs ~50-60 ms of load to climb from its idle clock to the
+    # steady one: 500 headline launches (~155 ms) warm it up fully
+    p.add_argument("--warmup", type=int, default=500)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--extra", action="store_true", help="also time the other modes and shapes")
     p.add_argument("--cpu-rows", type=int, default=32768,
@@ -54,14 +56,21 @@ def parse():
     return p.parse_args()
 
 
-def timed(fn, steps, warmup):
+def timed(fn, steps, warmup, min_warm_s=0.0):
     """Average ms per call over ``steps`` back-to-back launches on the current
-    stream (HIP events), after ``warmup`` launches; synchronised both sides."""
+    stream (HIP events), after ``warmup`` launches -- and, with min_warm_s,
+    after at least that much wall time of launches, so that the part has left
+    its idle clock; synchronised both sides."""
     import torch
 
+    t0 = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_warm_s:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(steps):
@@ -263,7 +272,7 @@ def mfma_ceiling(dmm, torch, frag, all_variants=False, iters=1200, launches=100)
     return res
 
 
-def vendor_baseline(torch, qa, qb, sa, sb, ours, steps, warmup):
+def vendor_baseline(torch, qa, qb, sa, sb, ours, steps, warmup, min_warm_s=0.0):
     """The vendor library on the same codes and scales: torch._scaled_mm
     (hipBLASLt on ROCm) with per-row A and per-column B fp32 scales, bf16
     out, timed like the headline; its output is compared with this
@@ -276,7 +285,7 @@ def vendor_baseline(torch, qa, qb, sa, sb, ours, steps, warmup):
         def f():
             return torch._scaled_mm(a8, b8.t(), scale_a=sa2, scale_b=sb2, out_dtype=torch.bfloat16)
 
-        ms = timed(f, steps, warmup)
+        ms = timed(f, steps, warmup, min_warm_s)
         c = f()
         m, k = qa.shape
         n = qb.shape[0]
@@ -292,7 +301,8 @@ def extra_shapes(dmm, torch, args):
     """Secondary lines: the other scaling modes, the tail-only and gathered
     shapes, and the bf16 GEMM (fewer steps each)."""
     res = {}
-    steps, warm = max(5, args.steps // 4), 20
+    # short shapes: at least 150 ms of launches before timing (the clock ramp)
+    steps, warm, warm_s = max(5, args.steps // 4), 20, 0.15
     for name, mode, m, n, k, sa_seed, sb_seed in [
         ("blockscale_16384x7168x2048", "blockscale", 16384, 7168, 2048, 41, 42),
         ("mxfp8_32768x7168x1792", "mxfp8", 32768, 7168, 1792, 31, 32),
@@ -306,13 +316,13 @@ def extra_shapes(dmm, torch, args):
         qa, bs, sa, sb, qb = headline_operands(dmm, torch, m, n, k, sa_seed, sb_seed, mode, keep_b=True)
         out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
         fn = {"ptpc": dmm.gemm_a8w8_ptpc, "blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
-        ms = timed(lambda: fn(qa, bs, sa, sb, out=out), steps, warm)
+        ms = timed(lambda: fn(qa, bs, sa, sb, out=out), steps, warm, warm_s)
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         hbm = (m * k + n * k + 2 * m * n) / (ms * 1e-3) / 1e9
         res[name] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1), "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 1),
                      "alg_GB/s": round(hbm, 0)}
         if mode == "ptpc":  # the vendor library has the per-row / per-column form only
-            v = vendor_baseline(torch, qa, qb, sa, sb, out, steps, warm)
+            v = vendor_baseline(torch, qa, qb, sa, sb, out, steps, warm, warm_s)
             res[name]["vendor_us"] = v.get("us")
         del qa, bs, sa, sb, qb, out
         torch.cuda.empty_cache()
@@ -323,7 +333,7 @@ def extra_shapes(dmm, torch, args):
     a = torch.from_numpy(a32).to(torch.bfloat16).to("cuda:0")
     b = torch.from_numpy(b_kn.T.copy()).to(torch.bfloat16).to("cuda:0")
     out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
-    ms = timed(lambda: dmm.gemm_bf16(a, b, out=out), 200, 20)
+    ms = timed(lambda: dmm.gemm_bf16(a, b, out=out), 200, 20, warm_s)
     tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
     res["bf16_4096x1024x896"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
                                  "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}

@@ -12,6 +12,8 @@ without any oracle:
 - a one-hot B (row n holds 1.0 at column p(n), p injective):
   C[:, n] = bf16(dec(A[:, p(n)]) sa(:, p(n)));
 - A = 0: C = 0;
+- A made only of subnormal E4M3 codes, identity B: the same exact closed
+  form, so the matrix core keeps fp8 subnormals;
 - doubling every A scale (the E8M0 byte + 1 for mxfp8) doubles C exactly:
   a power-of-two factor commutes with every fp32 and bf16 rounding at these
   magnitudes;
@@ -21,7 +23,9 @@ without any oracle:
 
 In each closed form the sum has a single non-zero term (or none), so it is
 exact in any order; decoding uses torch's CPU float8_e4m3fn cast and
-rounding torch's CPU bfloat16 cast (library routines).  The shapes include
+rounding torch's CPU bfloat16 cast (library routines).  Zeros compare by
+value: where the selected code is -0 the other terms are zeros of either
+sign, and an fp32 sum of mixed-sign zeros is +0.  The shapes include
 a partial last row tile (M = 300), a partial last 256-column tile and K
 with a main loop and a peeled tail.
 """
@@ -60,6 +64,11 @@ def dec(codes):
 def bf16_bits_of(f32):
     """fp32 -> bf16 bit patterns, round to nearest even (torch's CPU cast)."""
     return torch.from_numpy(np.ascontiguousarray(f32, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def zero_as_plus(bits):
+    """bf16 bits with -0 read as +0 (zeros compare by value)."""
+    return np.where(bits == 0x8000, np.uint16(0), bits)
 
 
 def run(dmm, mode, qa, qb, sa, sb):
@@ -104,7 +113,7 @@ def unit_b_scales(mode, n, k):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("m,k", [(300, 384), (64, 256), (17, 128)])
+@pytest.mark.parametrize("m,k", [(300, 384), (64, 256), (17, 128), (1, 128)])
 def test_identity_b(dmm, mode, m, k):
     """B = I (N = K): C[m, n] = bf16(dec(A[m, n]) * sa(m, n)), bitwise."""
     announce("identity B", mode, m, k)
@@ -114,23 +123,42 @@ def test_identity_b(dmm, mode, m, k):
     qb[np.arange(k), np.arange(k)] = ONE
     got = run(dmm, mode, qa, qb, sa, unit_b_scales(mode, k, k))
     want = bf16_bits_of(dec(qa) * sa_full)
-    bad = np.argwhere(got != want)
+    bad = np.argwhere(zero_as_plus(got) != zero_as_plus(want))
     assert bad.size == 0, f"{mode} {m}x{k}: {len(bad)} mismatches, first at {bad[:4].tolist()}"
 
 
 @pytest.mark.parametrize("mode", MODES)
-def test_one_hot_b_selects_columns(dmm, mode):
+@pytest.mark.parametrize("m,n,k", [(300, 272, 640), (1, 16, 128), (513, 1168, 1792)])
+def test_one_hot_b_selects_columns(dmm, mode, m, n, k):
     """Row n of B holds 1.0 at column p(n): C[:, n] = bf16(dec(A[:, p(n)]) sa(:, p(n)))."""
-    m, n, k = 300, 272, 640
     announce("one-hot B", mode, m, n, k)
-    qa = a_codes(m, k, 910)
-    sa, sa_full = a_scales(mode, m, k, 911)
-    p = np.random.default_rng(912).permutation(k)[:n]
+    qa = a_codes(m, k, 910 + m)
+    sa, sa_full = a_scales(mode, m, k, 911 + n)
+    p = np.random.default_rng(912 + k).permutation(k)[:n]
     qb = np.zeros((n, k), np.uint8)
     qb[np.arange(n), p] = ONE
     got = run(dmm, mode, qa, qb, sa, unit_b_scales(mode, n, k))
     want = bf16_bits_of(dec(qa)[:, p] * sa_full[:, p])
-    bad = np.argwhere(got != want)
+    bad = np.argwhere(zero_as_plus(got) != zero_as_plus(want))
+    assert bad.size == 0, f"{mode}: {len(bad)} mismatches, first at {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_subnormal_codes_are_kept(dmm, mode):
+    """A made only of the fourteen subnormal E4M3 codes (+-f 2^-9, f = 1..7),
+    identity B: every output is bf16(dec(A) sa) exactly, so the matrix core
+    neither flushes nor rescales fp8 subnormal inputs."""
+    m, k = 300, 384
+    announce("subnormal A", mode, m, k)
+    subs = np.array([f | s for f in range(1, 8) for s in (0, 0x80)], np.uint8)
+    qa = inputs.choice((m, k), subs, 950)
+    sa, sa_full = a_scales(mode, m, k, 951)
+    qb = np.zeros((k, k), np.uint8)
+    qb[np.arange(k), np.arange(k)] = ONE
+    got = run(dmm, mode, qa, qb, sa, unit_b_scales(mode, k, k))
+    want = bf16_bits_of(dec(qa) * sa_full)
+    assert np.all(dec(qa) != 0)
+    bad = np.argwhere(zero_as_plus(got) != zero_as_plus(want))
     assert bad.size == 0, f"{mode}: {len(bad)} mismatches, first at {bad[:4].tolist()}"
 
 

@@ -208,3 +208,23 @@ def test_modes_agree_under_unit_scales(dmm):
     mx = run(dmm, "mxfp8", qa, qb, np.full((k // 32, m), 127, np.uint8), np.full((k // 32, n), 127, np.uint8))
     assert np.array_equal(ptpc_w, ptpc_n), f"ptpc tiles differ at {np.argwhere(ptpc_w != ptpc_n)[:4].tolist()}"
     assert np.array_equal(ptpc_w, mx), f"ptpc and mxfp8 differ at {np.argwhere(ptpc_w != mx)[:4].tolist()}"
+
+
+@pytest.mark.parametrize("tile", ["auto", "128x128", "64x64"])
+@pytest.mark.parametrize("m,n,k", [(300, 272, 640), (1, 16, 64), (4096, 896, 1024)])
+def test_bf16_one_hot_b_selects_columns(dmm, tile, m, n, k):
+    """bf16 GEMM (DeepGEMM PR 453, "Fix SM120 BF16 GEMM shared-memory reuse
+    ordering", Reproduction and validation: the [4096, 1024] x [1024, 896]
+    shape among others): row n of B holds 1.0 at column p(n), so
+    C[:, n] = A[:, p(n)] bit for bit (zeros by value)."""
+    announce("bf16 one-hot B", tile, m, n, k)
+    a = torch.from_numpy(inputs.normal((m, k), 960 + m)).to(torch.bfloat16)
+    p = np.random.default_rng(961 + k).permutation(k)[:n]
+    b = torch.zeros((n, k), dtype=torch.bfloat16)
+    b[torch.arange(n), torch.from_numpy(p)] = 1.0
+    c = dmm.gemm_bf16(a.to(DEV), b.to(DEV), tile=tile)
+    torch.cuda.synchronize()
+    got = c.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = a.view(torch.int16).numpy().view(np.uint16)[:, p]
+    bad = np.argwhere(zero_as_plus(got) != zero_as_plus(want))
+    assert bad.size == 0, f"bf16 {tile} {m}x{n}x{k}: {len(bad)} mismatches, first at {bad[:4].tolist()}"

@@ -59,6 +59,36 @@ __device__ __forceinline__ v4f load4(const uint16_t* xr, int c) {
                  __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xFFFF0000u)};
 }
 
+// Rows of up to 256 NC columns stay in registers (NC 16-byte chunks per
+// lane), so each value is read from HBM once and every load of the row is
+// in flight before the first wait; longer rows take the two-pass kernel
+// below, whose second pass re-reads the row from L2.
+template <typename In, int NC>
+__global__ void __launch_bounds__(256) quantize_rows_reg_kernel(const In* __restrict__ x, uint8_t* __restrict__ q,
+                                                                float* __restrict__ scale, int rows, int cols) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const In* xr = x + (size_t)row * cols;
+    uint32_t* qr = (uint32_t*)(q + (size_t)row * cols);
+    const int n4 = cols / 4;
+    v4f v[NC];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = lane + 64 * j;
+        v[j] = c < n4 ? load4(xr, c) : (v4f){0.f, 0.f, 0.f, 0.f};
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
+    }
+    const float s = amax_to_scale(wave_max(amax));
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = lane + 64 * j;
+        if (c < n4) qr[c] = pack4(v[j], s);
+    }
+    if (lane == 0) scale[row] = s;
+}
+
 template <typename In>
 __global__ void __launch_bounds__(256) quantize_rows_kernel(const In* __restrict__ x, uint8_t* __restrict__ q,
                                                             float* __restrict__ scale, int rows, int cols) {
@@ -190,14 +220,26 @@ __global__ void __launch_bounds__(256) preshuffle_b_kernel(const uint8_t* __rest
 }
 
 // -------------------------------------------------------------- launch
-hipError_t launch_quantize_rows(const float* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st) {
-    hipLaunchKernelGGL(quantize_rows_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, st, x, q, s, rows, cols);
+// Per-token quantisation: the register-resident kernel for rows of up to
+// 7168 columns (the chunk count rounded up to 8, 16 or 28 per lane), the
+// two-pass kernel beyond.
+template <typename In>
+static hipError_t launch_rows(const In* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st) {
+    const dim3 g((rows + 3) / 4), b(256);
+    const int chunks = (cols / 4 + 63) / 64;  // 16-byte chunks per lane
+    if (chunks <= 8) hipLaunchKernelGGL((quantize_rows_reg_kernel<In, 8>), g, b, 0, st, x, q, s, rows, cols);
+    else if (chunks <= 16) hipLaunchKernelGGL((quantize_rows_reg_kernel<In, 16>), g, b, 0, st, x, q, s, rows, cols);
+    else if (chunks <= 28) hipLaunchKernelGGL((quantize_rows_reg_kernel<In, 28>), g, b, 0, st, x, q, s, rows, cols);
+    else hipLaunchKernelGGL(quantize_rows_kernel<In>, g, b, 0, st, x, q, s, rows, cols);
     return hipGetLastError();
 }
 
+hipError_t launch_quantize_rows(const float* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st) {
+    return launch_rows<float>(x, q, s, rows, cols, st);
+}
+
 hipError_t launch_quantize_rows_bf16(const uint16_t* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st) {
-    hipLaunchKernelGGL(quantize_rows_kernel<uint16_t>, dim3((rows + 3) / 4), dim3(256), 0, st, x, q, s, rows, cols);
-    return hipGetLastError();
+    return launch_rows<uint16_t>(x, q, s, rows, cols, st);
 }
 
 hipError_t launch_quantize_blockscale_a(const float* x, uint8_t* q, float* s, int m, int k, hipStream_t st) {

@@ -62,7 +62,8 @@ def to_dev(a):
 
 
 # ------------------------------------------------------------ quantisers
-@pytest.mark.parametrize("rows,cols,seed", [(512, 256, 1), (300, 1792, 2), (7, 7168, 3), (64, 16, 4)])
+@pytest.mark.parametrize("rows,cols,seed", [(512, 256, 1), (300, 1792, 2), (7, 7168, 3), (64, 16, 4),
+                                           (33, 4096, 14), (3, 2064, 16), (5, 9216, 15)])
 def test_quantize_per_token_bitexact(dmm, rows, cols, seed):
     announce("quantize_per_token", rows, cols, seed)
     x = inputs.normal((rows, cols), seed)
@@ -77,7 +78,8 @@ def test_quantize_per_token_bitexact(dmm, rows, cols, seed):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
 
 
-@pytest.mark.parametrize("rows,cols,seed", [(512, 256, 21), (300, 1792, 22), (5, 7168, 23)])
+@pytest.mark.parametrize("rows,cols,seed", [(512, 256, 21), (300, 1792, 22), (5, 7168, 23), (33, 4096, 24),
+                                           (5, 9216, 25)])
 def test_quantize_per_token_bf16_input_bitexact(dmm, rows, cols, seed):
     """bf16 activations: the oracle quantises the same values widened to fp32
     (bf16 -> fp32 is exact), so codes and scales must match bitwise."""

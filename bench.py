@@ -328,6 +328,18 @@ def extra_shapes(dmm, torch, args):
         torch.cuda.empty_cache()
     from dense_matmul_amd import inputs
 
+    # the quantiser of the headline's activations (not in the GEMM's time):
+    # algorithmic bytes 4 M K in + M K codes + 4 M scales
+    m, k = 32768, 1792
+    x = torch.from_numpy(inputs.operand_a(m, k, 31)).to("cuda:0")
+    q = torch.empty((m, k), dtype=torch.uint8, device="cuda:0")
+    s = torch.empty((m,), dtype=torch.float32, device="cuda:0")
+    ms = timed(lambda: dmm.quantize_per_token(x, q, s), 100, 20, warm_s)
+    gbs = (5 * m * k + 4 * m) / (ms * 1e-3) / 1e9
+    res["quantize_per_token_32768x1792_fp32"] = {"us": round(ms * 1e3, 1), "alg_GB/s": round(gbs),
+                                                 "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+    del x, q, s
+
     m, k, n = 4096, 1024, 896
     a32, b_kn = inputs.bf16_operands(m, k, n, 233)
     a = torch.from_numpy(a32).to(torch.bfloat16).to("cuda:0")

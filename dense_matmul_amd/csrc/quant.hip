@@ -133,27 +133,34 @@ __global__ void __launch_bounds__(256) quantize_blockscale_a_kernel(const float*
 }
 
 // ------------------------------------------------------- blockscale B
-// One workgroup per 128 x 128 block (rows past n are skipped).
+// One workgroup per 128 x 128 block (rows past n are skipped).  The block
+// stays in registers (16 rows of 16 bytes per thread): it is read from HBM
+// once, with all of a thread's loads in flight before the first wait.
 __global__ void __launch_bounds__(256) quantize_blockscale_b_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
                                                                     float* __restrict__ scale, int n, int k) {
     __shared__ float red[4];
     const int kb = blockIdx.x, nb = blockIdx.y, kblocks = k / 128;
     const int t = threadIdx.x;
     const int col4 = t & 31;  // float4 column within the block
-    const int r0 = t >> 5;    // 8 row lanes
+    const int r0 = t >> 5;    // 8 row lanes: thread rows r0, r0 + 8, ..., r0 + 120
     const int rows = min(128, n - nb * 128);
+    v4f v[16];
     float amax = 0.0f;
-    for (int r = r0; r < rows; r += 8) {
-        const v4f v = *(const v4f*)(x + (size_t)(nb * 128 + r) * k + kb * 128 + col4 * 4);
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int r = r0 + 8 * j;
+        v[j] = r < rows ? *(const v4f*)(x + (size_t)(nb * 128 + r) * k + kb * 128 + col4 * 4)
+                        : (v4f){0.f, 0.f, 0.f, 0.f};
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
     }
     amax = wave_max(amax);
     if ((t & 63) == 0) red[t >> 6] = amax;
     __syncthreads();
     const float s = amax_to_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
-    for (int r = r0; r < rows; r += 8) {
-        const size_t off = (size_t)(nb * 128 + r) * k + kb * 128 + col4 * 4;
-        *(uint32_t*)(q + off) = pack4(*(const v4f*)(x + off), s);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int r = r0 + 8 * j;
+        if (r < rows) *(uint32_t*)(q + (size_t)(nb * 128 + r) * k + kb * 128 + col4 * 4) = pack4(v[j], s);
     }
     if (t == 0) scale[(size_t)nb * kblocks + kb] = s;
 }

@@ -89,6 +89,41 @@ __global__ void __launch_bounds__(256) quantize_rows_reg_kernel(const In* __rest
     if (lane == 0) scale[row] = s;
 }
 
+// Rows of 2049 .. 7168 columns: two waves per row, each holding every other
+// 64-chunk slice of it (NC chunks per lane), their maxima combined through
+// LDS; half the registers of one wave per row, so twice the rows in flight.
+template <typename In, int NC>
+__global__ void __launch_bounds__(256) quantize_rows_pair_kernel(const In* __restrict__ x, uint8_t* __restrict__ q,
+                                                                 float* __restrict__ scale, int rows, int cols) {
+    __shared__ float red[4];
+    const int w = threadIdx.x >> 6, h = w & 1;
+    const int row = blockIdx.x * 2 + (w >> 1);
+    const int lane = threadIdx.x & 63;
+    const bool live = row < rows;  // both waves of a pair agree; every wave reaches the barrier
+    const In* xr = x + (size_t)(live ? row : 0) * cols;
+    uint32_t* qr = (uint32_t*)(q + (size_t)(live ? row : 0) * cols);
+    const int n4 = cols / 4;
+    v4f v[NC];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = lane + 64 * (2 * j + h);
+        v[j] = live && c < n4 ? load4(xr, c) : (v4f){0.f, 0.f, 0.f, 0.f};
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
+    }
+    amax = wave_max(amax);
+    if (lane == 0) red[w] = amax;
+    __syncthreads();
+    const float s = amax_to_scale(fmaxf(red[w & 2], red[(w & 2) + 1]));
+    if (!live) return;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = lane + 64 * (2 * j + h);
+        if (c < n4) qr[c] = pack4(v[j], s);
+    }
+    if (lane == 0 && h == 0) scale[row] = s;
+}
+
 template <typename In>
 __global__ void __launch_bounds__(256) quantize_rows_kernel(const In* __restrict__ x, uint8_t* __restrict__ q,
                                                             float* __restrict__ scale, int rows, int cols) {
@@ -227,17 +262,17 @@ __global__ void __launch_bounds__(256) preshuffle_b_kernel(const uint8_t* __rest
 }
 
 // -------------------------------------------------------------- launch
-// Per-token quantisation: the register-resident kernel for rows of up to
-// 7168 columns (the chunk count rounded up to 8, 16 or 28 per lane), the
-// two-pass kernel beyond.
+// Per-token quantisation: one wave per row held in registers up to 2048
+// columns, a pair of waves per row up to 7168 (8 or 14 chunks per lane of
+// each), the two-pass kernel beyond.
 template <typename In>
 static hipError_t launch_rows(const In* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st) {
-    const dim3 g((rows + 3) / 4), b(256);
-    const int chunks = (cols / 4 + 63) / 64;  // 16-byte chunks per lane
-    if (chunks <= 8) hipLaunchKernelGGL((quantize_rows_reg_kernel<In, 8>), g, b, 0, st, x, q, s, rows, cols);
-    else if (chunks <= 16) hipLaunchKernelGGL((quantize_rows_reg_kernel<In, 16>), g, b, 0, st, x, q, s, rows, cols);
-    else if (chunks <= 28) hipLaunchKernelGGL((quantize_rows_reg_kernel<In, 28>), g, b, 0, st, x, q, s, rows, cols);
-    else hipLaunchKernelGGL(quantize_rows_kernel<In>, g, b, 0, st, x, q, s, rows, cols);
+    const dim3 g4((rows + 3) / 4), g2((rows + 1) / 2), b(256);
+    const int chunks = (cols / 4 + 63) / 64;  // 64-lane slices of 16-byte chunks in a row
+    if (chunks <= 8) hipLaunchKernelGGL((quantize_rows_reg_kernel<In, 8>), g4, b, 0, st, x, q, s, rows, cols);
+    else if (chunks <= 16) hipLaunchKernelGGL((quantize_rows_pair_kernel<In, 8>), g2, b, 0, st, x, q, s, rows, cols);
+    else if (chunks <= 28) hipLaunchKernelGGL((quantize_rows_pair_kernel<In, 14>), g2, b, 0, st, x, q, s, rows, cols);
+    else hipLaunchKernelGGL(quantize_rows_kernel<In>, g4, b, 0, st, x, q, s, rows, cols);
     return hipGetLastError();
 }
 

@@ -328,17 +328,23 @@ def extra_shapes(dmm, torch, args):
         torch.cuda.empty_cache()
     from dense_matmul_amd import inputs
 
-    # the quantiser of the headline's activations (not in the GEMM's time):
-    # algorithmic bytes 4 M K in + M K codes + 4 M scales
-    m, k = 32768, 1792
-    x = torch.from_numpy(inputs.operand_a(m, k, 31)).to("cuda:0")
-    q = torch.empty((m, k), dtype=torch.uint8, device="cuda:0")
-    s = torch.empty((m,), dtype=torch.float32, device="cuda:0")
-    ms = timed(lambda: dmm.quantize_per_token(x, q, s), 100, 20, warm_s)
-    gbs = (5 * m * k + 4 * m) / (ms * 1e-3) / 1e9
-    res["quantize_per_token_32768x1792_fp32"] = {"us": round(ms * 1e3, 1), "alg_GB/s": round(gbs),
-                                                 "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
-    del x, q, s
+    # the quantisers (run before the GEMM, not in its time), on the configured
+    # shapes' operands: algorithmic bytes = fp32 in + codes + scales
+    for name, fn, rows, cols, extra_bytes in [
+            ("quantize_per_token_32768x1792", dmm.quantize_per_token, 32768, 1792, lambda r, c: 4 * r),
+            ("quantize_per_token_32768x7168", dmm.quantize_per_token, 32768, 7168, lambda r, c: 4 * r),
+            ("quantize_per_token_7168x1792", dmm.quantize_per_token, 7168, 1792, lambda r, c: 4 * r),
+            ("quantize_blockscale_a_16384x2048", dmm.quantize_blockscale_a, 16384, 2048, lambda r, c: 4 * r * c // 128),
+            ("quantize_blockscale_b_7168x2048", dmm.quantize_blockscale_b, 7168, 2048,
+             lambda r, c: 4 * ((r + 127) // 128) * (c // 128)),
+            ("quantize_mxfp8_32768x1792", dmm.quantize_mxfp8, 32768, 1792, lambda r, c: r * c // 32),
+            ("quantize_mxfp8_7168x1792", dmm.quantize_mxfp8, 7168, 1792, lambda r, c: r * c // 32)]:
+        x = torch.from_numpy(inputs.normal((rows, cols), 3)).to("cuda:0")
+        ms = timed(lambda: fn(x), 100, 20, warm_s)
+        gbs = (5 * rows * cols + extra_bytes(rows, cols)) / (ms * 1e-3) / 1e9
+        res[name] = {"us": round(ms * 1e3, 1), "alg_GB/s": round(gbs), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+        del x
+        torch.cuda.empty_cache()
 
     m, k, n = 4096, 1024, 896
     a32, b_kn = inputs.bf16_operands(m, k, n, 233)

@@ -91,6 +91,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // DPP control of row_ror:8 (rotate each 16-lane row by 8 lanes) and the
 // cache-policy bits of a non-temporal store (nt).
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowNewBcast = 0x150;  // + k: lane k of each 16-lane row to the whole row
 constexpr int kStoreStream = 2;
 
 // Gathered operand (order::gathered_coords): band b's rows of A and
@@ -491,10 +492,23 @@ __device__ __forceinline__ void mfma_drain(Ctx<MODE>& x) {
     }
 }
 
+// Within each 16-lane row, lane 4b + j (bank b) receives the value of lane
+// 4 NB + b: four row broadcasts, each written to one bank of four lanes.
+template <int NB>
+__device__ __forceinline__ int row_gather4(int src) {
+    int x = 0;
+    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + 4 * NB + 0, 0xF, 0x1, false);
+    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + 4 * NB + 1, 0xF, 0x2, false);
+    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + 4 * NB + 2, 0xF, 0x4, false);
+    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + 4 * NB + 3, 0xF, 0x8, false);
+    return x;
+}
+
 // Start of a step's mxfp8 scales: realign the 20 loaded A-scale bytes so word
 // q holds the bytes of rows 4q..4q+3, and give lane (i, g) the B-scale byte
 // of column 16 nb + i of each block, which lane (4 nb + i / 4, g) loaded as
-// byte i % 4 of its dword.
+// byte i % 4 of its dword (DPP row broadcasts: vector ops, where an LDS
+// crossbar permute would cost matrix time).
 template <int MODE, int T>
 __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
     if constexpr (MODE == MODE_MXFP8) {
@@ -506,11 +520,11 @@ __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
             x.sxa[T] = (v4i){(int)__builtin_amdgcn_alignbyte(w[1], w[0], sh), (int)__builtin_amdgcn_alignbyte(w[2], w[1], sh),
                              (int)__builtin_amdgcn_alignbyte(w[3], w[2], sh), (int)__builtin_amdgcn_alignbyte(t, w[3], sh)};
         }
-        const int src = 4 * (16 * x.g + (x.i >> 2));
         const int byte = 8 * (x.i & 3);
-#pragma unroll
-        for (int nb = 0; nb < Cfg<MODE>::NBW; ++nb)
-            x.sxb[nb] = (int)((uint32_t)__builtin_amdgcn_ds_bpermute(src + 16 * nb, x.sxb_raw[T]) >> byte);
+        static_for<0, Cfg<MODE>::NBW>([&](auto NBc) {
+            constexpr int nb = decltype(NBc)::value;
+            x.sxb[nb] = (int)((uint32_t)row_gather4<nb>(x.sxb_raw[T]) >> byte);
+        });
     }
 }
 

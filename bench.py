@@ -6,24 +6,41 @@ operands already resident in HBM: A quantised per token on the GPU
 (quantize_per_token), B quantised per output channel and preshuffled once.
 Inputs are seeded synthetic N(0,1) fp32 (A seed 31, B seed 32).
 
-Prints ONE JSON line.  The roofline object reports the GEMM kernel's
-algorithmic FLOPs per launch over its average launch time (HIP events on the
-launch stream) against the fp8 dense MFMA peak; traffic comes from the
-rocprofv3 FETCH_SIZE / WRITE_SIZE summaries under profiles/ when they were
-taken for the current kernel, else null.  Two context objects follow the
-timed run: mfma_ceiling, what the part sustains issuing nothing but the
-GEMM's matrix instruction (one and two waves per SIMD, dmm_mfma_ceiling_fp8),
-and vendor_baseline, the vendor library (hipBLASLt through torch._scaled_mm)
-on the same codes and scales.  cpu_baseline is the CPU oracle
-timed on a bounded row sample of the same workload; its result is also
-compared with the GPU output of the timed run (the acceptance rule of
-oracle.tolerance) and the statistics reported as cpu_baseline.parity.
+Timing protocol (DeepGEMM PR 453, Performance Overhead: the median per-call
+time over 9 batches; mori PR 785, Cost: an idle box, the arms alternating,
+the minimum over 3 passes):
+  * the device and its activity before the run are recorded (an idle check);
+  * warm-up: --warmup launches and at least WARM_S seconds of launches, so the
+    part has left its idle clock whatever the launch count;
+  * `steps` back-to-back launches are captured once in a HIP graph and the
+    graph is replayed 9 times, in 3 passes of 3 replays, each pass followed by
+    the vendor library's 3 batches of `steps` launches (the arms alternate);
+    each batch is bracketed by a device synchronisation and timed with HIP
+    events on the launch stream;
+  * ms_per_step is the median per-call time of the 9 batches (min and max
+    beside it, and the minimum of the 3 per-pass medians);
+  * a secondary cold figure: one launch right after a 1 GiB scrub write, the
+    median of 9.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+Prints ONE JSON line.  The roofline object reports the GEMM kernel's
+algorithmic FLOPs per launch over that per-call time against the fp8 dense
+MFMA peak; traffic comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+under profiles/ when it was taken for the current kernel sources, else null.
+Context objects follow the timed run: mfma_ceiling, what the part sustains
+issuing nothing but the GEMM's matrix instruction (the calibration library
+libdmm_calib.so, not part of libdmm), and vendor_baseline (hipBLASLt through
+torch._scaled_mm) on the same codes and scales.  cpu_baseline is the CPU
+oracle timed on the headline (all rows by default); its result is also
+compared with the GPU output of the timed run under the acceptance rule of
+oracle.tolerance and the statistics are reported as cpu_baseline.parity.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra] [--calibrate]
 """
 import argparse
+import ctypes
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -34,15 +51,19 @@ if ROOT not in sys.path:
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+# the part needs ~50-60 ms of load to climb from its idle clock to the
+# steady one; every timed workload first gets at least this much
+WARM_S = 0.3
+BATCHES, PASSES = 9, 3
+SCRUB_BYTES = 1 << 30
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    # the part needs ~50-60 ms of load to climb from its idle clock to the
-    # steady one: 500 headline launches (~155 ms) warm it up fully
-    p.add_argument("--warmup", type=int, default=500)
+    p.add_argument("--steps", type=int, default=200, help="launches per timed batch (graph)")
+    p.add_argument("--warmup", type=int, default=20,
+                   help="untimed launches before timing (at least WARM_S seconds of launches run regardless)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--extra", action="store_true", help="also time the other modes and shapes")
     p.add_argument("--cpu-rows", type=int, default=32768,
@@ -50,34 +71,147 @@ def parse():
     p.add_argument("--calibrate", action="store_true",
                    help="also time every variant of the matrix-op calibration kernel (what each kind of "
                         "instruction interleaved with the matrix ops costs)")
+    p.add_argument("--no-ceiling", action="store_true", help="skip the calibration-kernel context")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 1 GiB HBM copy kernel 3 times (the reference dispatch for "
                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return p.parse_args()
 
 
-def timed(fn, steps, warmup, min_warm_s=0.0):
-    """Average ms per call over ``steps`` back-to-back launches on the current
-    stream (HIP events), after ``warmup`` launches -- and, with min_warm_s,
-    after at least that much wall time of launches, so that the part has left
-    its idle clock; synchronised both sides."""
+# ------------------------------------------------------------------ timing
+def warm(fn, launches, min_s):
+    """``launches`` launches, then more until at least ``min_s`` seconds of
+    launches have run; synchronised.  Returns the wall seconds spent."""
     import torch
 
     t0 = time.perf_counter()
-    for _ in range(warmup):
+    for _ in range(launches):
         fn()
     torch.cuda.synchronize()
-    while time.perf_counter() - t0 < min_warm_s:
+    while time.perf_counter() - t0 < min_s:
         for _ in range(10):
             fn()
         torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def event_ms(run, calls):
+    """Per-call ms of one batch: ``run()`` issues ``calls`` launches on the
+    current stream, bracketed by device synchronisations and HIP events."""
+    import torch
+
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     start.record()
-    for _ in range(steps):
-        fn()
+    run()
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    return start.elapsed_time(end) / calls
+
+
+def capture(fn, steps):
+    """A HIP graph of ``steps`` back-to-back launches of fn (fn allocates
+    nothing: it writes a caller buffer)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager call on the side stream before capture
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def repeat(fn, n):
+    for _ in range(n):
+        fn()
+
+
+def summary(vals):
+    return {"median": statistics.median(vals), "min": min(vals), "max": max(vals)}
+
+
+def timed_arms(arms, steps, warmup, min_s, batches=BATCHES, passes=PASSES):
+    """Time several arms (name -> fn) with the protocol of the module
+    docstring: each arm warmed, captured as a graph of ``steps`` launches
+    (or, with ``eager`` in the name, issued eagerly), then ``passes`` passes
+    in which each arm in turn runs batches/passes batches.  Returns name ->
+    {median, min, max, pass_min (the least per-pass median), batches_ms,
+    warm_s} in ms per call."""
+    runs, res = {}, {}
+    for name, fn in arms.items():
+        res[name] = {"warm_s": round(warm(fn, warmup, min_s), 3)}
+        if name.endswith("eager"):
+            runs[name] = lambda fn=fn: repeat(fn, steps)
+        else:
+            g = capture(fn, steps)
+            runs[name] = g.replay
+    per = {name: [[] for _ in range(passes)] for name in arms}
+    for p in range(passes):
+        for name in arms:
+            for _ in range(batches // passes):
+                per[name][p].append(event_ms(runs[name], steps))
+    for name in arms:
+        flat = [v for pv in per[name] for v in pv]
+        res[name].update(summary(flat))
+        res[name]["pass_min"] = min(statistics.median(pv) for pv in per[name])
+        res[name]["batches_ms"] = [round(v, 5) for v in flat]
+    return res
+
+
+def cold_ms(fn, reps=BATCHES):
+    """One launch right after a 1 GiB scrub write (the operands leave the
+    caches, the clock stays up): median, min, max per-call ms over reps."""
+    import torch
+
+    scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    vals = []
+    for i in range(reps):
+        scrub.fill_(float(i))
+        vals.append(event_ms(fn, 1))
+    del scrub
+    torch.cuda.empty_cache()
+    return summary(vals)
+
+
+# ----------------------------------------------------------------- context
+def device_record():
+    """The device, the software stack and the GPU's activity before the run
+    (amdsmi when importable)."""
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    rec = {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+           "hbm_GiB": round(p.total_memory / 2**30, 1), "torch": torch.__version__, "hip": torch.version.hip}
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        try:
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+            act = amdsmi.amdsmi_get_gpu_activity(h)
+            rec["idle_check"] = {"gfx_activity_pct": act.get("gfx_activity"),
+                                 "umm_activity_pct": act.get("umc_activity")}
+            try:
+                rec["idle_check"]["processes"] = len(amdsmi.amdsmi_get_gpu_process_list(h))
+            except Exception:
+                pass
+            try:
+                clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+                rec["max_sclk_MHz"] = clk.get("max_clk")
+            except Exception:
+                pass
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception as e:  # no management library: record why
+        rec["idle_check"] = {"error": f"{type(e).__name__}: {str(e)[:100]}"}
+    return rec
 
 
 def headline_operands(dmm, torch, m, n, k, seed_a, seed_b, mode="ptpc", keep_b=False):
@@ -184,12 +318,93 @@ def cpu_baseline(m, n, k, rows_n, gpu_c=None):
             st = tolerance.check(got, ref, "bench headline vs oracle", mode="ptpc", operands=(qa, qb, sa, sb),
                                  rows=rows)
             res["parity"] = {"rel_l2": st["rel_l2"], "elements": st["elements"], "max_err": st["max_err"],
-                             "secondary": st["primary_fail"], "ok": True}
+                             "primary_fail": st["primary_fail"], "secondary_cap": st["secondary_cap"], "ok": True}
         except AssertionError as e:
             res["parity"] = {"ok": False, "error": str(e)[:200]}
     return res
 
 
+# ------------------------------------------------------------ calibration
+CALIB_LIB = os.path.join(ROOT, "dense_matmul_amd", "calib", "libdmm_calib.so")
+CALIB_VARIANTS = {"plain": 0, "scaled": 1, "lds_read": 2, "valu2": 3, "acc_read": 4, "acc_read16": 5,
+                  "vmem_load": 6, "lds_dma": 7, "w32_plain": 8, "w32_lds_read": 9, "w32_vmem_load": 10,
+                  "w32_lds_dma": 11}
+_calib = None
+
+
+def calib_lib():
+    """libdmm_calib.so (the benchmark's matrix-op calibration kernel)."""
+    global _calib
+    if _calib is None:
+        if not os.path.exists(CALIB_LIB):
+            raise ImportError(f"{CALIB_LIB} is not built")
+        L = ctypes.CDLL(CALIB_LIB)
+        P, I64 = ctypes.c_void_p, ctypes.c_int64
+        L.calib_mfma_ceiling_fp8.argtypes = [P, I64, P, I64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.POINTER(ctypes.c_int), P]
+        L.calib_mfma_ceiling_fp8.restype = ctypes.c_int
+        L.calib_last_error.argtypes = []
+        L.calib_last_error.restype = ctypes.c_char_p
+        _calib = L
+    return _calib
+
+
+def mfma_ceiling_fp8(frag, iters, waves_per_simd=1, variant="plain", out=None):
+    """One launch of the calibration kernel on e4m3 codes ``frag`` (at least
+    2 MiB); returns (out, FLOPs of the launch)."""
+    import torch
+
+    fb = frag.view(torch.uint8)
+    if out is None:
+        out = torch.empty(1 << 20, dtype=torch.float32, device=frag.device)
+    wg = ctypes.c_int(0)
+    L = calib_lib()
+    st = L.calib_mfma_ceiling_fp8(ctypes.c_void_p(fb.data_ptr()), fb.numel(), ctypes.c_void_p(out.data_ptr()),
+                                  out.numel(), int(iters), int(waves_per_simd), CALIB_VARIANTS[variant],
+                                  ctypes.byref(wg), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if st != 0:
+        raise (ValueError if st == 1 else RuntimeError)(L.calib_last_error().decode())
+    return out, 2.0 * 16 * 16 * 128 * 16 * int(iters) * wg.value * 4 * int(waves_per_simd)
+
+
+def mfma_ceiling(torch, frag, all_variants=False, iters=1200, launches=50):
+    """What the part sustains issuing nothing but the GEMM's matrix op:
+    back-to-back independent fp8 16x16x128 ops on every SIMD, one and two
+    waves per SIMD, operands taken from the headline's own A codes.  With
+    all_variants, also the mxfp8 form, the 32x32x64 op, and each with one
+    kind of instruction interleaved.  TFLOP/s over HIP events on the launch
+    stream (eager launches, each batch after a short warm-up)."""
+    out = torch.empty(1 << 20, dtype=torch.float32, device="cuda:0")
+
+    def rate(wps, variant):
+        flops = mfma_ceiling_fp8(frag, iters, wps, variant, out=out)[1]
+        fn = lambda: mfma_ceiling_fp8(frag, iters, wps, variant, out=out)
+        warm(fn, 5, 0.02)
+        ms = event_ms(lambda: repeat(fn, launches), launches)
+        return round(flops / (ms * 1e-3) / 1e12, 1)
+
+    warm(lambda: mfma_ceiling_fp8(frag, iters, 1, "plain", out=out), 0, WARM_S)
+    res = {"kind": "back-to-back independent fp8 16x16x128 matrix ops (calibration kernel)",
+           "one_wave_per_simd_TFLOP/s": rate(1, "plain"), "two_waves_per_simd_TFLOP/s": rate(2, "plain")}
+    if all_variants:
+        res["one_wave_per_simd_variants_TFLOP/s"] = {v: rate(1, v) for v in CALIB_VARIANTS}
+        res["two_waves_per_simd_variants_TFLOP/s"] = {v: rate(2, v) for v in CALIB_VARIANTS if v != "scaled"}
+    del out
+    return res
+
+
+def vendor_fn(torch, qa, qb, sa, sb):
+    """torch._scaled_mm (hipBLASLt on ROCm) on the same codes, per-row A and
+    per-column B fp32 scales, bf16 out."""
+    a8, b8 = qa.view(torch.float8_e4m3fn), qb.view(torch.float8_e4m3fn)
+    sa2, sb2 = sa.view(-1, 1), sb.view(1, -1)
+    return lambda: torch._scaled_mm(a8, b8.t(), scale_a=sa2, scale_b=sb2, out_dtype=torch.bfloat16)
+
+
+VENDOR = "hipBLASLt via torch._scaled_mm (per-row A / per-column B fp32 scales)"
+
+
+# -------------------------------------------------------------------- main
 def main():
     args = parse()
     if args.gpus != 1:
@@ -201,18 +416,40 @@ def main():
     import dense_matmul_amd as dmm
 
     dmm.lib()
+    device = device_record()
     if args.copy_calibration:
         copy_calibration(torch)
     m, n, k = 32768, 7168, 1792
+    flops = 2.0 * m * n * k
     qa, bs, sa, sb, qb = headline_operands(dmm, torch, m, n, k, 31, 32, keep_b=True)
     out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
-    ms = timed(lambda: dmm.gemm_a8w8_ptpc(qa, bs, sa, sb, out=out), args.steps, args.warmup)
-    # context, measured right after the timed run (the part as warm as it was)
-    ceiling = mfma_ceiling(dmm, torch, qa, all_variants=args.calibrate)
-    vendor = vendor_baseline(torch, qa, qb, sa, sb, out, args.steps, args.warmup)
-    gpu_c = None if args.no_cpu else out.view(torch.int16).cpu().numpy().view("uint16")
-    flops = 2.0 * m * n * k
+    ours = lambda: dmm.gemm_a8w8_ptpc(qa, bs, sa, sb, out=out)
+    arms = {"ours": ours}
+    vendor = {"library": VENDOR}
+    try:
+        vf = vendor_fn(torch, qa, qb, sa, sb)
+        vf()
+        arms["vendor_eager"] = vf
+    except Exception as e:  # an unsupported _scaled_mm form leaves only the error in the line
+        vendor["error"] = f"{type(e).__name__}: {str(e)[:160]}"
+    t = timed_arms(arms, args.steps, args.warmup, WARM_S)
+    ms = t["ours"]["median"]
     tflops = flops / (ms * 1e-3) / 1e12
+    timing = {"protocol": f"HIP graph of {args.steps} launches replayed {BATCHES} times in {PASSES} passes "
+                          f"alternating with the vendor arm; per-call median of the batches",
+              "warm_s": t["ours"]["warm_s"], "batches": BATCHES, "launches_per_batch": args.steps,
+              "min_ms": round(t["ours"]["min"], 5), "max_ms": round(t["ours"]["max"], 5),
+              "min_of_pass_medians_ms": round(t["ours"]["pass_min"], 5), "batches_ms": t["ours"]["batches_ms"]}
+    cold = cold_ms(ours)
+    timing["cold_ms_after_1GiB_scrub"] = {kk: round(v, 5) for kk, v in cold.items()}
+    if "vendor_eager" in t:
+        c = vf()
+        vms = t["vendor_eager"]["median"]
+        vendor.update({"us": round(vms * 1e3, 1), "TFLOP/s": round(flops / (vms * 1e-3) / 1e12, 1),
+                       "min_of_pass_medians_us": round(t["vendor_eager"]["pass_min"] * 1e3, 1),
+                       "rel_l2_vs_this_library": ((c.float() - out.float()).norm() / out.float().norm()).item()})
+        del c
+    gpu_c = None if args.no_cpu else out.view(torch.int16).cpu().numpy().view("uint16")
     rec = {
         "metric": "fp8 GEMM TFLOP/s + % of fp8 MFMA peak, ptpc 32768x7168x1792 (1 MI355X)",
         "value": round(tflops, 2),
@@ -230,11 +467,19 @@ def main():
                    "pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic_from_profiles("gemm_a8w8_ptpc")},
-        "mfma_ceiling": dict(ceiling, value_over_one_wave_ceiling=round(
-            tflops / ceiling["one_wave_per_simd_TFLOP/s"], 4)),
+        "timing": timing,
+        "device": device,
         "vendor_baseline": vendor,
     }
     del out, qb
+    torch.cuda.empty_cache()
+    if not args.no_ceiling:
+        try:
+            ceiling = mfma_ceiling(torch, qa, all_variants=args.calibrate)
+            rec["mfma_ceiling"] = dict(ceiling, value_over_one_wave_ceiling=round(
+                tflops / ceiling["one_wave_per_simd_TFLOP/s"], 4))
+        except ImportError as e:
+            rec["mfma_ceiling"] = {"error": str(e)}
     if args.extra:
         rec["extra"] = extra_shapes(dmm, torch, args)
     if not args.no_cpu:
@@ -242,67 +487,13 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def mfma_ceiling(dmm, torch, frag, all_variants=False, iters=1200, launches=100):
-    """What the part sustains issuing nothing but the GEMM's matrix op:
-    back-to-back independent fp8 16x16x128 ops on every SIMD, one and two
-    waves per SIMD, operands taken from the headline's own A codes
-    (dmm_mfma_ceiling_fp8).  With all_variants, also the mxfp8 form and the
-    same stream with one kind of instruction interleaved after each op, one
-    wave per SIMD.  TFLOP/s over HIP events on the launch stream."""
-    out = torch.empty(1 << 20, dtype=torch.float32, device="cuda:0")
-
-    def rate(wps, variant):
-        flops = dmm.mfma_ceiling_fp8(frag, iters, wps, variant, out=out)[1]
-        ms = timed(lambda: dmm.mfma_ceiling_fp8(frag, iters, wps, variant, out=out), launches, 10)
-        return round(flops / (ms * 1e-3) / 1e12, 1)
-
-    # the part's clock settles to a new load within a fraction of a second:
-    # run the plain stream ~0.3 s before the first figure
-    timed(lambda: dmm.mfma_ceiling_fp8(frag, iters, 1, "plain", out=out), 1000, 0)
-
-    res = {"kind": "back-to-back independent fp8 16x16x128 matrix ops (calibration kernel)",
-           "one_wave_per_simd_TFLOP/s": rate(1, "plain"), "two_waves_per_simd_TFLOP/s": rate(2, "plain")}
-    if all_variants:
-        res["one_wave_per_simd_variants_TFLOP/s"] = {
-            v: rate(1, v) for v in ("plain", "scaled", "lds_read", "valu2", "acc_read", "acc_read16", "vmem_load",
-                                    "lds_dma")}
-        res["two_waves_per_simd_variants_TFLOP/s"] = {
-            v: rate(2, v) for v in ("plain", "lds_read", "valu2", "acc_read", "acc_read16", "vmem_load", "lds_dma")}
-    del out
-    return res
-
-
-def vendor_baseline(torch, qa, qb, sa, sb, ours, steps, warmup, min_warm_s=0.0):
-    """The vendor library on the same codes and scales: torch._scaled_mm
-    (hipBLASLt on ROCm) with per-row A and per-column B fp32 scales, bf16
-    out, timed like the headline; its output is compared with this
-    library's (relative L2 distance)."""
-    lib = "hipBLASLt via torch._scaled_mm (per-row A / per-column B fp32 scales)"
-    try:
-        a8, b8 = qa.view(torch.float8_e4m3fn), qb.view(torch.float8_e4m3fn)
-        sa2, sb2 = sa.view(-1, 1), sb.view(1, -1)
-
-        def f():
-            return torch._scaled_mm(a8, b8.t(), scale_a=sa2, scale_b=sb2, out_dtype=torch.bfloat16)
-
-        ms = timed(f, steps, warmup, min_warm_s)
-        c = f()
-        m, k = qa.shape
-        n = qb.shape[0]
-        rel = ((c.float() - ours.float()).norm() / ours.float().norm()).item()
-        del c
-        return {"library": lib, "us": round(ms * 1e3, 1), "TFLOP/s": round(2.0 * m * n * k / (ms * 1e-3) / 1e12, 1),
-                "rel_l2_vs_this_library": rel}
-    except Exception as e:  # an unsupported _scaled_mm form leaves only the error in the line
-        return {"library": lib, "error": f"{type(e).__name__}: {str(e)[:160]}"}
-
-
 def extra_shapes(dmm, torch, args):
     """Secondary lines: the other scaling modes, the tail-only and gathered
-    shapes, and the bf16 GEMM (fewer steps each)."""
+    shapes, the quantisers and the bf16 GEMM, each timed with the same
+    protocol (graph batches, median of 9, vendor arm alternating for the
+    ptpc shapes) after at least 0.15 s of warm-up launches."""
     res = {}
-    # short shapes: at least 150 ms of launches before timing (the clock ramp)
-    steps, warm, warm_s = max(5, args.steps // 4), 20, 0.15
+    steps, warm_s = max(5, args.steps // 4), 0.15
     for name, mode, m, n, k, sa_seed, sb_seed in [
         ("blockscale_16384x7168x2048", "blockscale", 16384, 7168, 2048, 41, 42),
         ("mxfp8_32768x7168x1792", "mxfp8", 32768, 7168, 1792, 31, 32),
@@ -316,15 +507,19 @@ def extra_shapes(dmm, torch, args):
         qa, bs, sa, sb, qb = headline_operands(dmm, torch, m, n, k, sa_seed, sb_seed, mode, keep_b=True)
         out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
         fn = {"ptpc": dmm.gemm_a8w8_ptpc, "blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
-        ms = timed(lambda: fn(qa, bs, sa, sb, out=out), steps, warm, warm_s)
+        arms = {"ours": lambda: fn(qa, bs, sa, sb, out=out)}
+        if mode == "ptpc":  # the vendor library has the per-row / per-column form only
+            arms["vendor_eager"] = vendor_fn(torch, qa, qb, sa, sb)
+        t = timed_arms(arms, steps, 20, warm_s)
+        ms = t["ours"]["median"]
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         hbm = (m * k + n * k + 2 * m * n) / (ms * 1e-3) / 1e9
-        res[name] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1), "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 1),
-                     "alg_GB/s": round(hbm, 0)}
-        if mode == "ptpc":  # the vendor library has the per-row / per-column form only
-            v = vendor_baseline(torch, qa, qb, sa, sb, out, steps, warm, warm_s)
-            res[name]["vendor_us"] = v.get("us")
-        del qa, bs, sa, sb, qb, out
+        res[name] = {"us": round(ms * 1e3, 1), "min_us": round(t["ours"]["min"] * 1e3, 1),
+                     "max_us": round(t["ours"]["max"] * 1e3, 1), "TFLOP/s": round(tf, 1),
+                     "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 1), "alg_GB/s": round(hbm, 0)}
+        if "vendor_eager" in t:
+            res[name]["vendor_us"] = round(t["vendor_eager"]["median"] * 1e3, 1)
+        del qa, bs, sa, sb, qb, out, arms
         torch.cuda.empty_cache()
     from dense_matmul_amd import inputs
 
@@ -340,7 +535,8 @@ def extra_shapes(dmm, torch, args):
             ("quantize_mxfp8_32768x1792", dmm.quantize_mxfp8, 32768, 1792, lambda r, c: r * c // 32),
             ("quantize_mxfp8_7168x1792", dmm.quantize_mxfp8, 7168, 1792, lambda r, c: r * c // 32)]:
         x = torch.from_numpy(inputs.normal((rows, cols), 3)).to("cuda:0")
-        ms = timed(lambda: fn(x), 100, 20, warm_s)
+        t = timed_arms({"q_eager": lambda: fn(x)}, 100, 20, warm_s)
+        ms = t["q_eager"]["median"]
         gbs = (5 * rows * cols + extra_bytes(rows, cols)) / (ms * 1e-3) / 1e9
         res[name] = {"us": round(ms * 1e3, 1), "alg_GB/s": round(gbs), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
         del x
@@ -351,10 +547,12 @@ def extra_shapes(dmm, torch, args):
     a = torch.from_numpy(a32).to(torch.bfloat16).to("cuda:0")
     b = torch.from_numpy(b_kn.T.copy()).to(torch.bfloat16).to("cuda:0")
     out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
-    ms = timed(lambda: dmm.gemm_bf16(a, b, out=out), 200, 20, warm_s)
+    t = timed_arms({"bf16": lambda: dmm.gemm_bf16(a, b, out=out)}, 200, 20, warm_s)
+    ms = t["bf16"]["median"]
     tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
-    res["bf16_4096x1024x896"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
-                                 "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
+    res["bf16_4096x1024x896"] = {"us": round(ms * 1e3, 2), "min_us": round(t["bf16"]["min"] * 1e3, 2),
+                                 "TFLOP/s": round(tf, 1), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1),
+                                 "alg_GB/s": round((2 * (m * k + n * k + m * n)) / (ms * 1e-3) / 1e9)}
     return res
 
 

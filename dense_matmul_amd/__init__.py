@@ -18,8 +18,6 @@ Functions (names as in the C ABI):
     gemm_a8w8_blockscale(a, b_shuf, a_scale, b_scale, out=None) -> bf16 [M,N]
     gemm_a8w8_mxfp8(a, b_shuf, a_scale, b_scale, out=None)      -> bf16 [M,N]
     gemm_bf16(a, b, out=None, tile="auto")                       -> bf16 [M,N]
-    mfma_ceiling_fp8(frag, iters, waves_per_simd, variant=0, out=None) -> (out, FLOPs of the launch)
-        (calibration: back-to-back fp8 matrix ops, not a step of the GEMM)
 
 Argument errors (status DMM_EINVAL) raise ValueError; everything else raises
 RuntimeError.
@@ -38,7 +36,6 @@ EXPORTS = (
     "dmm_status_str", "dmm_last_error", "quantize_per_token", "quantize_per_token_bf16", "quantize_blockscale_a",
     "quantize_blockscale_b", "quantize_mxfp8", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile",
     "gemm_a8w8_ptpc_gathered", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8", "gemm_bf16", "gemm_bf16_tile",
-    "dmm_mfma_ceiling_fp8",
 )
 
 _lib = None
@@ -68,8 +65,6 @@ def lib():
                                               ctypes.c_uint32, I64, P, P]
         L.gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
         L.gemm_bf16_tile.argtypes = [P, P, P, I64, I64, I64, ctypes.c_int, P]
-        L.dmm_mfma_ceiling_fp8.argtypes = [P, I64, P, I64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                           ctypes.POINTER(ctypes.c_int), P]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -295,26 +290,3 @@ def gemm_bf16(a, b, out=None, tile="auto"):
             raise ValueError(f"tile must be 'auto' or one of {sorted(BF16_TILES)} (got {tile!r})")
         _check(lib().gemm_bf16_tile(_ptr(a), _ptr(b), _ptr(out), m, n, k, BF16_TILES[tile], _stream()))
     return out
-
-
-# ------------------------------------------------------------ calibration
-MFMA_CEILING_VARIANTS = {"plain": 0, "scaled": 1, "lds_read": 2, "valu2": 3, "acc_read": 4, "acc_read16": 5,
-                         "vmem_load": 6, "lds_dma": 7}
-
-
-def mfma_ceiling_fp8(frag, iters, waves_per_simd=1, variant="plain", out=None):
-    """One launch of the matrix-core issue-ceiling kernel (dmm_mfma_ceiling_fp8)
-    on e4m3 codes frag (at least 2 MiB, any shape); variant is a name of
-    MFMA_CEILING_VARIANTS; returns (out, FLOPs)."""
-    if variant not in MFMA_CEILING_VARIANTS:
-        raise ValueError(f"variant must be one of {sorted(MFMA_CEILING_VARIANTS)} (got {variant!r})")
-    _require(frag, "frag", None, None)
-    fb = _codes(frag, "frag")
-    if out is None:
-        out = torch.empty(1 << 20, dtype=torch.float32, device=frag.device)
-    _require(out, "out", torch.float32, 1)
-    wg = ctypes.c_int(0)
-    _check(lib().dmm_mfma_ceiling_fp8(_ptr(fb), fb.numel(), _ptr(out), out.numel(), int(iters), int(waves_per_simd),
-                                      MFMA_CEILING_VARIANTS[variant], ctypes.byref(wg), _stream()))
-    flops = 2.0 * 16 * 16 * 128 * 16 * int(iters) * wg.value * 4 * int(waves_per_simd)
-    return out, flops

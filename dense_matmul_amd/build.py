@@ -1,7 +1,9 @@
-"""Build libdmm.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Build libdmm.so (the HIP kernels and the C ABI) for gfx950 with hipcc,
+and the benchmark's calibration library libdmm_calib.so beside it.
 
-Compiles every time it is called.  Output: dense_matmul_amd/libdmm.so, built
-in-tree so that it travels with the source tree.
+Compiles every time it is called.  Outputs: dense_matmul_amd/libdmm.so and
+dense_matmul_amd/calib/libdmm_calib.so, built in-tree so that they travel
+with the source tree.
 """
 import os
 import shutil
@@ -12,7 +14,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdmm.so")
-SOURCES = ["gemm_a8w8.hip", "gemm_bf16.hip", "quant.hip", "calib.hip", "api.cpp"]
+SOURCES = ["gemm_a8w8.hip", "gemm_bf16.hip", "quant.hip", "api.cpp"]
+# the benchmark's matrix-op calibration kernel: its own library, not libdmm
+CALIB_SRC = os.path.join(HERE, "calib", "calib.hip")
+CALIB_LIB = os.path.join(HERE, "calib", "libdmm_calib.so")
 ARCH = "gfx950"
 # packed-fp32 instructions are kept out of every kernel (-packed-fp32-ops)
 FLAGS = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
@@ -26,14 +31,16 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(lib=LIB, jobs=4):
-    """Compile all sources to objects in parallel, then link libdmm.so."""
+def build(lib=LIB, calib_lib=CALIB_LIB):
+    """Compile all sources to objects in parallel, then link libdmm.so and
+    libdmm_calib.so."""
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     procs, objs = [], []
-    for src in SOURCES:
-        obj = os.path.join(objdir, src + ".o")
-        objs.append(obj)
+    for src in SOURCES + [CALIB_SRC]:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        if src != CALIB_SRC:
+            objs.append(obj)
         lang = [] if src.endswith(".hip") else ["-x", "hip"]
         cmd = [hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -47,9 +54,10 @@ def build(lib=LIB, jobs=4):
             sys.stderr.write(out + "\n")
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(f"--- {s}\n{o}" for s, o in failed))
-    tmp = lib + ".tmp"
-    subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], check=True)
-    os.replace(tmp, lib)
+    for out, ins in ((lib, objs), (calib_lib, [os.path.join(objdir, "calib.hip.o")])):
+        tmp = out + ".tmp"
+        subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *ins, "-o", tmp], check=True)
+        os.replace(tmp, out)
     return lib
 
 

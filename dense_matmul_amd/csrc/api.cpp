@@ -24,8 +24,6 @@ hipError_t launch_quantize_blockscale_a(const float* x, uint8_t* q, float* s, in
 hipError_t launch_quantize_blockscale_b(const float* x, uint8_t* q, float* s, int n, int k, hipStream_t st);
 hipError_t launch_quantize_mxfp8(const float* x, uint8_t* q, uint8_t* s, int rows, int k, hipStream_t st);
 hipError_t launch_preshuffle_b(const uint8_t* b, uint8_t* out, int n, int k, hipStream_t st);
-hipError_t launch_mfma_ceiling(const uint8_t* frag, float* out, int out_len, int iters, int wps, int variant,
-                               int* grid, hipStream_t st);
 }  // namespace dmm
 
 namespace {
@@ -254,24 +252,6 @@ dmm_status gemm_bf16_tile(const uint16_t* a, const uint16_t* b, uint16_t* c, int
 
 dmm_status gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream) {
     return gemm_bf16_tile(a, b, c, m, n, k, 0, stream);
-}
-
-dmm_status dmm_mfma_ceiling_fp8(const uint8_t* frag, int64_t frag_bytes, float* out, int64_t out_len, int iters,
-                                int waves_per_simd, int variant, int* workgroups, void* stream) {
-    REQUIRE_PTR(frag);
-    REQUIRE_PTR(out);
-    REQUIRE(frag_bytes >= ((int64_t)65536 * 32), "frag must hold at least 2 MiB (got %lld bytes)", (long long)frag_bytes);
-    REQUIRE(out_len >= 1 && out_len < kLimit, "out_len must be in [1, 2^31)");
-    REQUIRE(iters >= 1 && iters <= (1 << 20), "iters must be in [1, 2^20] (got %d)", iters);
-    REQUIRE(waves_per_simd == 1 || waves_per_simd == 2, "waves_per_simd must be 1 or 2 (got %d)", waves_per_simd);
-    REQUIRE(variant >= 0 && variant <= 7, "variant must be in [0, 7] (got %d)", variant);
-    dmm_status s = check_device();
-    if (s != DMM_OK) return s;
-    int grid = 0;
-    s = launched(dmm::launch_mfma_ceiling(frag, out, (int)out_len, iters, waves_per_simd, variant, &grid,
-                                           (hipStream_t)stream));
-    if (s == DMM_OK && workgroups) *workgroups = grid;
-    return s;
 }
 
 }  // extern "C"

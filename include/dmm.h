@@ -121,8 +121,9 @@ dmm_status gemm_a8w8_ptpc(const uint8_t* a, const uint8_t* b_shuf, const float* 
  * waves), 0 = the choice gemm_a8w8_ptpc makes (128 x 256 when the problem
  * has at most one 256 x 256 tile per two compute units).  The pages size the
  * tile to the problem in the same spirit (mori PR 785, Cost: the table's
- * shapes; aiter PR 6539, Benchmark: the tuned shapes).  Other values of
- * tile return DMM_EINVAL. */
+ * shapes; aiter PR 6539, Motivation and its review thread: the tuned rows,
+ * one kernel configuration per shape).  Other values of tile return
+ * DMM_EINVAL. */
 dmm_status gemm_a8w8_ptpc_tile(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale,
                                const float* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k, int tile,
                                void* stream);
@@ -180,36 +181,6 @@ dmm_status gemm_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t 
  * return DMM_EINVAL. */
 dmm_status gemm_bf16_tile(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t m, int64_t n, int64_t k,
                           int tile, void* stream);
-
-/* ------------------------------------------------------------ calibration */
-
-/* Matrix-core issue ceiling, for reading a GEMM's measured rate against what
- * the part sustains rather than only against the published peak (mori PR
- * 785, Cost, and the scope's target are stated as a fraction of the dense
- * fp8 peak); not a step of the GEMM.  One workgroup per compute unit, with
- * waves_per_simd (1 or 2) waves on each of its four SIMDs; every wave loads
- * four A and four B fragments (32 bytes per lane each) from frag and issues
- * iters x 16 back-to-back independent fp8 16x16x128 matrix ops on them, then
- * writes the sum of its accumulators to out[thread] for threads below
- * out_len.  variant selects the op and what follows each one:
- *   0  v_mfma_f32_16x16x128_f8f6f4 alone (the ptpc / blockscale instruction)
- *   1  v_mfma_scale_f32_16x16x128_f8f6f4 with unit E8M0 scales (mxfp8's)
- *   2  variant 0 + one ds_read_b128 per op
- *   3  variant 0 + two v_mul_f32 per op
- *   4  variant 0 + one v_accvgpr_read_b32 per op
- *   5  variant 0 + sixteen v_accvgpr_read_b32 after every sixteenth op
- *   6  variant 0 + one 16-byte-per-lane buffer load into VGPRs per four ops
- *   7  variant 0 + one 16-byte-per-lane buffer load into LDS per four ops
- *      (6 and 7 read frag's first 2 MiB, 1 KiB per instruction)
- * One launch does
- *     2 * 16 * 16 * 128 * 16 * iters * (*workgroups) * 4 * waves_per_simd
- * FLOPs; *workgroups (host pointer, may be NULL) receives the grid size (the
- * device's compute-unit count).  frag: device, at least 2 MiB of e4m3 codes
- * (the operand bytes change the power the part draws, so pass real codes);
- * out: device fp32 [out_len].  Rules: 1 <= iters <= 2^20; waves_per_simd 1
- * or 2; 0 <= variant <= 7; frag_bytes >= 2 MiB; 1 <= out_len < 2^31. */
-dmm_status dmm_mfma_ceiling_fp8(const uint8_t* frag, int64_t frag_bytes, float* out, int64_t out_len, int iters,
-                                int waves_per_simd, int variant, int* workgroups, void* stream);
 
 #ifdef __cplusplus
 }

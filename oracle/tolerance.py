@@ -5,58 +5,109 @@ Primary rule, for every element: |gpu - ref| <= 2e-2 |ref| + 1e-3, and over
 all checked elements relL2 < 3e-3 (the relL2 gate of mori PR 785, section
 Test, and PR 809, section Results).
 
-The fp8 matrix-core instructions of gfx950 sum the 128 (or 32) products of one
-instruction with about 12 significant bits relative to the largest of them
-(measured: worst |error| / max|product| = 2^-11.7 over 16k outputs, the same
-for the K=128 and K=32 fp8 instructions and whether or not the accumulator is
-added inside the instruction).  An output whose exact value nearly cancels can
-therefore miss the 1e-3 absolute floor by a hardware rounding that no
-instruction choice avoids.  Such an element is accepted only if
+Secondary rule (a stated departure from the element-wise primary rule).  The
+fp8 matrix-core instructions of gfx950 add the 128 (or, scaled, 4 x 32)
+products of one instruction with a precision tied to the largest of them, not
+to the result: the GPU test tests/test_gpu_mfma_precision.py pins, through the
+public GEMM, that one instruction's error stays within RHO = 2^-11 of its
+largest product (and that it is not zero, i.e. the instruction does round).
+An output whose exact value nearly cancels can then miss the fixed 1e-3 floor
+by a rounding that no instruction choice avoids.  Such an element is accepted
+only if
 
     |gpu - ref| <= 2e-2 |ref| + 1e-3 + ulp_bf16(ref)
-                   + 2^-9 * sum over 128-wide K blocks of max_k |a'(m,k) b'(n,k)|
+                   + RHO * sum over 128-wide K blocks b of max_{k in b} |a'(m,k) b'(n,k)|
 
-(a margin of 2^2.7 over the measured worst case), and at most 1e-3 of the
-checked elements may need it (a sanity limit: at the full-size workloads
-3-4e-5 of the sampled elements need it at K = 1792-2048 and 1.5e-4 at
-K = 7168, since near-cancelling outputs fall under the fixed 1e-3 floor more
-often as the sums grow; they use at most 2.2 % of their bound).  A wrong K tile, a stale
-LDS read or a missing scale gives errors of the order of |C| itself, far
-outside the per-element bound whatever their number.
+and the number of elements that need it stays within a cap derived from the
+same bound, not from observed counts: if every instruction rounded as
+coarsely as RHO allows, each block's error would be uniform on
+[-RHO M_b, RHO M_b] (M_b its largest product), the element's error a sum of
+such independent terms with variance RHO^2 / 3 * sum_b M_b^2, and the expected
+number of elements missing the primary rule
+
+    E = sum_i P(|e_i| > 2e-2 |ref_i| + 1e-3) ~ sum_i 2 Phi(-t_i / s_i)
+
+(normal approximation).  M_b is over-estimated by max_k |a'| * max_k |b'| of
+the block, so E is an upper estimate; the cap is E + 4 sqrt(E) + 1 (a Poisson
+allowance).  A wrong K tile, a stale LDS read or a missing scale gives errors
+of the order of |C| itself, far outside the per-element bound whatever their
+number; a precision loss spread over many elements trips the cap.
 """
+import math
+
 import numpy as np
 
 PRIMARY_REL, PRIMARY_ABS, REL_L2 = 2e-2, 1e-3, 3e-3
-MFMA_REL = 2.0**-9
-MAX_SECONDARY_FRACTION = 1e-3
+RHO = 2.0**-11  # pinned on the GPU: tests/test_gpu_mfma_precision.py
 
 
 def bits_to_f64(h):
     return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def block_max_bound(mode, qa, qb, sa, sb, m_idx, n_idx):
-    """sum over 128-K blocks of max |a'(m,k) b'(n,k)| for element pairs."""
+def element_scales(mode, sa, sb, m_rows, n_rows, k):
+    """Per-element scales [len(m_rows), K] and [len(n_rows), K] in float64."""
+    m_rows, n_rows = np.asarray(m_rows), np.asarray(n_rows)
+    if mode == "ptpc":
+        fa = np.broadcast_to(np.asarray(sa, np.float64)[m_rows][:, None], (len(m_rows), k))
+        fb = np.broadcast_to(np.asarray(sb, np.float64)[n_rows][:, None], (len(n_rows), k))
+    elif mode == "blockscale":
+        fa = np.repeat(np.asarray(sa, np.float64)[:, m_rows].T, 128, axis=1)
+        fb = np.repeat(np.asarray(sb, np.float64)[n_rows // 128], 128, axis=1)
+    elif mode == "mxfp8":
+        from oracle import dec_e8m0
+
+        fa = np.repeat(dec_e8m0(np.asarray(sa)[:, m_rows]).astype(np.float64).T, 32, axis=1)
+        fb = np.repeat(dec_e8m0(np.asarray(sb)[:, n_rows]).astype(np.float64).T, 32, axis=1)
+    else:
+        raise ValueError(mode)
+    return fa, fb
+
+
+def dequantised_rows(mode, qa, qb, sa, sb, m_rows, n_rows):
+    """a'[m_rows] and b'[n_rows] in float64 (exact: an e4m3 value times an
+    fp32 or power-of-two scale)."""
     from oracle import dec_e4m3
 
+    fa, fb = element_scales(mode, sa, sb, m_rows, n_rows, qa.shape[1])
+    return dec_e4m3(qa[m_rows]).astype(np.float64) * fa, dec_e4m3(qb[n_rows]).astype(np.float64) * fb
+
+
+def block_max_bound(mode, qa, qb, sa, sb, m_idx, n_idx):
+    """sum over 128-K blocks of max |a'(m,k) b'(n,k)| for element pairs."""
+    um, un = np.unique(m_idx), np.unique(n_idx)
+    a, b = dequantised_rows(mode, qa, qb, sa, sb, um, un)
+    ra = {m: i for i, m in enumerate(um)}
+    rb = {n: i for i, n in enumerate(un)}
     k = qa.shape[1]
     out = np.empty(len(m_idx))
     for t, (m, n) in enumerate(zip(m_idx, n_idx)):
-        a = dec_e4m3(qa[m]).astype(np.float64)
-        b = dec_e4m3(qb[n]).astype(np.float64)
-        if mode == "ptpc":
-            a = a * float(sa[m])
-            b = b * float(sb[n])
-        elif mode == "blockscale":
-            a = a * np.repeat(sa[:, m].astype(np.float64), 128)
-            b = b * np.repeat(sb[n // 128].astype(np.float64), 128)
-        elif mode == "mxfp8":
-            from oracle import dec_e8m0
-
-            a = a * np.repeat(dec_e8m0(sa[:, m]).astype(np.float64), 32)
-            b = b * np.repeat(dec_e8m0(sb[:, n]).astype(np.float64), 32)
-        out[t] = np.abs(a * b).reshape(k // 128, 128).max(axis=1).sum()
+        out[t] = np.abs(a[ra[m]] * b[rb[n]]).reshape(k // 128, 128).max(axis=1).sum()
     return out
+
+
+def secondary_cap(mode, operands, ref_f64, rows, chunk=4096):
+    """The cap on the number of elements that may need the secondary rule
+    (module docstring): E + 4 sqrt(E) + 1 with E the expected count of
+    primary misses under RHO-coarse uniform rounding of every block, using
+    the over-estimate M_b <= max|a'| max|b'| of each 128-K block."""
+    from scipy.special import erfc
+
+    qa, qb, sa, sb = operands
+    k, n = qa.shape[1], qb.shape[0]
+    r = np.arange(qa.shape[0]) if rows is None else np.asarray(rows)
+    _, b = dequantised_rows(mode, qa, qb, sa, sb, r[:1], np.arange(n))
+    bmax2 = np.abs(b).reshape(n, k // 128, 128).max(axis=2) ** 2  # [N, KB]
+    del b
+    e = 0.0
+    for c0 in range(0, len(r), chunk):
+        a, _ = dequantised_rows(mode, qa, qb, sa, sb, r[c0:c0 + chunk], np.arange(1))
+        amax2 = np.abs(a).reshape(a.shape[0], k // 128, 128).max(axis=2) ** 2  # [rows, KB]
+        s = RHO / math.sqrt(3.0) * np.sqrt(amax2 @ bmax2.T)
+        t = PRIMARY_REL * np.abs(ref_f64[c0:c0 + chunk]) + PRIMARY_ABS
+        with np.errstate(divide="ignore"):
+            e += float(erfc(t / (s * math.sqrt(2.0))).sum())  # 2 Phi(-t/s); an all-zero block row gives 0
+    return e + 4.0 * math.sqrt(e) + 1.0, e
 
 
 def check(got_bits, ref_bits, what, mode=None, operands=None, rows=None):
@@ -64,27 +115,31 @@ def check(got_bits, ref_bits, what, mode=None, operands=None, rows=None):
 
     got_bits / ref_bits: bf16 bit patterns of the same elements; ``rows``
     maps their row index to the GEMM's row (for sampled checks); operands =
-    (qa, qb, sa, sb) enables the secondary bound (fp8 modes)."""
+    (qa, qb, sa, sb) enables the secondary rule (fp8 modes)."""
     g, r = bits_to_f64(got_bits), bits_to_f64(ref_bits)
     assert np.isfinite(g).all(), f"{what}: non-finite output ({np.count_nonzero(~np.isfinite(g))} elements)"
     err = np.abs(g - r)
     rl2 = float(np.sqrt((err**2).sum() / max((r**2).sum(), 1e-300)))
     assert rl2 < REL_L2, f"{what}: relL2 {rl2:.3g} >= {REL_L2}"
     bad = np.argwhere(err > PRIMARY_REL * np.abs(r) + PRIMARY_ABS)
-    stats = {"rel_l2": rl2, "elements": int(err.size), "primary_fail": int(len(bad)), "max_err": float(err.max())}
+    stats = {"rel_l2": rl2, "elements": int(err.size), "primary_fail": int(len(bad)), "max_err": float(err.max()),
+             "secondary_cap": None}
     if len(bad) == 0:
         return stats
     assert operands is not None and mode is not None, \
-        f"{what}: {len(bad)} elements out of tolerance (max err {err.max():.3g}) and no secondary bound applies"
-    assert len(bad) <= MAX_SECONDARY_FRACTION * err.size + 1, \
-        f"{what}: {len(bad)} of {err.size} elements out of the primary tolerance (max err {err.max():.3g})"
+        f"{what}: {len(bad)} elements out of tolerance (max err {err.max():.3g}) and no secondary rule applies"
+    cap, expect = secondary_cap(mode, operands, r, rows)
+    stats["secondary_cap"] = round(cap, 1)
+    stats["secondary_model_expectation"] = round(expect, 1)
+    assert len(bad) <= cap, (f"{what}: {len(bad)} of {err.size} elements out of the primary tolerance, over the "
+                             f"cap {cap:.0f} the rounding model allows (max err {err.max():.3g})")
     qa, qb, sa, sb = operands
     mi = bad[:, 0] if rows is None else np.asarray(rows)[bad[:, 0]]
     ni = bad[:, 1]
     bound = block_max_bound(mode, qa, qb, sa, sb, mi, ni)
     rr = r[bad[:, 0], bad[:, 1]]
     ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(rr), 1e-38))[1] - 8)
-    lim = PRIMARY_REL * np.abs(rr) + PRIMARY_ABS + ulp + MFMA_REL * bound
+    lim = PRIMARY_REL * np.abs(rr) + PRIMARY_ABS + ulp + RHO * bound
     e = err[bad[:, 0], bad[:, 1]]
     worst = int(np.argmax(e / lim))
     assert np.all(e <= lim), (f"{what}: element ({mi[worst]}, {ni[worst]}) err {e[worst]:.3g} exceeds the "

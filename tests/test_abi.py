@@ -34,8 +34,10 @@ def test_header_declares_the_boundary():
               "gemm_a8w8_blockscale",
               "gemm_a8w8_mxfp8",
               "gemm_bf16", "gemm_bf16_tile", "quantize_blockscale_a", "quantize_blockscale_b", "quantize_mxfp8", "dmm_status_str",
-              "dmm_last_error", "dmm_mfma_ceiling_fp8"):
+              "dmm_last_error"):
         assert f in names, f
+    # the benchmark's calibration kernel lives in its own library, not in the boundary
+    assert not any("ceiling" in f or "calib" in f for f in names)
 
 
 def test_library_exports_every_declared_function(L):
@@ -130,18 +132,3 @@ def test_quantiser_and_preshuffle_rules(L):
     assert L.preshuffle_b(ALIGNED, ctypes.c_void_p((1 << 20) + 256), 16, 128, None) == 1
     assert b"overlap" in L.dmm_last_error()
     assert L.gemm_bf16(ALIGNED, ALIGNED, ALIGNED, 4, 16, 96, None) == 1
-
-
-@pytest.mark.parametrize("frag,frag_bytes,out_len,iters,wps,var,why", [
-    (ALIGNED, 1 << 20, 16, 1, 1, 0, "frag must hold"), (ALIGNED, 1 << 21, 0, 1, 1, 0, "out_len"),
-    (ALIGNED, 1 << 21, 16, 0, 1, 0, "iters"), (ALIGNED, 1 << 21, 16, (1 << 20) + 1, 1, 0, "iters"),
-    (ALIGNED, 1 << 21, 16, 1, 3, 0, "waves_per_simd"), (ALIGNED, 1 << 21, 16, 1, 0, 0, "waves_per_simd"),
-    (ALIGNED, 1 << 21, 16, 1, 1, 8, "variant"), (ALIGNED, 1 << 21, 16, 1, 1, -1, "variant"),
-    (ctypes.c_void_p((1 << 20) + 4), 1 << 21, 16, 1, 1, 0, "frag: pointer"),
-    (None, 1 << 21, 16, 1, 1, 0, "frag: pointer"),
-])
-def test_mfma_ceiling_rules(L, frag, frag_bytes, out_len, iters, wps, var, why):
-    """The calibration entry point checks its arguments before any HIP call."""
-    st = L.dmm_mfma_ceiling_fp8(frag, frag_bytes, ALIGNED, out_len, iters, wps, var, None, None)
-    assert st == 1, st
-    assert why in L.dmm_last_error().decode()

@@ -304,11 +304,26 @@ def test_bf16_gemm(dmm, tile):
     a32, b_kn = inputs.bf16_operands(m, k, n, GOLD["bf16_seed"]["value"])
     a = torch.from_numpy(a32).to(torch.bfloat16)
     b = torch.from_numpy(np.ascontiguousarray(b_kn.T)).to(torch.bfloat16)  # [N, K]
-    c = dmm.gemm_bf16(a.to(DEV), b.to(DEV), tile=tile)
+    ad, bd = a.to(DEV), b.to(DEV)
+    # 20 launches, each into a freshly NaN-poisoned C followed by a canary
+    # (DeepGEMM PR 453, Reproduction and validation: repeated launches of this
+    # shape compared bit for bit)
+    buf = torch.empty(m * n + 2048, dtype=torch.bfloat16, device=DEV)
+    c = buf[: m * n].view(m, n)
+    canary = buf[m * n:].view(torch.int16)
+    first = None
+    for i in range(20):
+        buf.fill_(float("nan"))
+        canary.fill_(0x5A5A)
+        dmm.gemm_bf16(ad, bd, out=c, tile=tile)
+        if first is None:
+            first = c.clone()
+            assert not torch.isnan(first).any().item(), "unwritten elements"
+        else:
+            assert torch.equal(c.view(torch.int16), first.view(torch.int16)), f"launch {i} differs from launch 0"
+        assert bool((canary == 0x5A5A).all().item()), f"launch {i} wrote past the end of C"
     ref = oracle.gemm_bf16(a.view(torch.int16).numpy().view(np.uint16), b.view(torch.int16).numpy().view(np.uint16))
-    check_close(bf16_bits(c), ref, f"bf16 4096x1024x896 {tile}")
-    outs = [bf16_bits(dmm.gemm_bf16(a.to(DEV), b.to(DEV), tile=tile)) for _ in range(20)]
-    assert all(np.array_equal(o, outs[0]) for o in outs)
+    check_close(bf16_bits(first), ref, f"bf16 4096x1024x896 {tile}")
 
 
 @pytest.mark.parametrize("tile", ["128x128", "64x64"])
@@ -359,27 +374,3 @@ def test_many_tiles_per_workgroup_every_k_phase(dmm, mode, k):
     got = outs[0][rows]
     mism = np.argwhere(got != ref)
     assert mism.size == 0, f"{mode} {m}x{n}x{k}: {len(mism)} mismatches, first at {mism[:4].tolist()}"
-
-
-@pytest.mark.parametrize("variant", ["plain", "scaled", "lds_read", "valu2", "acc_read", "acc_read16", "vmem_load",
-                                     "lds_dma"])
-@pytest.mark.parametrize("wps", [1, 2])
-def test_mfma_ceiling_calibration(dmm, wps, variant):
-    """The calibration kernel runs on every compute unit, reports the FLOPs of
-    its launch, and is deterministic (its accumulators are finite and equal
-    across two launches, and the same for every variant: the extra
-    instructions never feed the matrix ops)."""
-    announce("mfma ceiling calibration, waves per SIMD", wps, "variant", variant)
-    g = torch.Generator().manual_seed(5)
-    frag = torch.randint(0, 0x7F, (1 << 21,), dtype=torch.uint8, generator=g).to(DEV)  # finite e4m3 codes
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    out1, flops = dmm.mfma_ceiling_fp8(frag, 3, wps, variant)
-    out2, _ = dmm.mfma_ceiling_fp8(frag, 3, wps, variant)
-    ref, _ = dmm.mfma_ceiling_fp8(frag, 3, wps, "plain")
-    torch.cuda.synchronize()
-    assert flops == 2.0 * 16 * 16 * 128 * 16 * 3 * cus * 4 * wps
-    used = cus * 256 * wps
-    assert torch.isfinite(out1[:used]).all()
-    assert torch.equal(out1[:used], out2[:used])
-    assert torch.equal(out1[:used], ref[:used])
-    assert (out1[:used] != 0).any()

@@ -16,7 +16,8 @@ Functions (names as in the C ABI):
     gemm_a8w8_ptpc_gathered(a, b_shuf, a_scale, b_scale, flags, src_rows, nchunks, own, epoch,
                             spin_limit=1 << 22, status=None, out=None) -> (bf16 [M,N], status)
     gemm_a8w8_blockscale(a, b_shuf, a_scale, b_scale, out=None) -> bf16 [M,N]
-    gemm_a8w8_mxfp8(a, b_shuf, a_scale, b_scale, out=None)      -> bf16 [M,N]
+    gemm_a8w8_mxfp8(a, b_shuf, a_scale, b_scale, out=None, tile="auto") -> bf16 [M,N]
+        (tile "256x256" / "256x128" calls gemm_a8w8_mxfp8_tile)
     gemm_bf16(a, b, out=None, tile="auto")                       -> bf16 [M,N]
 
 Argument errors (status DMM_EINVAL) raise ValueError; everything else raises
@@ -35,7 +36,8 @@ DMM_OK, DMM_EINVAL, DMM_ENODEV, DMM_ELAUNCH = 0, 1, 2, 3
 EXPORTS = (
     "dmm_status_str", "dmm_last_error", "quantize_per_token", "quantize_per_token_bf16", "quantize_blockscale_a",
     "quantize_blockscale_b", "quantize_mxfp8", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile",
-    "gemm_a8w8_ptpc_gathered", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8", "gemm_bf16", "gemm_bf16_tile",
+    "gemm_a8w8_ptpc_gathered", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8", "gemm_a8w8_mxfp8_tile", "gemm_bf16",
+    "gemm_bf16_tile",
 )
 
 _lib = None
@@ -61,6 +63,7 @@ def lib():
         for name in ("gemm_a8w8_ptpc", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8"):
             getattr(L, name).argtypes = [P, P, P, P, P, I64, I64, I64, P]
         L.gemm_a8w8_ptpc_tile.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
+        L.gemm_a8w8_mxfp8_tile.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
         L.gemm_a8w8_ptpc_gathered.argtypes = [P, P, P, P, P, I64, I64, I64, P, I64, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_uint32, I64, P, P]
         L.gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
@@ -255,16 +258,26 @@ def gemm_a8w8_blockscale(a, b_shuf, a_scale, b_scale, out=None):
     return out
 
 
-def gemm_a8w8_mxfp8(a, b_shuf, a_scale, b_scale, out=None):
-    """mxfp8 GEMM: E8M0 scale bytes a_scale [K/32, M], b_scale [K/32, N]."""
+MXFP8_TILES = {"256x256": 1, "256x128": 2}
+
+
+def gemm_a8w8_mxfp8(a, b_shuf, a_scale, b_scale, out=None, tile="auto"):
+    """mxfp8 GEMM: E8M0 scale bytes a_scale [K/32, M], b_scale [K/32, N].
+    tile: "auto" (the library's choice), "256x256" or "256x128" (same result)."""
     au, bu, out, m, n, k = _gemm_args(a, b_shuf, out)
     for t, name, rows in ((a_scale, "a_scale", m), (b_scale, "b_scale", n)):
         _require(t, name, None, 2)
         if t.dtype not in (torch.uint8, torch.float8_e8m0fnu):
             raise ValueError(f"{name}: expected uint8 or float8_e8m0fnu, got {t.dtype}")
         _shape(t, (k // 32, rows), name)
-    _check(lib().gemm_a8w8_mxfp8(_ptr(au), _ptr(bu), _ptr(a_scale.view(torch.uint8)), _ptr(b_scale.view(torch.uint8)),
-                                 _ptr(out), m, n, k, _stream()))
+    sa, sb = _ptr(a_scale.view(torch.uint8)), _ptr(b_scale.view(torch.uint8))
+    if tile == "auto":
+        _check(lib().gemm_a8w8_mxfp8(_ptr(au), _ptr(bu), sa, sb, _ptr(out), m, n, k, _stream()))
+    else:
+        if tile not in MXFP8_TILES:
+            raise ValueError(f"tile must be 'auto' or one of {sorted(MXFP8_TILES)} (got {tile!r})")
+        _check(lib().gemm_a8w8_mxfp8_tile(_ptr(au), _ptr(bu), sa, sb, _ptr(out), m, n, k, MXFP8_TILES[tile],
+                                          _stream()))
     return out
 
 

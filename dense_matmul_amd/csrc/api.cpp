@@ -234,6 +234,13 @@ dmm_status gemm_a8w8_mxfp8(const uint8_t* a, const uint8_t* b_shuf, const uint8_
     return gemm_common(2, 0, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
 }
 
+dmm_status gemm_a8w8_mxfp8_tile(const uint8_t* a, const uint8_t* b_shuf, const uint8_t* a_scale,
+                                const uint8_t* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k, int tile,
+                                void* stream) {
+    REQUIRE(tile >= 0 && tile <= 2, "tile must be 0 (auto), 1 (256x256) or 2 (256x128) (got %d)", tile);
+    return gemm_common(2, tile, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
+}
+
 dmm_status gemm_bf16_tile(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t m, int64_t n, int64_t k,
                           int tile, void* stream) {
     REQUIRE_PTR(a);

@@ -51,13 +51,16 @@
 namespace dmm {
 
 // MODE_PTPC_N: ptpc on the 128 x 256 tile of eight waves (see Cfg);
-// MODE_PTPC_G: ptpc over a gathered A (Gather), 256 x 256 tiles.
-enum { MODE_PTPC = 0, MODE_BLOCKSCALE = 1, MODE_MXFP8 = 2, MODE_PTPC_N = 3, MODE_PTPC_G = 4 };
+// MODE_PTPC_G: ptpc over a gathered A (Gather), 256 x 256 tiles;
+// MODE_MXFP8_N: mxfp8 on the 256 x 128 tile of four waves.
+enum { MODE_PTPC = 0, MODE_BLOCKSCALE = 1, MODE_MXFP8 = 2, MODE_PTPC_N = 3, MODE_PTPC_G = 4, MODE_MXFP8_N = 5 };
 
 template <int MODE>
 constexpr bool kWidePtpc = MODE == MODE_PTPC || MODE == MODE_PTPC_G;
 template <int MODE>
 constexpr bool kPtpc = kWidePtpc<MODE> || MODE == MODE_PTPC_N;
+template <int MODE>
+constexpr bool kMx = MODE == MODE_MXFP8 || MODE == MODE_MXFP8_N;
 
 constexpr int BK = 128;
 
@@ -123,30 +126,41 @@ struct GemmArgs {
 // lane) and 8 waves, two per SIMD, share a 128 x 256 tile: each SIMD then
 // has a second wave to issue matrix ops while one waits.  MODE_PTPC_N runs
 // ptpc on that narrow tile (matrix ops straight into VGPR accumulators),
-// which doubles the tile count of small problems.
+// which doubles the tile count of small problems.  MODE_MXFP8_N runs mxfp8
+// on a 256 x 128 tile of four waves, each owning all 256 rows and 32
+// columns (matrix ops straight into VGPR accumulators): A, the operand that
+// goes through LDS, is twice the size of B in each K tile.
 template <int MODE>
 struct Cfg {
-    static constexpr bool NARROW = MODE == MODE_BLOCKSCALE || MODE == MODE_PTPC_N;
-    static constexpr int MB = NARROW ? 8 : 16;   // 16-row blocks per wave
-    static constexpr int NBW = NARROW ? 2 : 4;   // 16-column blocks per wave
-    static constexpr int WAVES = NARROW ? 8 : 4;  // waves per workgroup
+    static constexpr sched::Shape S = sched::shape_of(MODE);  // kpipe.h
+    static constexpr bool NARROW = MODE == MODE_BLOCKSCALE || MODE == MODE_PTPC_N;  // 128 x 256, 8 waves
+    static constexpr int MB = S.MB;        // 16-row blocks per wave
+    static constexpr int NBW = S.NBW;      // 16-column blocks per wave
+    static constexpr int WAVES = S.WAVES;  // waves per workgroup
     static constexpr int NTHREADS = 64 * WAVES;
-    static constexpr int BM = 16 * MB;                             // tile rows
-    static constexpr int WN = 16 * NBW;                            // columns per wave
-    static constexpr int BN = WAVES * WN;                          // tile columns
-    static constexpr int NA = 2 * MB / WAVES;                      // DMA instructions per wave per K tile
+    static constexpr int BM = 16 * MB;     // tile rows
+    static constexpr int WN = 16 * NBW;    // columns per wave
+    static constexpr int BN = WAVES * WN;  // tile columns
+    static constexpr int NA = S.NA;        // DMA instructions per wave per K tile
     // vector-memory instructions of one B event: 2 NBW fragment loads plus scales
-    static constexpr int NB = kPtpc<MODE> ? 2 * NBW : 2 * NBW + 2 + 1;
+    static constexpr int NB = S.NB;
     // vector-memory instructions of the ptpc epilogue's scale loads (two
     // 1 KiB DMAs per wave)
-    static constexpr int NSC = kPtpc<MODE> ? 2 : 0;
+    static constexpr int NSC = S.NSC;
+    static_assert(NA == 2 * MB / WAVES && NB == (kPtpc<MODE> ? 2 * NBW : 2 * NBW + 3) && NSC == (kPtpc<MODE> ? 2 : 0),
+                  "the counts kpipe.h gives the mode are the loads the kernel issues");
     static_assert(2 * NB + NA <= 63, "vmcnt range");
 };
 
 // Whether a tile's epilogue is deferred into the next tile's first K step
-// (modes whose accumulators live in AGPRs).
+// (the 256 x 256 tiles), and whether the accumulators are pinned to AGPRs
+// (those and the 256 x 128 mxfp8 tile: 128 accumulators per lane there, which
+// leave the VGPRs to the operands, so the compiler never has to move an
+// accumulator that an asm matrix op may still be writing).
 template <int MODE>
-constexpr bool kDeferEpilogue = !Cfg<MODE>::NARROW;
+constexpr bool kDeferEpilogue = Cfg<MODE>::NBW == 4;
+template <int MODE>
+constexpr bool kAgprAcc = kDeferEpilogue<MODE> || MODE == MODE_MXFP8_N;
 
 // Tile order of the persistent grid: tile_order.h (order::xcd_list, or
 // order::round_list with the gathered order).
@@ -287,7 +301,7 @@ __device__ __forceinline__ void b_scales(Ctx<MODE>& x, TileRef r, int kt) {
     using C = Cfg<MODE>;
     const bool valid = r.m0 >= 0;
     const int n0 = valid ? r.n0 : 0, m0 = valid ? r.m0 : 0;
-    if constexpr (MODE == MODE_MXFP8) {
+    if constexpr (kMx<MODE>) {
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x.sa, valid ? (uint32_t)(x.K / 32) * (uint32_t)x.M : 0u);
         const __amdgpu_buffer_rsrc_t rsb = make_rsrc(x.sb, valid ? (uint32_t)(x.K / 32) * (uint32_t)x.N : 0u);
         // A: 16 consecutive E8M0 bytes (rows 16i .. 16i+15 of the tile) of K
@@ -298,9 +312,10 @@ __device__ __forceinline__ void b_scales(Ctx<MODE>& x, TileRef r, int kt) {
         x.sxa[T] = __builtin_amdgcn_raw_buffer_load_b128(rsa, base, 0, 0);
         x.sxa_tail[T] = __builtin_amdgcn_raw_buffer_load_b32(rsa, base + 16, 0, 0);
         x.sxa_shift[T] = off & 3;
-        // B: lane (i, g) loads columns 4i .. 4i+3 of the wave's 64 for K
+        // B: lane (i, g) loads columns 4i .. 4i+3 of the wave's WN for K
         // group 4kt + g (one aligned dword; N is a multiple of 16); the bytes
         // are distributed across lanes when the step that uses them starts
+        // (with WN = 32, lanes i >= 8 load a neighbour's columns, unused)
         const int boff = (4 * kt + x.g) * x.N + n0 + C::WN * x.w + 4 * x.i;
         x.sxb_raw[T] = __builtin_amdgcn_raw_buffer_load_b32(rsb, boff, 0, 0);
     } else if constexpr (MODE == MODE_BLOCKSCALE) {
@@ -440,17 +455,19 @@ template <int MODE, int T, int mb, int nb, bool FIRST>
 __device__ __forceinline__ void mfma_block(Ctx<MODE>& x, const v8i& a) {
     if constexpr (kWidePtpc<MODE>) {
         mfma_acc<FIRST>(x.acc[mb][nb], x.bq[T][nb], a);
-    } else {
-        static_assert(MODE == MODE_MXFP8, "blockscale issues its row blocks as a whole");
+    } else if constexpr (MODE == MODE_MXFP8) {
         // src1 (A) scale: byte mb % 4 of word mb / 4 of the realigned bytes;
         // src0 (B) scale: byte 0 of the block's register
+        mfma_scaled_acc<FIRST, 0, mb % 4>(x.acc[mb][nb], x.bq[T][nb], a, x.sxb[nb], x.sxa[T][mb / 4]);
+    } else {
+        static_assert(MODE == MODE_MXFP8_N, "blockscale issues its row blocks as a whole");
         mfma_scaled_acc<FIRST, 0, mb % 4>(x.acc[mb][nb], x.bq[T][nb], a, x.sxb[nb], x.sxa[T][mb / 4]);
     }
 }
 
 template <int MODE, int T, int mb, bool FIRST>
 __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
-    if constexpr (kWidePtpc<MODE> || MODE == MODE_MXFP8) {
+    if constexpr (kWidePtpc<MODE> || kMx<MODE>) {
         static_for<0, Cfg<MODE>::NBW>([&](auto NBc) { mfma_block<MODE, T, mb, decltype(NBc)::value, FIRST>(x, a); });
     } else if constexpr (MODE == MODE_PTPC_N) {
         // each accumulator is rewritten once per K tile, 2 MB - 1 matrix ops
@@ -486,7 +503,7 @@ __device__ __forceinline__ void mfma_drain(Ctx<MODE>& x) {
         for (int mb = 0; mb < Cfg<MODE>::MB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < Cfg<MODE>::NBW; ++nb) {
-                if constexpr (kDeferEpilogue<MODE>) asm volatile("" : "+a"(x.acc[mb][nb]));
+                if constexpr (kAgprAcc<MODE>) asm volatile("" : "+a"(x.acc[mb][nb]));
                 else asm volatile("" : "+v"(x.acc[mb][nb]));
             }
     }
@@ -511,7 +528,7 @@ __device__ __forceinline__ int row_gather4(int src) {
 // crossbar permute would cost matrix time).
 template <int MODE, int T>
 __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
-    if constexpr (MODE == MODE_MXFP8) {
+    if constexpr (kMx<MODE>) {
         const int sh = x.sxa_shift[T];
         if (sh) {
             const v4i w = x.sxa[T];
@@ -812,13 +829,19 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, Step
         constexpr int SR = (S + 3) & 3;  // stage refilled by this step (tile k-1's)
         constexpr int SN = (S + 1) & 3;  // stage of the next K tile
         constexpr int HALF = C::MB / 2;
-        constexpr int BPR = 2 * C::NBW / HALF;  // B fragment loads per row block
-        static_assert((BPR == 1 || BPR == 2) && BPR * HALF == 2 * C::NBW,
+        // the 2 NBW B fragment loads of the event, spread over the first
+        // half: BPR per row block, or one per BSTRIDE row blocks
+        constexpr int NBL = 2 * C::NBW;
+        constexpr int BPR = NBL >= HALF ? NBL / HALF : 1;
+        constexpr int BSTRIDE = NBL >= HALF ? 1 : HALF / NBL;
+        static_assert((BPR == 1 || BPR == 2) && BPR * HALF == NBL * BSTRIDE,
                       "every B fragment load of the event, spread over the first half");
         constexpr int nxt = mb + 2;
         if constexpr (mb < HALF) {
-            b_piece<MODE, T ^ 1, mb * BPR>(x, L.rb, L.bbase);
-            if constexpr (BPR == 2) b_piece<MODE, T ^ 1, mb * BPR + 1>(x, L.rb, L.bbase);
+            if constexpr (mb % BSTRIDE == 0) {
+                b_piece<MODE, T ^ 1, mb / BSTRIDE * BPR>(x, L.rb, L.bbase);
+                if constexpr (BPR == 2) b_piece<MODE, T ^ 1, mb * BPR + 1>(x, L.rb, L.bbase);
+            }
             if constexpr (mb == HALF - 1) {
                 b_scales<MODE, T ^ 1>(x, L.bref, L.bkt);
                 if constexpr (FIRST && LAST) issue_epilogue_scales<MODE>(x, cur);
@@ -1110,14 +1133,34 @@ static hipError_t launch_gemm(const GemmArgs& base, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// ptpc tile choice: the 256 x 256 tile moves the fewest bytes per matrix op
-// and wins wherever it fills the chip.  When it would leave at least half
-// the CUs idle, the 128 x 256 tile of eight waves puts twice as many CUs to
-// work (each narrow tile runs at about 0.8 of the wide tile's rate, so the
-// trade pays only there).
+// Tile choice.  The persistent grid gives each CU ceil(T / CUs) tiles at
+// most, so a launch takes about ceil(T / CUs) tile times.  The 256 x 256 tile
+// moves the fewest bytes per matrix op; a half-size tile (128 x 256 for
+// ptpc, 256 x 128 for mxfp8) takes `half_cost` of a wide tile's time (more
+// than one half: it reads the same LDS fragments for half the matrix ops).
+// The half tile is chosen when its waves cost less, which happens where the
+// wide grid leaves many CUs idle in its last wave (at most half the CUs
+// busy, or a last wave well short of full).
+static bool half_tile_wins(long wide_tiles, long half_tiles, double half_cost) {
+    const long cus = device_cus();
+    const long wide_waves = (wide_tiles + cus - 1) / cus, half_waves = (half_tiles + cus - 1) / cus;
+    return (double)half_waves * half_cost < (double)wide_waves;
+}
+
+// ptpc: the 128 x 256 tile of eight waves runs at about 0.8 of the wide
+// tile's rate per matrix op (measured), so it costs 0.625 of a wide tile.
 int ptpc_tile_for(int m, int n) {
     const long wide = (long)((m + 255) / 256) * ((n + 255) / 256);
-    return 2 * wide <= device_cus() ? 2 : 1;
+    const long half = (long)((m + 127) / 128) * ((n + 255) / 256);
+    return half_tile_wins(wide, half, 0.625) ? 2 : 1;
+}
+
+// mxfp8: the 256 x 128 tile of four waves.
+constexpr double kMxfp8HalfCost = 0.625;
+int mxfp8_tile_for(int m, int n) {
+    const long wide = (long)((m + 255) / 256) * ((n + 255) / 256);
+    const long half = (long)((m + 255) / 256) * ((n + 127) / 128);
+    return half_tile_wins(wide, half, kMxfp8HalfCost) ? 2 : 1;
 }
 
 hipError_t launch_gemm_a8w8(int mode, int tile, const uint8_t* a, const uint8_t* b, const void* sa, const void* sb,
@@ -1126,7 +1169,9 @@ hipError_t launch_gemm_a8w8(int mode, int tile, const uint8_t* a, const uint8_t*
     if (mode == MODE_PTPC && (tile == 0 ? ptpc_tile_for(m, n) : tile) == 2) mode = MODE_PTPC_N;
     if (mode == MODE_PTPC) return launch_gemm<MODE_PTPC>(p, stream);
     if (mode == MODE_PTPC_N) return launch_gemm<MODE_PTPC_N>(p, stream);
+    if (mode == MODE_MXFP8 && (tile == 0 ? mxfp8_tile_for(m, n) : tile) == 2) mode = MODE_MXFP8_N;
     if (mode == MODE_MXFP8) return launch_gemm<MODE_MXFP8>(p, stream);
+    if (mode == MODE_MXFP8_N) return launch_gemm<MODE_MXFP8_N>(p, stream);
     return launch_gemm<MODE_BLOCKSCALE>(p, stream);
 }
 

@@ -118,8 +118,10 @@ dmm_status gemm_a8w8_ptpc(const uint8_t* a, const uint8_t* b_shuf, const float* 
 
 /* ptpc with an explicit output-tile shape, the same result as
  * gemm_a8w8_ptpc: tile 1 = 256 x 256 (four waves), 2 = 128 x 256 (eight
- * waves), 0 = the choice gemm_a8w8_ptpc makes (128 x 256 when the problem
- * has at most one 256 x 256 tile per two compute units).  The pages size the
+ * waves), 0 = the choice gemm_a8w8_ptpc makes (128 x 256 when its waves
+ * over the compute units cost less than the 256 x 256 tile's: each costs
+ * 0.625 of a wide tile, so e.g. when the wide grid would leave at least
+ * half the compute units idle).  The pages size the
  * tile to the problem in the same spirit (mori PR 785, Cost: the table's
  * shapes; aiter PR 6539, Motivation and its review thread: the tuned rows,
  * one kernel configuration per shape).  Other values of tile return
@@ -166,6 +168,19 @@ dmm_status gemm_a8w8_blockscale(const uint8_t* a, const uint8_t* b_shuf, const f
  * Scale byte 255 (NaN) is outside the contract. */
 dmm_status gemm_a8w8_mxfp8(const uint8_t* a, const uint8_t* b_shuf, const uint8_t* a_scale,
                            const uint8_t* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream);
+
+/* mxfp8 with an explicit output-tile shape, the same result as
+ * gemm_a8w8_mxfp8: tile 1 = 256 x 256, 2 = 256 x 128 (four waves, each
+ * owning all 256 rows and 32 columns: the A tile that goes through LDS is
+ * twice the B tile -- the narrow mxfp8 shape whose A side outgrows its B
+ * side, mori PR 785, review thread), 0 = the choice gemm_a8w8_mxfp8 makes (256 x 128 when its
+ * waves over the compute units cost less than the 256 x 256 tile's, e.g.
+ * when the wide grid leaves most CUs idle).  The same choice rule picks
+ * between gemm_a8w8_ptpc's two tiles.  Other values of tile return
+ * DMM_EINVAL. */
+dmm_status gemm_a8w8_mxfp8_tile(const uint8_t* a, const uint8_t* b_shuf, const uint8_t* a_scale,
+                                const uint8_t* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k, int tile,
+                                void* stream);
 
 /* bf16 GEMM with fp32 accumulation (DeepGEMM PR 453, "Fix SM120 BF16 GEMM
  * shared-memory reuse ordering", Reproduction and validation: [4096, 1024]

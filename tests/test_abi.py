@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("quantize_per_token", "quantize_per_token_bf16", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_ptpc_gathered",
               "gemm_a8w8_blockscale",
-              "gemm_a8w8_mxfp8",
+              "gemm_a8w8_mxfp8", "gemm_a8w8_mxfp8_tile",
               "gemm_bf16", "gemm_bf16_tile", "quantize_blockscale_a", "quantize_blockscale_b", "quantize_mxfp8", "dmm_status_str",
               "dmm_last_error"):
         assert f in names, f

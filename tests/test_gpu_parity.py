@@ -151,18 +151,22 @@ def test_preshuffle_is_the_documented_permutation(dmm, n, k):
 # ptpc runs on two tile shapes; "ptpc" is the library's own choice, the
 # other two force one shape (same data, same oracle).
 PTPC_TILE = {"ptpc": "auto", "ptpc_w": "256x256", "ptpc_n": "128x256"}
+# mxfp8 likewise: "mxfp8" forces the 256x256 tile, "mxfp8_n" the 256x128 one
+MXFP8_TILE = {"mxfp8": "256x256", "mxfp8_n": "256x128", "mxfp8_auto": "auto"}
 MODE_ID = {"ptpc": 0, "blockscale": 1, "mxfp8": 2}
-GEMM_MODES = ["ptpc_w", "ptpc_n", "blockscale", "mxfp8"]
+GEMM_MODES = ["ptpc_w", "ptpc_n", "blockscale", "mxfp8", "mxfp8_n"]
 
 
 def base_mode(mode):
-    return "ptpc" if mode in PTPC_TILE else mode
+    return "ptpc" if mode in PTPC_TILE else "mxfp8" if mode in MXFP8_TILE else mode
 
 
 def gemm_fn(dmm, mode):
     if mode in PTPC_TILE:
         return lambda *args, **kw: dmm.gemm_a8w8_ptpc(*args, tile=PTPC_TILE[mode], **kw)
-    return {"blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
+    if mode in MXFP8_TILE:
+        return lambda *args, **kw: dmm.gemm_a8w8_mxfp8(*args, tile=MXFP8_TILE[mode], **kw)
+    return dmm.gemm_a8w8_blockscale
 
 
 def tile_rows(mode):
@@ -266,26 +270,26 @@ def run_poisoned(dmm, mode, qa, qb, sa, sb, launches, hog=False):
     return outs
 
 
-@pytest.mark.parametrize("mode", ["ptpc", "ptpc_w", "ptpc_n"])
+@pytest.mark.parametrize("mode", ["ptpc", "ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale"])
 @pytest.mark.parametrize("m,n,k,seed_a,seed_b", [(4096, 7168, 256, 11, 12), (16384, 7168, 512, 21, 22)])
 def test_race_shapes_bit_stable_and_correct(dmm, mode, m, n, k, seed_a, seed_b):
-    """The pages' race shapes (mori PR 785, Test table): 20 launches into a
-    NaN-poisoned C must be bitwise identical, leave no NaN, and match the
-    oracle on sampled rows (every row of the first and last 256-row tiles
-    plus one per 64-row band)."""
+    """The pages' race shapes (mori PR 785, Test table), in every mode and
+    tile shape: 20 launches into a NaN-poisoned C must be bitwise identical,
+    leave no NaN, and match the oracle on sampled rows (every row of the
+    first and last 256-row tiles plus one per 64-row band)."""
     announce("race", mode, m, n, k)
-    qa, qb, sa, sb = quantised_operands("ptpc", m, n, k, seed_a, seed_b)
+    qa, qb, sa, sb = quantised_operands(mode, m, n, k, seed_a, seed_b)
     outs = run_poisoned(dmm, mode, qa, qb, sa, sb, 20)
     for i, o in enumerate(outs[1:], 1):
         diff = np.count_nonzero(o != outs[0])
         assert diff == 0, f"launch {i} differs from launch 0 in {diff} elements"
     assert not np.isnan(bits_to_f64(outs[0])).any()
     rows = inputs.rows_sample(m, seed=m)
-    ref = oracle.gemm_ptpc(qa, qb, sa, sb, rows=rows)
-    check_close(outs[0][rows], ref, f"{mode} {m}x{n}x{k} sampled rows", "ptpc", (qa, qb, sa, sb), rows)
+    ref = oracle.gemm_a8w8(MODE_ID[base_mode(mode)], qa, qb, sa, sb, rows=rows)
+    check_close(outs[0][rows], ref, f"{mode} {m}x{n}x{k} sampled rows", base_mode(mode), (qa, qb, sa, sb), rows)
 
 
-@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "blockscale"])
+@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale"])
 def test_bit_stable_under_concurrent_copy(dmm, mode):
     """Same 20-launch identity with an HBM copy loop on a second stream."""
     m, n, k = 4096, 7168, 256
@@ -352,7 +356,7 @@ def test_invalid_arguments_raise_value_error(dmm):
                            torch.ones(16, dtype=torch.float32, device=DEV))
 
 
-@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "blockscale"])
+@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale"])
 @pytest.mark.parametrize("k", [128, 256, 384, 512, 640])
 def test_many_tiles_per_workgroup_every_k_phase(dmm, mode, k):
     """More tiles than CUs, so every workgroup runs 2-3 tiles back to back,

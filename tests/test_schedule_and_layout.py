@@ -46,6 +46,11 @@ int dma_row(int b, int l, int MB) { return lds::dma_row(b, l, MB); }
 int dma_chunk(int b, int l, int MB) { return lds::dma_chunk(b, l, MB); }
 int frag_byte(int i, int g, int mb, int half, int MB) { return lds::frag_byte(i, g, mb, half, MB); }
 int bf16_chunk_pos(int r, int c) { return lds::bf16_chunk_pos(r, c); }
+int shape_field(int mode, int f) {
+    const sched::Shape sh = sched::shape_of(mode);
+    const int v[6] = {sh.MB, sh.NBW, sh.WAVES, sh.NA, sh.NB, sh.NSC};
+    return v[f];
+}
 }
 """
 
@@ -59,13 +64,41 @@ def shim(tmp_path_factory):
     subprocess.run(["g++", "-std=c++17", "-O1", "-shared", "-fPIC", "-I", CSRC, str(src), "-o", str(lib)], check=True)
     L = ctypes.CDLL(str(lib))
     for f in ("prologue_wait", "wait_at", "stage_of", "refill_stage", "dma_lds_byte", "dma_row", "dma_chunk",
-              "frag_byte", "dma_ahead_tile", "dma_ahead_kt", "case_of", "phase_advance", "bf16_chunk_pos"):
+              "frag_byte", "dma_ahead_tile", "dma_ahead_kt", "case_of", "phase_advance", "bf16_chunk_pos",
+              "shape_field"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
 
 # ---------------------------------------------------------------- schedule
-MODES = {"ptpc": (8, 8, 2), "mxfp8": (8, 11, 0), "blockscale": (2, 7, 0), "ptpc_128x256": (2, 4, 2)}  # NA, NB, NSC per wave
+# the kernel's modes (kpipe.h, shape_of): name -> mode id
+MODE_IDS = {"ptpc": 0, "blockscale": 1, "mxfp8": 2, "ptpc_128x256": 3, "ptpc_gathered": 4, "mxfp8_256x128": 5}
+
+
+def _shapes():
+    """NA, NB, NSC per wave for every mode, read from kpipe.h through the
+    shim (the numbers the kernel's waits are built from)."""
+    import tempfile
+
+    d = tempfile.mkdtemp()
+    src = os.path.join(d, "shim.cpp")
+    open(src, "w").write(SHIM)
+    lib = os.path.join(d, "libshim.so")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-shared", "-fPIC", "-I", CSRC, src, "-o", lib], check=True)
+    L = ctypes.CDLL(lib)
+    L.shape_field.restype = ctypes.c_int
+    return {name: tuple(L.shape_field(mid, f) for f in (3, 4, 5)) for name, mid in MODE_IDS.items()}
+
+
+MODES = _shapes()  # NA, NB, NSC per wave
+
+
+def test_mode_shapes_are_the_documented_loads():
+    """The counts the proof runs on, as kpipe.h states them: per K tile NA
+    = 2 MB / waves A DMAs and NB = 2 NBW B fragment halves (+ 3 scale loads
+    for mxfp8 and blockscale); the ptpc tiles add 2 epilogue-scale DMAs."""
+    assert MODES == {"ptpc": (8, 8, 2), "blockscale": (2, 7, 0), "mxfp8": (8, 11, 0), "ptpc_128x256": (2, 4, 2),
+                     "ptpc_gathered": (8, 8, 2), "mxfp8_256x128": (8, 7, 0)}
 
 
 def program(L, KI, ntiles, NA, NB, NSC, wait_fn=None):

@@ -35,6 +35,8 @@ compared with the GPU output of the timed run under the acceptance rule of
 oracle.tolerance and the statistics are reported as cpu_baseline.parity.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra] [--calibrate]
+       python bench.py --workload NAME [--steps K] [--warmup W]   (one workload, eager
+           launches, for profilers; NAME from dense_matmul_amd.inputs.WORKLOADS)
 """
 import argparse
 import ctypes
@@ -72,6 +74,9 @@ def parse():
                    help="also time every variant of the matrix-op calibration kernel (what each kind of "
                         "instruction interleaved with the matrix ops costs)")
     p.add_argument("--no-ceiling", action="store_true", help="skip the calibration-kernel context")
+    p.add_argument("--workload", default=None,
+                   help="run only this workload (a key of dense_matmul_amd.inputs.WORKLOADS): --warmup then "
+                        "--steps eager launches, one short JSON line; for rocprofv3")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 1 GiB HBM copy kernel 3 times (the reference dispatch for "
                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -416,9 +421,12 @@ def main():
     import dense_matmul_amd as dmm
 
     dmm.lib()
-    device = device_record()
     if args.copy_calibration:
         copy_calibration(torch)
+    if args.workload:
+        run_workload(dmm, torch, args.workload, args.steps, args.warmup)
+        return
+    device = device_record()
     m, n, k = 32768, 7168, 1792
     flops = 2.0 * m * n * k
     qa, bs, sa, sb, qb = headline_operands(dmm, torch, m, n, k, 31, 32, keep_b=True)
@@ -485,6 +493,32 @@ def main():
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(m, n, k, args.cpu_rows, gpu_c)
     print(json.dumps(rec), flush=True)
+
+
+def run_workload(dmm, torch, name, steps, warmup):
+    """One named workload: operands as the bench builds them, ``warmup``
+    launches, then ``steps`` launches, eagerly on the current stream (so a
+    profiler sees each dispatch), then a synchronisation."""
+    from dense_matmul_amd import inputs
+
+    mode, m, n, k, seed_a, seed_b = inputs.WORKLOADS[name]
+    if mode == "bf16":
+        a32, b_kn = inputs.bf16_operands(m, k, n, seed_a)
+        a = torch.from_numpy(a32).to(torch.bfloat16).to("cuda:0")
+        b = torch.from_numpy(b_kn.T.copy()).to(torch.bfloat16).to("cuda:0")
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+        fn = lambda: dmm.gemm_bf16(a, b, out=out)
+    else:
+        qa, bs, sa, sb = headline_operands(dmm, torch, m, n, k, seed_a, seed_b, mode)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+        g = {"ptpc": dmm.gemm_a8w8_ptpc, "blockscale": dmm.gemm_a8w8_blockscale, "mxfp8": dmm.gemm_a8w8_mxfp8}[mode]
+        fn = lambda: g(qa, bs, sa, sb, out=out)
+    repeat(fn, warmup)
+    torch.cuda.synchronize()
+    ms = event_ms(lambda: repeat(fn, steps), steps)
+    print(json.dumps({"workload": name, "mode": mode, "m": m, "n": n, "k": k, "launches": steps,
+                      "us_per_launch": round(ms * 1e3, 2), "TFLOP/s": round(2.0 * m * n * k / (ms * 1e-3) / 1e12, 1)}),
+          flush=True)
 
 
 def extra_shapes(dmm, torch, args):

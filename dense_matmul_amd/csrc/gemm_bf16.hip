@@ -6,20 +6,35 @@
 // BM x BN output tile per 256-thread workgroup, 2 x 2 waves of BM/2 x BN/2.
 // Both operands stream global -> LDS by direct-to-LDS buffer loads into an
 // NS-stage ring of separate arrays (K tile 64 = 128 B per row, 16-byte chunks
-// placed by lds::bf16_chunk_pos, conflict-free for the fragment reads),
-// refilled NS - 1 K tiles ahead;
+// placed by lds::bf16_chunk_pos, conflict-free for the fragment reads);
 // v_mfma_f32_16x16x32_bf16 with src0 = B rows (output columns) and src1 =
 // A rows (output rows), so each lane ends with 4 consecutive output columns
-// of one row.  The stage written by a refill was last read one step
-// earlier; the barrier that ends that step (after lgkmcnt(0)) orders the
-// reads before the refill, and the wait before it (vmcnt) makes the next
-// stage complete in every wave before anyone reads it.
+// of one row.
+//
+// K step kt (stage S = kt % NS) splits at its middle: the fragments of its
+// first 32-wide k-half are already in registers (read during the previous
+// step), its second k-half's are read while the first half's matrix ops
+// run; then one wait (vmcnt: this wave's DMAs of K tile kt+1 have landed;
+// lgkmcnt(0): its reads of stage S have retired) and a barrier (every wave
+// has done both); then stage S itself is refilled with K tile kt + NS, and
+// the next stage's first k-half is read while the second half's matrix ops
+// run.  So each K tile is loaded NS steps ahead, no wave ever waits on an LDS
+// read right after the barrier, and NS - 2 K tiles stay in flight behind the
+// one each wait covers.
 //
 // Two tile sizes: 128 x 128 with 4 stages (one workgroup per CU, 128 KiB of
 // LDS) in general, and 64 x 64 with 3 stages (48 KiB, three workgroups per
 // CU) for grids too small to occupy half the CUs with 128 x 128 tiles.
+//
+// One workgroup per tile, placed XCD-aware (tile_order.h): workgroup b runs
+// on XCD b % 8, and the tiles of one XCD are a contiguous run of the order
+// in which groups of four row tiles sweep the column tiles, so an XCD's L2
+// holds only its own rows of A (and B) instead of every XCD fetching nearly
+// all of A.
 #include "common.h"
+#include "kpipe.h"
 #include "lds_layout.h"
+#include "tile_order.h"
 
 #include <type_traits>
 
@@ -88,43 +103,42 @@ __device__ __forceinline__ void read_frags(const Ctx<BM, BN>& x, bf8 (&af)[Cfg<B
     for (int q = 0; q < C::NBW; ++q) bfr[q] = *(lds_bf8*)(x.lds.b[S] + ((BN / 2) * x.wn + 16 * q) * 128 + x.rd[KK]);
 }
 
-// The two 32-wide k-halves of stage S: the second half's fragments are read
-// while the first half's matrix ops run.
-template <int BM, int BN, int S>
-__device__ __forceinline__ void compute(Ctx<BM, BN>& x) {
+template <int BM, int BN>
+struct Frags {
+    bf8 a[Cfg<BM, BN>::MBW], b[Cfg<BM, BN>::NBW];
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void mfmas(Ctx<BM, BN>& x, const Frags<BM, BN>& f) {
     using C = Cfg<BM, BN>;
-    bf8 a0[C::MBW], b0[C::NBW], a1[C::MBW], b1[C::NBW];
-    read_frags<BM, BN, S, 0>(x, a0, b0);
-    read_frags<BM, BN, S, 1>(x, a1, b1);
 #pragma unroll
     for (int mb = 0; mb < C::MBW; ++mb)
 #pragma unroll
         for (int nb = 0; nb < C::NBW; ++nb)
-            x.acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[nb], a0[mb], x.acc[mb][nb], 0, 0, 0);
-#pragma unroll
-    for (int mb = 0; mb < C::MBW; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < C::NBW; ++nb)
-            x.acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[nb], a1[mb], x.acc[mb][nb], 0, 0, 0);
+            x.acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[nb], f.a[mb], x.acc[mb][nb], 0, 0, 0);
 }
 
-// Step kt computes stage S = kt % NS and refills stage (kt + NS - 1) % NS
-// (the one step kt - 1 read).
+// Step kt (stage S); h0 holds its first k-half's fragments on entry and the
+// next step's on exit.
 template <int BM, int BN, int S>
-__device__ __forceinline__ void step(Ctx<BM, BN>& x, int kt) {
+__device__ __forceinline__ void step(Ctx<BM, BN>& x, int kt, Frags<BM, BN>& h0) {
     using C = Cfg<BM, BN>;
     constexpr int NS = C::NS;
-    issue<BM, BN, (S + NS - 1) % NS>(x, kt + NS - 1);
-    compute<BM, BN, S>(x);
-    // tile kt+1 was followed by the NS - 2 later tiles' loads
-    wait_vm_lgkm0<(NS - 2) * (C::NLA + C::NLB)>();
+    Frags<BM, BN> h1;
+    read_frags<BM, BN, S, 1>(x, h1.a, h1.b);
+    mfmas<BM, BN>(x, h0);
+    // K tile kt+1 was followed by the DMAs of K tiles kt+2 .. kt+NS-1
+    wait_vm_lgkm0<sched::bf16_mid_wait(NS, C::NLA + C::NLB)>();
     __builtin_amdgcn_s_barrier();
+    issue<BM, BN, S>(x, kt + NS);
+    read_frags<BM, BN, (S + 1) % NS, 0>(x, h0.a, h0.b);
+    mfmas<BM, BN>(x, h1);
 }
 }  // namespace bf16k
 
 template <int BM, int BN>
 __global__ void __launch_bounds__(bf16k::NT) gemm_bf16_kernel(const uint16_t* a, const uint16_t* b, uint16_t* c, int m,
-                                                              int n, int k, int tiles_n) {
+                                                              int n, int k, int tiles_m, int tiles_n) {
     using namespace bf16k;
     using C = Cfg<BM, BN>;
     constexpr int NS = C::NS;
@@ -133,7 +147,9 @@ __global__ void __launch_bounds__(bf16k::NT) gemm_bf16_kernel(const uint16_t* a,
     Ctx<BM, BN> x;
     x.lds = Ring{{(lds_char*)a0, (lds_char*)a1, (lds_char*)a2, (lds_char*)a3},
                  {(lds_char*)b0, (lds_char*)b1, (lds_char*)b2, (lds_char*)b3}};
-    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    // the grid has one workgroup per tile: each list holds one position
+    int tm, tn;
+    order::coords(order::xcd_list(blockIdx.x, gridDim.x, tiles_m * tiles_n).first, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int w = wave_id();
     x.lane = lane_id();
@@ -167,18 +183,22 @@ __global__ void __launch_bounds__(bf16k::NT) gemm_bf16_kernel(const uint16_t* a,
 #pragma unroll
         for (int nb = 0; nb < C::NBW; ++nb) x.acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    // prologue: tiles 0 .. NS-2; wait for tile 0
+    // prologue: K tiles 0 .. NS-1 into stages 0 .. NS-1; wait for tile 0
+    // (followed by NS - 1 tiles' DMAs); the first k-half of tile 0
     issue<BM, BN, 0>(x, 0);
     issue<BM, BN, 1>(x, 1);
-    if constexpr (NS == 4) issue<BM, BN, 2>(x, 2);
-    wait_vm_lgkm0<(NS - 2) * (C::NLA + C::NLB)>();
+    issue<BM, BN, 2>(x, 2);
+    if constexpr (NS == 4) issue<BM, BN, 3>(x, 3);
+    wait_vm_lgkm0<sched::bf16_prologue_wait(NS, C::NLA + C::NLB)>();
     __builtin_amdgcn_s_barrier();
+    Frags<BM, BN> h0;
+    read_frags<BM, BN, 0, 0>(x, h0.a, h0.b);
     for (int kt = 0; kt < x.KT; kt += NS) {
-        step<BM, BN, 0>(x, kt);
-        if (kt + 1 < x.KT) step<BM, BN, 1>(x, kt + 1);
-        if (kt + 2 < x.KT) step<BM, BN, 2>(x, kt + 2);
+        step<BM, BN, 0>(x, kt, h0);
+        if (kt + 1 < x.KT) step<BM, BN, 1>(x, kt + 1, h0);
+        if (kt + 2 < x.KT) step<BM, BN, 2>(x, kt + 2, h0);
         if constexpr (NS == 4)
-            if (kt + 3 < x.KT) step<BM, BN, 3>(x, kt + 3);
+            if (kt + 3 < x.KT) step<BM, BN, 3>(x, kt + 3, h0);
     }
 
     // lane (i, g), block (mb, nb): row m0 + BM/2 wm + 16 mb + i, columns
@@ -203,7 +223,7 @@ template <int BM, int BN>
 static hipError_t launch_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int m, int n, int k, hipStream_t st) {
     const int tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN>), dim3(tiles_m * tiles_n), dim3(bf16k::NT), 0, st, a, b, c, m, n, k,
-                       tiles_n);
+                       tiles_m, tiles_n);
     return hipGetLastError();
 }
 

@@ -114,5 +114,18 @@ constexpr int phase_advance(int CASE) { return CASE == 4 ? 1 : CASE; }
 constexpr int stage_of(int j) { return j % kStages; }
 constexpr int refill_stage(int s) { return (s + 3) % kStages; }
 
+// The bf16 GEMM (gemm_bf16.hip) runs a simpler ring: NS stages, one output
+// tile per workgroup, NL DMAs per wave per K tile (A and B both through LDS).
+//   prologue: D(0) .. D(NS-1) into stages 0 .. NS-1;
+//             wait vmcnt(bf16_prologue_wait) lgkmcnt(0); s_barrier; R(0, half 0)
+//   step kt : R(kt, half 1); wait vmcnt(bf16_mid_wait) lgkmcnt(0); s_barrier;
+//             D(kt + NS) into stage kt % NS; R(kt + 1, half 0)
+// D(j) past the last K tile goes through an empty descriptor (counted, no
+// data).  The prologue wait covers D(0) (NS - 1 tiles' DMAs after it); the
+// mid wait of step kt covers D(kt + 1), after which D(kt + 2) .. D(kt + NS -
+// 1) were issued.
+constexpr int bf16_prologue_wait(int NS, int NL) { return cap((NS - 1) * NL); }
+constexpr int bf16_mid_wait(int NS, int NL) { return cap((NS - 2) * NL); }
+
 }  // namespace sched
 }  // namespace dmm

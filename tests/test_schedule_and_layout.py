@@ -46,6 +46,8 @@ int dma_row(int b, int l, int MB) { return lds::dma_row(b, l, MB); }
 int dma_chunk(int b, int l, int MB) { return lds::dma_chunk(b, l, MB); }
 int frag_byte(int i, int g, int mb, int half, int MB) { return lds::frag_byte(i, g, mb, half, MB); }
 int bf16_chunk_pos(int r, int c) { return lds::bf16_chunk_pos(r, c); }
+int bf16_prologue_wait(int NS, int NL) { return sched::bf16_prologue_wait(NS, NL); }
+int bf16_mid_wait(int NS, int NL) { return sched::bf16_mid_wait(NS, NL); }
 int shape_field(int mode, int f) {
     const sched::Shape sh = sched::shape_of(mode);
     const int v[6] = {sh.MB, sh.NBW, sh.WAVES, sh.NA, sh.NB, sh.NSC};
@@ -65,7 +67,7 @@ def shim(tmp_path_factory):
     L = ctypes.CDLL(str(lib))
     for f in ("prologue_wait", "wait_at", "stage_of", "refill_stage", "dma_lds_byte", "dma_row", "dma_chunk",
               "frag_byte", "dma_ahead_tile", "dma_ahead_kt", "case_of", "phase_advance", "bf16_chunk_pos",
-              "shape_field"):
+              "shape_field", "bf16_prologue_wait", "bf16_mid_wait"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -341,3 +343,84 @@ def test_bf16_old_swizzle_would_conflict():
     check above would reject it."""
     groups = {(i * 128 + ((0 ^ (i & 7)) * 16)) // 16 % 16 for i in range(16)}
     assert len(groups) == 8
+
+
+# ------------------------------------------------------- the bf16 GEMM's ring
+BF16_RINGS = {"128x128": (4, 8), "64x64": (3, 4)}  # NS, NL (DMAs per wave per K tile) of each tile shape
+
+
+def program_bf16(L, KT, NS, NL, prologue=None, mid=None, refill_before_barrier=False):
+    """One wave's events in the bf16 GEMM (kpipe.h, the bf16 ring): DMA j
+    writes stage j % NS; R(t) reads K tile t's stage."""
+    prologue = L.bf16_prologue_wait(NS, NL) if prologue is None else prologue
+    mid = L.bf16_mid_wait(NS, NL) if mid is None else mid
+    ev = [("load", "A", j, NL) for j in range(NS)]
+    ev += [("wait", prologue), ("barrier",), ("read", 0)]
+    for kt in range(KT):
+        ev.append(("read", kt))
+        if refill_before_barrier:
+            ev.append(("load", "A", kt + NS, NL))
+        ev += [("wait", mid), ("barrier",)]
+        if not refill_before_barrier:
+            ev.append(("load", "A", kt + NS, NL))
+        ev.append(("read", kt + 1))
+    return ev
+
+
+def check_ring(ev, NS):
+    """RAW: a read of tile t follows a barrier whose waits (in every wave)
+    covered t's DMAs.  WAR: a DMA of tile j into stage j % NS comes after a
+    barrier that every wave passed with its reads of the stage's previous
+    tile (j - NS) retired (the lgkmcnt(0) in each wait)."""
+    bad, n_loads, last_instr, complete_upto, covered = [], 0, {}, 0, -1
+    unretired, retired_at_barrier = set(), set()
+    for e in ev:
+        if e[0] == "load":
+            _, _, j, n = e
+            if j - NS >= 0 and (j - NS) not in retired_at_barrier:
+                bad.append(f"DMA of tile {j} while tile {j - NS} may still be read")
+            n_loads += n
+            last_instr[j] = n_loads - 1
+        elif e[0] == "wait":
+            complete_upto = max(complete_upto, n_loads - e[1])
+        elif e[0] == "barrier":
+            covered = complete_upto
+            retired_at_barrier |= unretired
+            unretired = set()
+        elif e[0] == "read":
+            t = e[1]
+            if t not in last_instr or last_instr[t] >= covered:
+                bad.append(f"read of tile {t} before a barrier covering its DMA")
+            unretired.add(t)
+            retired_at_barrier.discard(t)
+    return bad
+
+
+@pytest.mark.parametrize("tile", sorted(BF16_RINGS))
+def test_bf16_ring_is_covered_for_every_k(shim, tile):
+    NS, NL = BF16_RINGS[tile]
+    for KT in range(1, 40):
+        assert check_ring(program_bf16(shim, KT, NS, NL), NS) == [], (tile, KT)
+
+
+def test_bf16_ring_counts_are_the_loosest_safe_ones(shim):
+    """One more outstanding DMA at either wait breaks coverage."""
+    for NS, NL in BF16_RINGS.values():
+        for KT in (1, 2, 5, 16):
+            assert check_ring(program_bf16(shim, KT, NS, NL, prologue=shim.bf16_prologue_wait(NS, NL) + 1), NS)
+            if KT >= 2:
+                assert check_ring(program_bf16(shim, KT, NS, NL, mid=shim.bf16_mid_wait(NS, NL) + 1), NS)
+
+
+def test_bf16_ring_catches_a_refill_before_the_barrier(shim):
+    for NS, NL in BF16_RINGS.values():
+        assert check_ring(program_bf16(shim, 8, NS, NL, refill_before_barrier=True), NS)
+
+
+def test_bf16_ring_shapes_match_the_kernel():
+    """NS and NL as gemm_bf16.hip derives them: 4 stages of a 128 x 128 tile
+    (A and B 16 KiB each per K tile of 64 = 8 KiB per wave), 3 of 64 x 64."""
+    src = open(os.path.join(CSRC, "gemm_bf16.hip")).read()
+    assert "static constexpr int NS = BM == 128 ? 4 : 3;" in src
+    for bm, (NS, NL) in ((128, BF16_RINGS["128x128"]), (64, BF16_RINGS["64x64"])):
+        assert NL == 2 * (bm * 64 * 2 // 1024 // 4)

@@ -52,7 +52,7 @@ def positions(L, fn, grid, T):
 
 
 @pytest.mark.parametrize("grid,T", [(256, 3584), (256, 448), (256, 3200), (100, 1000), (8, 8), (256, 40),
-                                    (13, 97), (256, 257)])
+                                    (13, 97), (256, 257), (224, 224), (896, 896), (1000, 1000)])
 @pytest.mark.parametrize("kind", ["xcd_list", "round_list"])
 def test_every_position_once(L, kind, grid, T):
     grid = min(grid, T)  # the launch never starts more workgroups than tiles

@@ -35,12 +35,14 @@
 //     past the end go through a zero-length buffer descriptor), so the
 //     counts never depend on K: the tail, K = 256 and K = 128 run the same
 //     rule as the middle of a long K loop.
-//   * Epilogue: permlane16 swaps (and, for 64-column waves, a DPP exchange)
-//     give each lane 8 consecutive columns, so the bf16 tile leaves in
-//     16-byte stores of whole 128-byte row segments; rows past M and
-//     16-column blocks past N fall outside the C descriptor and are dropped.
-//     ptpc and mxfp8 spread it over a tile's last K step and the next tile's
-//     first.
+//   * Epilogue: preshuffle_b orders B's rows within each group of 64 output
+//     columns (b_layout.h) so that every lane ends a row block with two runs
+//     of 8 adjacent columns: the bf16 tile leaves in 16-byte stores, four
+//     lanes covering 64 contiguous bytes of a row, with no lane exchange;
+//     rows past M and runs past N fall outside the C descriptor and are
+//     dropped.  ptpc and mxfp8 spread it over a tile's last K step and the
+//     next tile's first.
+#include "b_layout.h"
 #include "common.h"
 #include "kpipe.h"
 #include "lds_layout.h"
@@ -91,9 +93,8 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// DPP control of row_ror:8 (rotate each 16-lane row by 8 lanes) and the
-// cache-policy bits of a non-temporal store (nt).
-constexpr int kDppRowRor8 = 0x128;
+// DPP control of a row broadcast, and the cache-policy bits of a
+// non-temporal store (nt).
 constexpr int kDppRowNewBcast = 0x150;  // + k: lane k of each 16-lane row to the whole row
 constexpr int kStoreStream = 2;
 
@@ -178,11 +179,13 @@ struct TileRef {
 // What the epilogue of one tile needs besides the accumulators.
 struct Epi {
     v4f eas[4], ebs[4];  // ptpc: a_scale of this lane's rows, b_scale of its columns
-    int row;             // first row this lane writes
-    int col;             // column of this lane's 8 values
-    uint32_t cdrop;      // 0, or 2^31 when that column group lies at or past N: added to the
-                         // store offsets (all below 2^31), it puts them past the C descriptor,
-                         // so the hardware drops the stores without a branch
+    // byte offsets into C, for row block 0, of this lane's two 16-byte runs
+    // (columns 8g .. 8g + 7 of blocks 0-1, and of blocks 2-3, b_layout.h) and
+    // of its 8-byte run in a lone block; a run that does not exist carries
+    // 2^31 on top (all real offsets are below 2^31), which puts it past the C
+    // descriptor, so the hardware drops the store without a branch
+    uint32_t o16[2], o8;
+    int lone;  // the wave's group ends in a lone block among this wave's (uniform)
 };
 
 template <int MODE>
@@ -211,8 +214,9 @@ struct Ctx {
     v4i sxa[2];
     int sxa_tail[2];
     int sxa_shift[2];
-    int sxb_raw[2];      // B scale bytes of 4 columns as loaded
-    int sxb[C::NBW];     // B scale of this lane's column in each block (byte 0), current step
+    int sxb_raw[2];      // B scale bytes of 4 columns as loaded, per K tile
+    int sxb_lone[2];     // whether the B event's tile ends its wave's columns in a lone block (uniform)
+    int sxb[C::NBW];     // B scale of this lane's fragment row in each block (byte 0), current step
     // blockscale: A scales of this lane's MB rows and the wave's B block scale;
     // the products of the last two row blocks, before they are scaled in
     v4f sfa[2][C::MB / 4];
@@ -312,12 +316,17 @@ __device__ __forceinline__ void b_scales(Ctx<MODE>& x, TileRef r, int kt) {
         x.sxa[T] = __builtin_amdgcn_raw_buffer_load_b128(rsa, base, 0, 0);
         x.sxa_tail[T] = __builtin_amdgcn_raw_buffer_load_b32(rsa, base + 16, 0, 0);
         x.sxa_shift[T] = off & 3;
-        // B: lane (i, g) loads columns 4i .. 4i+3 of the wave's WN for K
-        // group 4kt + g (one aligned dword; N is a multiple of 16); the bytes
-        // are distributed across lanes when the step that uses them starts
+        // B: lane (i, g) loads the dword of columns 4i .. 4i+3 of the wave's
+        // WN for K group 4kt + g (N is a multiple of 16); the step that uses
+        // them hands each lane the bytes of the columns its fragment rows feed
         // (with WN = 32, lanes i >= 8 load a neighbour's columns, unused)
         const int boff = (4 * kt + x.g) * x.N + n0 + C::WN * x.w + 4 * x.i;
         x.sxb_raw[T] = __builtin_amdgcn_raw_buffer_load_b32(rsb, boff, 0, 0);
+        // a lone block: the last of a group with an odd block count, whose
+        // rows keep their order (b_layout.h); a wave's lone block is its
+        // block 0 or 2 (64-column waves) or its block 0 (32-column waves)
+        const int p = bl::group_blocks((n0 + C::WN * x.w) >> 6, x.N >> 4);
+        x.sxb_lone[T] = C::NBW == 4 ? (p & 1) * p : (2 * (x.w & 1) + 1 == p);
     } else if constexpr (MODE == MODE_BLOCKSCALE) {
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x.sa, valid ? (uint32_t)x.KI * (uint32_t)x.M * 4u : 0u);
         const __amdgpu_buffer_rsrc_t rsb =
@@ -509,23 +518,26 @@ __device__ __forceinline__ void mfma_drain(Ctx<MODE>& x) {
     }
 }
 
-// Within each 16-lane row, lane 4b + j (bank b) receives the value of lane
-// 4 NB + b: four row broadcasts, each written to one bank of four lanes.
-template <int NB>
+// Within each 16-lane row, lane 4q + t (bank q) receives the value of lane
+// src(q): four row broadcasts, each written to one bank of four lanes.
+template <int S0, int S1, int S2, int S3>
 __device__ __forceinline__ int row_gather4(int src) {
     int x = 0;
-    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + 4 * NB + 0, 0xF, 0x1, false);
-    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + 4 * NB + 1, 0xF, 0x2, false);
-    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + 4 * NB + 2, 0xF, 0x4, false);
-    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + 4 * NB + 3, 0xF, 0x8, false);
+    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + S0, 0xF, 0x1, false);
+    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + S1, 0xF, 0x2, false);
+    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + S2, 0xF, 0x4, false);
+    x = __builtin_amdgcn_update_dpp(x, src, kDppRowNewBcast + S3, 0xF, 0x8, false);
     return x;
 }
 
 // Start of a step's mxfp8 scales: realign the 20 loaded A-scale bytes so word
 // q holds the bytes of rows 4q..4q+3, and give lane (i, g) the B-scale byte
-// of column 16 nb + i of each block, which lane (4 nb + i / 4, g) loaded as
-// byte i % 4 of its dword (DPP row broadcasts: vector ops, where an LDS
-// crossbar permute would cost matrix time).
+// of the column its fragment row i feeds in each block (b_layout.h), which
+// lane (src, g) loaded as byte i % 4 of its dword: for the wave's block j and
+// bank q = i / 4, src = 8 (j / 2) + 2q + j % 2 (a paired block: columns
+// 8q .. 8q + 7 and 32 + 8q .. of the wave's), or 4j + q (a lone block:
+// columns 16 j + 4q ..).  DPP row broadcasts: vector ops, where an LDS
+// crossbar permute would cost matrix time.
 template <int MODE, int T>
 __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
     if constexpr (kMx<MODE>) {
@@ -538,21 +550,31 @@ __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
                              (int)__builtin_amdgcn_alignbyte(w[3], w[2], sh), (int)__builtin_amdgcn_alignbyte(t, w[3], sh)};
         }
         const int byte = 8 * (x.i & 3);
-        static_for<0, Cfg<MODE>::NBW>([&](auto NBc) {
-            constexpr int nb = decltype(NBc)::value;
-            x.sxb[nb] = (int)((uint32_t)row_gather4<nb>(x.sxb_raw[T]) >> byte);
+        const int raw = x.sxb_raw[T], lone = x.sxb_lone[T];
+        static_for<0, Cfg<MODE>::NBW>([&](auto Jc) {
+            constexpr int j = decltype(Jc)::value;
+            constexpr int b = 8 * (j / 2) + (j % 2);
+            int v = row_gather4<b, b + 2, b + 4, b + 6>(raw);
+            if constexpr (j % 2 == 0) {
+                // block j is lone when the wave's group ends with it
+                if (lone == (Cfg<MODE>::NBW == 4 ? j + 1 : 1)) v = row_gather4<4 * j, 4 * j + 1, 4 * j + 2, 4 * j + 3>(raw);
+            }
+            x.sxb[j] = (int)((uint32_t)v >> byte);
         });
     }
 }
 
 // ------------------------------------------------------------ epilogue
-// Result lane l, register v of block (mb, nb) holds row MB (l % 16) + mb,
-// column WN w + 16 nb + 4 (l / 16) + v of the tile.  One permlane16 swap per
-// pair of blocks moves the data so that each lane holds 8 consecutive
-// columns.  With two block pairs per wave (ptpc, mxfp8) a DPP exchange
-// between lanes i and i + 8 then makes every store write 8 whole 128-byte
-// row segments: store 0 rows MB (i % 8) + mb, store 1 rows MB (i % 8 + 8) +
-// mb, lane i writing pair i / 8 of the row.
+// Result lane l, register v of block (mb, nb) holds row MB (l % 16) + mb of
+// the tile and the output column that B-fragment row 4 (l / 16) + v of the
+// block feeds (b_layout.h): in a full group, lane (i, g) holds columns
+// 8g .. 8g + 7 of its wave's 64 in blocks 0-1 and 32 + 8g .. 32 + 8g + 7 in
+// blocks 2-3 (a 32-column wave: 8g .. 8g + 7 in its two blocks), so after the
+// bf16 conversion each run is one 16-byte store and the four lanes of a row
+// write 64 contiguous bytes.  A lone block (the odd last block of the last
+// group when N % 64 is 16 or 48) holds columns 16 nb + 4g .. + 3 and leaves
+// in an 8-byte store.  Rows at or past M fall outside the C descriptor;
+// runs at or past N carry 2^31 on their offset and fall outside it too.
 //
 // ptpc and mxfp8 (accumulators in AGPRs) spread a tile's epilogue over two
 // K steps, so that its conversion work and its stores overlap matrix ops
@@ -567,71 +589,88 @@ __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
 // With one K tile per tile both halves would land in the same step, so
 // there the whole tile is stored in the next tile's first step, each row
 // block just ahead of the matrix ops that overwrite it.  The workgroup's
-// last rows are stored after its loop.  Blockscale (accumulators in VGPRs,
-// written by the compiler) stores each tile at its end.
+// last rows are stored after its loop.  Blockscale and the other 32-column
+// waves store each tile at its end.
 
-// Start the epilogue of the tile at (m0, n0).  ptpc reads its scales from
-// this wave's LDS region, where the scale DMAs (issue_epilogue_scales) put
-// them: in the previous tile's last step or the prologue, or, with one K
-// tile per tile, earlier in the same or the previous step.  Every such DMA
-// was followed by at least the NA A-tile DMAs of a step (and possibly by
-// stores), so vmcnt(NA) covers it; each wave reads only the region it
-// filled.  The reads are written out so that the compiler, which cannot
-// tell the A-tile DMAs still in flight from writes to this region, does not
-// drain the whole prefetch pipeline (vmcnt(0)) before them.
+constexpr uint32_t kDrop = 0x80000000u;
+
+// Start the epilogue of the tile at (m0, n0): the store offsets and, for
+// ptpc, the scales.  ptpc reads its scales from this wave's LDS region,
+// where the scale DMAs (issue_epilogue_scales) put them: in the previous
+// tile's last step or the prologue, or, with one K tile per tile, earlier in
+// the same or the previous step.  Every such DMA was followed by at least
+// the NA A-tile DMAs of a step (and possibly by stores), so vmcnt(NA) covers
+// it; each wave reads only the region it filled.  The reads are written out
+// so that the compiler, which cannot tell the A-tile DMAs still in flight
+// from writes to this region, does not drain the whole prefetch pipeline
+// (vmcnt(0)) before them.
 template <int MODE>
 __device__ __forceinline__ Epi epi_begin(Ctx<MODE>& x, int m0, int n0) {
     using C = Cfg<MODE>;
     Epi e;
+    // the wave's first column, its group's block count, and the byte
+    // offset of row MB i (this lane's row in row block 0) at that column
+    const int wc = n0 + C::WN * x.w;
+    const int p = bl::group_blocks(wc >> 6, x.N >> 4);
+    const uint32_t base = (uint32_t)(((m0 + C::MB * x.i) * x.N + wc) * 2);
     if constexpr (C::NBW == 4) {
-        const int nb_of_lane = 2 * (x.i >> 3) + (x.g & 1);
-        e.col = n0 + C::WN * x.w + 16 * nb_of_lane + 8 * (x.g >> 1);
-        e.cdrop = n0 + C::WN * x.w + 16 * nb_of_lane < x.N ? 0u : 0x80000000u;
-        e.row = m0 + C::MB * (x.i & 7);
+        e.o16[0] = base + 16 * x.g + (p >= 2 ? 0u : kDrop);       // blocks 0-1: columns 8g ..
+        e.o16[1] = base + 64 + 16 * x.g + (p == 4 ? 0u : kDrop);  // blocks 2-3: columns 32 + 8g ..
+        e.lone = p & 1;                                           // block p - 1 is lone
+        e.o8 = base + 32 * (p - 1) + 8 * x.g + (p & 1 ? 0u : kDrop);
     } else {
-        // one block pair per wave: the 4 lanes of row MB i + mb hold its
-        // 64 bytes; the neighbouring wave writes the other half of each
-        // 128-byte segment, so these stores go through the L2, which merges
-        // the halves
-        e.col = n0 + C::WN * x.w + 16 * (x.g & 1) + 8 * (x.g >> 1);
-        e.cdrop = n0 + C::WN * x.w + 16 * (x.g & 1) < x.N ? 0u : 0x80000000u;
-        e.row = m0 + C::MB * x.i;
+        // the wave holds blocks 2 (w % 2) and 2 (w % 2) + 1 of its group
+        const int first = 2 * (x.w & 1);
+        e.o16[0] = base + 16 * x.g + (first + 2 <= p ? 0u : kDrop);
+        e.o16[1] = kDrop;
+        e.lone = first + 1 == p;
+        e.o8 = base + 8 * x.g + (first + 1 == p ? 0u : kDrop);
     }
     if constexpr (MODE == MODE_PTPC_N) {
-        // rows MB i .. MB i + 7 and, per block, columns WN w + 16 nb + 4 g + v
+        // rows MB i .. MB i + 7; columns 8g + 4j + v of the wave's 32 (a lone
+        // block: 4g + v)
         static_assert(C::MB == 8 && C::NBW == 2, "two A- and two B-scale vectors");
         wait_vm<C::NA>();
         const uint32_t sc = (uint32_t)(uintptr_t)(x.lds.scale + x.w * 2048);
-        const uint32_t pa = sc + C::MB * x.i * 4, pb = sc + 1024 + (C::WN * x.w + 4 * x.g) * 4;
+        const uint32_t pa = sc + C::MB * x.i * 4;
+        const uint32_t pb = sc + 1024 + (C::WN * x.w + (e.lone ? 4 : 8) * x.g) * 4;
         asm volatile(
             "ds_read_b128 %0, %4\n"
             "ds_read_b128 %1, %4 offset:16\n"
             "ds_read_b128 %2, %5\n"
-            "ds_read_b128 %3, %5 offset:64\n"
+            "ds_read_b128 %3, %5 offset:16\n"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(e.eas[0]), "=&v"(e.eas[1]), "=&v"(e.ebs[0]), "=&v"(e.ebs[1])
             : "v"(pa), "v"(pb)
             : "memory");
     }
     if constexpr (kWidePtpc<MODE>) {
+        // rows MB i .. MB i + 15; block nb's columns 8g + {0, 4, 32, 36}[nb] + v
+        // of the wave's 64 (a lone block nb: 16 nb + 4g + v)
         static_assert(C::MB == 16 && C::NBW == 4, "ptpc epilogue reads four A- and four B-scale vectors");
         wait_vm<C::NA>();
         const uint32_t sc = (uint32_t)(uintptr_t)(x.lds.scale + x.w * 2048);
-        const uint32_t pa = sc + C::MB * x.i * 4, pb = sc + 1024 + (C::WN * x.w + 4 * x.g) * 4;
+        const uint32_t pa = sc + C::MB * x.i * 4, pb = sc + 1024 + (C::WN * x.w + 8 * x.g) * 4;
+        const uint32_t pl = sc + 1024 + (C::WN * x.w + 16 * (p - 1) + 4 * x.g) * 4;
+        v4f lone;
         asm volatile(
-            "ds_read_b128 %0, %8\n"
-            "ds_read_b128 %1, %8 offset:16\n"
-            "ds_read_b128 %2, %8 offset:32\n"
-            "ds_read_b128 %3, %8 offset:48\n"
-            "ds_read_b128 %4, %9\n"
-            "ds_read_b128 %5, %9 offset:64\n"
-            "ds_read_b128 %6, %9 offset:128\n"
-            "ds_read_b128 %7, %9 offset:192\n"
+            "ds_read_b128 %0, %9\n"
+            "ds_read_b128 %1, %9 offset:16\n"
+            "ds_read_b128 %2, %9 offset:32\n"
+            "ds_read_b128 %3, %9 offset:48\n"
+            "ds_read_b128 %4, %10\n"
+            "ds_read_b128 %5, %10 offset:16\n"
+            "ds_read_b128 %6, %10 offset:128\n"
+            "ds_read_b128 %7, %10 offset:144\n"
+            "ds_read_b128 %8, %11\n"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(e.eas[0]), "=&v"(e.eas[1]), "=&v"(e.eas[2]), "=&v"(e.eas[3]), "=&v"(e.ebs[0]),
-              "=&v"(e.ebs[1]), "=&v"(e.ebs[2]), "=&v"(e.ebs[3])
-            : "v"(pa), "v"(pb)
+              "=&v"(e.ebs[1]), "=&v"(e.ebs[2]), "=&v"(e.ebs[3]), "=&v"(lone)
+            : "v"(pa), "v"(pb), "v"(p > 0 ? pl : pb)
             : "memory");
+        // a lone block (p odd) is block 0 or 2
+        if (p == 1) e.ebs[0] = lone;
+        if (p == 3) e.ebs[2] = lone;
     }
     return e;
 }
@@ -640,8 +679,8 @@ __device__ __forceinline__ Epi epi_begin(Ctx<MODE>& x, int m0, int n0) {
 // spread over eight matrix ops:
 //   0, 1  read the accumulators of column-block pair 0 / 1
 //   2..5  ptpc scaling, pair (PH - 2) / 2, first / second block of the pair
-//   6     bf16 conversion and permlane16 swaps of both pairs
-//   7     DPP exchange and the two stores
+//   6     bf16 conversion of both pairs
+//   7     the stores
 struct EpiRow {
     v4f u[2], v[2];
     v4i d[2];
@@ -668,29 +707,21 @@ __device__ __forceinline__ void epi_phase(Ctx<MODE>& x, const Epi& e, EpiRow& q)
         }
     } else if constexpr (PH == 6) {
 #pragma unroll
-        for (int pair = 0; pair < 2; ++pair) {
-            const uint32_t u0 = pack_bf16(q.u[pair][0], q.u[pair][1]), u1 = pack_bf16(q.u[pair][2], q.u[pair][3]);
-            const uint32_t v0 = pack_bf16(q.v[pair][0], q.v[pair][1]), v1 = pack_bf16(q.v[pair][2], q.v[pair][3]);
-            const auto s0 = __builtin_amdgcn_permlane16_swap(u0, v0, false, false);
-            const auto s1 = __builtin_amdgcn_permlane16_swap(u1, v1, false, false);
-            q.d[pair] = (v4i){(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
-        }
+        for (int pair = 0; pair < 2; ++pair)
+            q.d[pair] = (v4i){pack_bf16(q.u[pair][0], q.u[pair][1]), pack_bf16(q.u[pair][2], q.u[pair][3]),
+                              pack_bf16(q.v[pair][0], q.v[pair][1]), pack_bf16(q.v[pair][2], q.v[pair][3])};
     } else {
+        // C is written once and never read back, so the stores stream past
+        // the caches that hold the A and B panels
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(x.c, (uint32_t)x.M * (uint32_t)x.N * 2u);
-        v4i lo, hi;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            lo[c] = __builtin_amdgcn_update_dpp(q.d[0][c], q.d[1][c], kDppRowRor8, 0xF, 0xC, false);
-            hi[c] = __builtin_amdgcn_update_dpp(q.d[1][c], q.d[0][c], kDppRowRor8, 0xF, 0x3, false);
+        const uint32_t ro = (uint32_t)(r * x.N * 2);
+        __builtin_amdgcn_raw_buffer_store_b128(q.d[0], rc, e.o16[0] + ro, 0, kStoreStream);
+        __builtin_amdgcn_raw_buffer_store_b128(q.d[1], rc, e.o16[1] + ro, 0, kStoreStream);
+        if (e.lone) {
+            // the lone block is block 0 (then run 0 is dropped) or block 2
+            const v4i& d = e.o16[0] < kDrop ? q.d[1] : q.d[0];
+            __builtin_amdgcn_raw_buffer_store_b64((v2i){d[0], d[1]}, rc, e.o8 + ro, 0, kStoreStream);
         }
-        // C is written once and never read back, so whole-line stores
-        // stream past the caches that hold the A and B panels; rows at or
-        // past M, and column groups at or past N (cdrop), fall outside the
-        // buffer and are dropped
-        const uint32_t o0 = (uint32_t)(((e.row + r) * x.N + e.col) * 2) + e.cdrop;
-        const uint32_t o1 = (uint32_t)(((e.row + 8 * C::MB + r) * x.N + e.col) * 2) + e.cdrop;
-        __builtin_amdgcn_raw_buffer_store_b128(lo, rc, o0, 0, kStoreStream);
-        __builtin_amdgcn_raw_buffer_store_b128(hi, rc, o1, 0, kStoreStream);
     }
 }
 
@@ -721,12 +752,14 @@ __device__ __forceinline__ void epi_row(Ctx<MODE>& x, const Epi& e) {
             u = u * sa * e.ebs[0];
             v = v * sa * e.ebs[1];
         }
-        const uint32_t u0 = pack_bf16(u[0], u[1]), u1 = pack_bf16(u[2], u[3]);
-        const uint32_t v0 = pack_bf16(v[0], v[1]), v1 = pack_bf16(v[2], v[3]);
-        const auto s0 = __builtin_amdgcn_permlane16_swap(u0, v0, false, false);
-        const auto s1 = __builtin_amdgcn_permlane16_swap(u1, v1, false, false);
-        const v4i d = (v4i){(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
-        __builtin_amdgcn_raw_buffer_store_b128(d, rc, (uint32_t)(((e.row + mb) * x.N + e.col) * 2) + e.cdrop, 0, 0);
+        // the wave's two blocks (columns 8g .. 8g + 7), or its lone block 0
+        // (columns 4g .. 4g + 3); the neighbouring wave writes the other
+        // half of each 128-byte segment, so these stores go through the L2,
+        // which merges the halves
+        const v4i d = (v4i){pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3]), pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        const uint32_t ro = (uint32_t)(mb * x.N * 2);
+        __builtin_amdgcn_raw_buffer_store_b128(d, rc, e.o16[0] + ro, 0, 0);
+        if (e.lone) __builtin_amdgcn_raw_buffer_store_b64((v2i){d[0], d[1]}, rc, e.o8 + ro, 0, 0);
     }
 }
 
@@ -1043,6 +1076,7 @@ __global__ void __launch_bounds__(Cfg<MODE>::NTHREADS, 1) gemm_a8w8_kernel(GemmA
     // (block * KI + kt) * 2048; lane l reads 16 bytes at 16 l of each half.
 #pragma unroll
     for (int nb = 0; nb < C::NBW; ++nb) x.voff_b[nb] = ((C::NBW * x.w + nb) * x.KI) * 2048 + 16 * x.lane;
+
 
     Ring g{x.ref(0), x.ref(1), x.ref(2)};
 

@@ -6,6 +6,7 @@
 // mori PR 785 (section Cost).  All kernels are HBM-bound streams: fully
 // coalesced 16-byte loads, wave-level max reductions through lane shuffles,
 // and the quantised bytes written 4 per lane.
+#include "b_layout.h"
 #include "common.h"
 
 namespace dmm {
@@ -242,10 +243,14 @@ __global__ void __launch_bounds__(256) quantize_mxfp8_kernel(const float* __rest
 }
 
 // ----------------------------------------------------------- preshuffle
-// Output chunk (block j of 16 rows, K tile kt) = 2 KiB at (j * KI + kt) * 2048.
-// Byte 16 l + t of half h (t < 16) holds B[16 j + l % 16][128 kt + 64 h +
-// 16 (l / 16) + t]: exactly the 32 bytes matrix-core lane l consumes for a
-// 16 x 128 fp8 operand, so each half is one coalesced 1 KiB load.
+// Output chunk (block j of 16 fragment rows, K tile kt) = 2 KiB at
+// (j * KI + kt) * 2048.  Byte 16 l + t of half h (t < 16) holds
+// B[src(j, l % 16)][128 kt + 64 h + 16 (l / 16) + t]: exactly the 32 bytes
+// matrix-core lane l consumes for a 16 x 128 fp8 operand, so each half is
+// one coalesced 1 KiB load.  Fragment row r of block j is B row
+// src(j, r) = 64 G + bl::frag_col(j % 4, r, p) of its group G = j / 4 of p
+// blocks (b_layout.h): the order in which the GEMM's lanes hold contiguous
+// output columns.
 __global__ void __launch_bounds__(256) preshuffle_b_kernel(const uint8_t* __restrict__ b, uint8_t* __restrict__ out,
                                                            int n, int k) {
     const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;  // one 16-byte piece per thread
@@ -257,7 +262,9 @@ __global__ void __launch_bounds__(256) preshuffle_b_kernel(const uint8_t* __rest
     const size_t chunk = t >> 7;
     const int kt = (int)(chunk % KI);
     const int j = (int)(chunk / KI);
-    const size_t src = (size_t)(16 * j + (l & 15)) * k + 128 * kt + 64 * h + 16 * (l >> 4);
+    const int G = j >> 2;
+    const int row = 64 * G + bl::frag_col(j & 3, l & 15, bl::group_blocks(G, n / 16));
+    const size_t src = (size_t)row * k + 128 * kt + 64 * h + 16 * (l >> 4);
     *(v4i*)(out + t * 16) = *(const v4i*)(b + src);
 }
 

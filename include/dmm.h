@@ -96,8 +96,15 @@ dmm_status quantize_mxfp8(const float* x, uint8_t* q, uint8_t* scale, int64_t ro
 /* Reorders B [n, k] E4M3 codes (one row per output channel) into the byte
  * order the GEMM's matrix-core operands use (aiter PR 6539 names the kernels
  * "bpreshuffle"; mori PR 809, Using it, calls preshuffle_b once per weight).
- * The layout is library-defined and opaque: b_shuf has the same size as b
- * (n * k bytes) and is only meant to be passed to the gemm_a8w8_* calls.
+ * The layout is library-defined: b_shuf has the same size as b (n * k
+ * bytes) and is only meant to be passed to the gemm_a8w8_* calls.  (For
+ * reference: 2 KiB chunk (j, kt) at (j * k/128 + kt) * 2048 holds block j of
+ * 16 fragment rows for K tile kt; byte 16 l + t of its half h is
+ * B[src(j, l % 16)][128 kt + 64 h + 16 (l / 16) + t].  Blocks come in groups
+ * of four, 64 output columns; in group G = j / 4 of p blocks, fragment row r
+ * of block nb = j % 4 is B row 64 G + 32 (nb / 2) + 8 (r / 4) + 4 (nb % 2) +
+ * r % 4, except that the last block of a group with an odd p keeps row
+ * order, 64 G + 16 nb + r.)
  * b and b_shuf must not overlap.  Rules: n >= 16, n % 16 == 0, k >= 128,
  * k % 128 == 0. */
 dmm_status preshuffle_b(const uint8_t* b, uint8_t* b_shuf, int64_t n, int64_t k, void* stream);

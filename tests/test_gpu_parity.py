@@ -128,17 +128,34 @@ def test_quantize_mxfp8_bitexact(dmm, rows, k, seed):
 
 
 # ------------------------------------------------------------ preshuffle
+def documented_src_row(j, r, n):
+    """B row held by fragment row r of block j, as include/dmm.h and
+    preshuffle_b document it: blocks come in groups of four (64 output
+    columns); in a group of p blocks, a block with a partner puts row r at
+    column 32 (nb // 2) + 8 (r // 4) + 4 (nb % 2) + r % 4 of the group, the
+    lone last block of an odd group keeps row order (16 nb + r)."""
+    G, nb = divmod(j, 4)
+    p = min(4, n // 16 - 4 * G)
+    if p % 2 == 1 and nb == p - 1:
+        return 64 * G + 16 * nb + r
+    return 64 * G + 32 * (nb // 2) + 8 * (r // 4) + 4 * (nb % 2) + r % 4
+
+
 def unshuffle(bs, n, k):
     """Inverse of the library's B order, written from its documented layout:
     chunk (j, kt) of 2 KiB; byte 16 l + t of half h is
-    B[16 j + l % 16][128 kt + 64 h + 16 (l / 16) + t]."""
+    B[src(j, l % 16)][128 kt + 64 h + 16 (l / 16) + t]."""
     ki = k // 128
-    v = bs.reshape(n // 16, ki, 2, 4, 16, 16)  # j, kt, h, l/16 (g), l%16 (i), t
-    # B[16 j + i][128 kt + 64 h + 16 g + t]
-    return v.transpose(0, 4, 1, 2, 3, 5).reshape(n, k)
+    v = bs.reshape(n // 16, ki, 2, 4, 16, 16)  # j, kt, h, l/16 (g), l%16 (r), t
+    frag = v.transpose(0, 4, 1, 2, 3, 5).reshape(n // 16, 16, k)  # [j][r] = row data in fragment order
+    out = np.empty((n, k), np.uint8)
+    for j in range(n // 16):
+        for r in range(16):
+            out[documented_src_row(j, r, n)] = frag[j, r]
+    return out
 
 
-@pytest.mark.parametrize("n,k", [(16, 128), (272, 384), (1168, 1792)])
+@pytest.mark.parametrize("n,k", [(16, 128), (32, 128), (48, 256), (272, 384), (1120, 256), (1168, 1792), (6288, 128)])
 def test_preshuffle_is_the_documented_permutation(dmm, n, k):
     announce("preshuffle_b", n, k)
     b = np.random.default_rng(n + k).integers(0, 256, size=(n, k), dtype=np.uint8)
@@ -213,7 +230,9 @@ def exact_operands(mode, m, n, k, seed):
     return qa, qb, sa, sb
 
 
-EXACT_SHAPES = [(1, 16, 128), (17, 272, 256), (300, 1168, 384), (256, 256, 512), (513, 528, 640), (64, 48, 1792)]
+# N % 64 = 16, 16, 16, 0, 16, 48, 32, 32: every kind of last column group
+EXACT_SHAPES = [(1, 16, 128), (17, 272, 256), (300, 1168, 384), (256, 256, 512), (513, 528, 640), (64, 48, 1792),
+                (130, 1120, 256), (40, 32, 128)]
 
 
 @pytest.mark.parametrize("mode", GEMM_MODES)

@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "dense_matmul_amd", "csrc")
 
 SHIM = r"""
+#include "b_layout.h"
 #include "kpipe.h"
 #include "lds_layout.h"
 using namespace dmm;
@@ -48,6 +49,8 @@ int frag_byte(int i, int g, int mb, int half, int MB) { return lds::frag_byte(i,
 int bf16_chunk_pos(int r, int c) { return lds::bf16_chunk_pos(r, c); }
 int bf16_prologue_wait(int NS, int NL) { return sched::bf16_prologue_wait(NS, NL); }
 int bf16_mid_wait(int NS, int NL) { return sched::bf16_mid_wait(NS, NL); }
+int frag_col(int nb, int r, int p) { return bl::frag_col(nb, r, p); }
+int group_blocks(int G, int nblocks) { return bl::group_blocks(G, nblocks); }
 int shape_field(int mode, int f) {
     const sched::Shape sh = sched::shape_of(mode);
     const int v[6] = {sh.MB, sh.NBW, sh.WAVES, sh.NA, sh.NB, sh.NSC};
@@ -67,7 +70,7 @@ def shim(tmp_path_factory):
     L = ctypes.CDLL(str(lib))
     for f in ("prologue_wait", "wait_at", "stage_of", "refill_stage", "dma_lds_byte", "dma_row", "dma_chunk",
               "frag_byte", "dma_ahead_tile", "dma_ahead_kt", "case_of", "phase_advance", "bf16_chunk_pos",
-              "shape_field", "bf16_prologue_wait", "bf16_mid_wait"):
+              "shape_field", "bf16_prologue_wait", "bf16_mid_wait", "frag_col", "group_blocks"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -424,3 +427,33 @@ def test_bf16_ring_shapes_match_the_kernel():
     assert "static constexpr int NS = BM == 128 ? 4 : 3;" in src
     for bm, (NS, NL) in ((128, BF16_RINGS["128x128"]), (64, BF16_RINGS["64x64"])):
         assert NL == 2 * (bm * 64 * 2 // 1024 // 4)
+
+
+# ------------------------------------------------------------- B row order
+def test_b_layout_is_a_permutation_of_each_group(shim):
+    """Every group of p blocks (p = 1..4) sends its 16 p fragment rows to its
+    16 p output columns exactly once."""
+    for p in range(1, 5):
+        cols = sorted(shim.frag_col(nb, r, p) for nb in range(p) for r in range(16))
+        assert cols == list(range(16 * p)), p
+
+
+def test_b_layout_gives_each_lane_two_runs_of_eight_columns(shim):
+    """Lane (i, g) holds B-operand rows 4g .. 4g+3 of each block in its
+    accumulators: in a full group its blocks 0-1 cover columns 8g .. 8g+7
+    and blocks 2-3 columns 32+8g .. 32+8g+7, in register order; a pair in a
+    partial group covers 8g .. 8g+7 the same way; a lone block covers
+    16 nb + 4g .. + 3."""
+    for p in range(1, 5):
+        for g in range(4):
+            for pair in range(p // 2):
+                run = [shim.frag_col(2 * pair + h, 4 * g + v, p) for h in range(2) for v in range(4)]
+                assert run == list(range(32 * pair + 8 * g, 32 * pair + 8 * g + 8)), (p, g, pair)
+            if p % 2:
+                nb = p - 1
+                assert [shim.frag_col(nb, 4 * g + v, p) for v in range(4)] == [16 * nb + 4 * g + v for v in range(4)]
+
+
+def test_group_blocks_counts_the_last_partial_group(shim):
+    assert [shim.group_blocks(G, 393) for G in (0, 97, 98, 99)] == [4, 4, 1, 0]  # N = 6288
+    assert [shim.group_blocks(G, 3) for G in (0, 1)] == [3, 0]                  # N = 48

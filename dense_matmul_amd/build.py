@@ -69,5 +69,23 @@ def device_asm(src="gemm_a8w8.hip", out=None):
     return out
 
 
+def disassemble(src="gemm_a8w8.hip"):
+    """gfx950 disassembly of the kernels this build compiled from one source
+    file (the device code object inside _build/<src>.o, which build() leaves
+    there), for audits of the emitted waits, barriers and loads."""
+    obj = os.path.join(ROOT, "_build", src + ".o")
+    if not os.path.exists(obj):
+        build()
+    llvm = "/opt/rocm/llvm/bin"
+    work = os.path.join(ROOT, "_build", "disasm")
+    os.makedirs(work, exist_ok=True)
+    fat, co = os.path.join(work, src + ".fatbin"), os.path.join(work, src + ".co")
+    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", obj], check=True)
+    subprocess.run([f"{llvm}/clang-offload-bundler", "--unbundle", "--type=o", f"--input={fat}",
+                    f"--targets=hipv4-amdgcn-amd-amdhsa--{ARCH}", f"--output={co}"], check=True)
+    return subprocess.run([f"{llvm}/llvm-objdump", "-d", f"--mcpu={ARCH}", co], check=True,
+                          capture_output=True, text=True).stdout
+
+
 if __name__ == "__main__":
     print(build())

@@ -802,18 +802,18 @@ struct StepLoads {
 // LDS.  WAR: every wave's reads of stage (S+3)%4 (stream step s-1) have
 // retired, so the A DMAs that follow may refill it.  The count is
 // sched::wait_at(s, k, KI, ...), specialised (FIRST && LAST is KI == 1):
-// only the stream's very first step differs from the rest of its kind.
-template <int MODE, int S, bool FIRST, bool LAST>
-__device__ __forceinline__ void mid_step(int s) {
+// only the stream's very first step (HEAD: the first K step of the
+// workgroup's first tile, s = 0) differs from the rest of its kind.  Every
+// count is a compile-time constant, so each barrier has exactly one wait in
+// front of it on every path through the code.
+template <int MODE, int S, bool FIRST, bool LAST, bool HEAD>
+__device__ __forceinline__ void mid_step() {
     using C = Cfg<MODE>;
     constexpr int NA = C::NA, NB = C::NB, NSC = C::NSC;
     constexpr int XT = FIRST && LAST ? 2 : FIRST ? 1 : 0;
-    if constexpr (FIRST) {
-        if (s == 0) wait_vm_lgkm0<sched::cap(sched::first_mid_wait(NA, NB) + (LAST ? NSC : 0))>();
-        else wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB) + XT * NSC)>();
-    } else {
-        wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB))>();
-    }
+    static_assert(!HEAD || FIRST, "the stream starts with a tile's first K step");
+    if constexpr (HEAD) wait_vm_lgkm0<sched::cap(sched::first_mid_wait(NA, NB) + (LAST ? NSC : 0))>();
+    else wait_vm_lgkm0<sched::cap(sched::mid_wait(NA, NB) + XT * NSC)>();
     __builtin_amdgcn_s_barrier();
 }
 
@@ -853,9 +853,9 @@ __device__ __forceinline__ void mfma_row_epi(Ctx<MODE>& x, const v8i& a, EpiRow&
 //   previous tile, each row block just ahead of its matrix ops (one K tile
 //   per tile); 2 row blocks 8..15 of the previous tile (first K step);
 //   3 row blocks 0..7 of this tile (last K step).
-template <int MODE, int S, bool FIRST, bool LAST, int EPM, int mb>
-__device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, StepLoads L, EpiRow& q, v8i& f0,
-                                          v8i& f1, v8i& f2) {
+template <int MODE, int S, bool FIRST, bool LAST, bool HEAD, int EPM, int mb>
+__device__ __forceinline__ void step_rows(Ctx<MODE>& x, TileRef cur, StepLoads L, EpiRow& q, v8i& f0, v8i& f1,
+                                          v8i& f2) {
     using C = Cfg<MODE>;
     if constexpr (mb < C::MB) {
         constexpr int T = S & 1;
@@ -877,11 +877,15 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, Step
             }
             if constexpr (mb == HALF - 1) {
                 b_scales<MODE, T ^ 1>(x, L.bref, L.bkt);
-                if constexpr (FIRST && LAST) issue_epilogue_scales<MODE>(x, cur);
+                if constexpr (FIRST && LAST && kPtpc<MODE>) {
+                    // after the whole B event, as the wait counts assume
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_epilogue_scales<MODE>(x, cur);
+                }
             }
         }
         if constexpr (mb == HALF) {
-            mid_step<MODE, S, FIRST, LAST>(s);
+            mid_step<MODE, S, FIRST, LAST, HEAD>();
             if constexpr (LAST && !FIRST) issue_epilogue_scales<MODE>(x, L.enext);
         }
         // NA DMAs spread over the second half, the first at mb = HALF
@@ -917,7 +921,7 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, Step
         } else {
             mfma_row<MODE, T, mb, FIRST>(x, fa);
         }
-        step_rows<MODE, S, FIRST, LAST, EPM, mb + 1>(x, s, cur, L, q, f0, f1, f2);
+        step_rows<MODE, S, FIRST, LAST, HEAD, EPM, mb + 1>(x, cur, L, q, f0, f1, f2);
     } else if constexpr (EPM == 3) {
         // the second half of row block 7 (MB = 16)
         static_assert(Cfg<MODE>::MB == 16, "row blocks 0..7 of 16 in the last K step");
@@ -932,10 +936,11 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, int s, TileRef cur, Step
 // Stream step s = K tile k of tile j.  S = s % 4 is the LDS stage of the
 // tile, T = s % 2 the B register buffer.  FIRST / LAST: k == 0 / k == KI-1
 // (both for KI == 1).  PREV: a tile precedes this one in the workgroup's
-// list, so a first K step also stores (part of) it.
-template <int MODE, int S, bool FIRST, bool LAST, bool PREV = false>
+// list, so a first K step also stores (part of) it.  HEAD: s == 0.
+template <int MODE, int S, bool FIRST, bool LAST, bool PREV = false, bool HEAD = false>
 __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRef prev = TileRef{}) {
     static_assert(!PREV || FIRST, "the previous tile's epilogue runs in the first K step");
+    static_assert(!(PREV && HEAD), "the stream's first tile has no predecessor");
     constexpr int EPM = !kDeferEpilogue<MODE> ? 0
                         : FIRST && LAST       ? (PREV ? 1 : 0)
                         : FIRST               ? (PREV ? 2 : 0)
@@ -983,7 +988,7 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRe
     realign_mx<MODE, T>(x);
     v8i f0 = x.pre[0], f1 = x.pre[1], f2;
     EpiRow q;
-    step_rows<MODE, S, FIRST, LAST, EPM, 0>(x, s, g.t0, L, q, f0, f1, f2);
+    step_rows<MODE, S, FIRST, LAST, HEAD, EPM, 0>(x, g.t0, L, q, f0, f1, f2);
 }
 
 // All K tiles of tile j, whose first K tile sits in stage P.  CASE = KI % 4
@@ -992,14 +997,15 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRe
 // groups of four plus exactly (CASE - 2) & 3 more, so every stage index and
 // every wait count is a constant.  PREV: the first step also stores tile
 // j - 1 (prev); without a deferred epilogue the tile stores itself at its end.
-template <int MODE, int P, int CASE, bool PREV>
+// HEAD: the workgroup's first tile (s0 = 0).
+template <int MODE, int P, int CASE, bool PREV, bool HEAD>
 __device__ __forceinline__ void tile_body(Ctx<MODE>& x, int s0, Ring g, TileRef prev) {
     const int KI = x.KI;
     if constexpr (CASE == 4) {
-        kstep<MODE, P, true, true, PREV>(x, s0, 0, g, prev);
+        kstep<MODE, P, true, true, PREV, HEAD>(x, s0, 0, g, prev);
     } else {
         constexpr int REM = (CASE - 2) & 3;  // (KI - 2) % 4
-        kstep<MODE, P, true, false, PREV>(x, s0, 0, g, prev);
+        kstep<MODE, P, true, false, PREV, HEAD>(x, s0, 0, g, prev);
         int k = 1;
         for (; k + 4 <= KI - 1; k += 4) {
             kstep<MODE, (P + 1) & 3, false, false>(x, s0 + k, k, g);
@@ -1021,7 +1027,7 @@ __device__ __forceinline__ void tile_body(Ctx<MODE>& x, int s0, Ring g, TileRef 
 
 template <int MODE, int P, int CASE, bool PREV>
 __device__ __forceinline__ void run_tile(Ctx<MODE>& x, int j, Ring& g, TileRef& prev) {
-    tile_body<MODE, P, CASE, PREV && kDeferEpilogue<MODE>>(x, j * x.KI, g, prev);
+    tile_body<MODE, P, CASE, PREV && kDeferEpilogue<MODE>, !PREV>(x, j * x.KI, g, prev);
     prev = g.t0;
     g = Ring{g.t1, g.t2, x.ref(j + 3)};
 }

@@ -60,19 +60,28 @@ int shape_field(int mode, int f) {
 """
 
 
-@pytest.fixture(scope="module")
-def shim(tmp_path_factory):
-    d = tmp_path_factory.mktemp("shim")
-    src = d / "shim.cpp"
-    src.write_text(SHIM)
-    lib = d / "libshim.so"
-    subprocess.run(["g++", "-std=c++17", "-O1", "-shared", "-fPIC", "-I", CSRC, str(src), "-o", str(lib)], check=True)
-    L = ctypes.CDLL(str(lib))
-    for f in ("prologue_wait", "wait_at", "stage_of", "refill_stage", "dma_lds_byte", "dma_row", "dma_chunk",
+SHIM_FUNCS = ("prologue_wait", "wait_at", "stage_of", "refill_stage", "dma_lds_byte", "dma_row", "dma_chunk",
               "frag_byte", "dma_ahead_tile", "dma_ahead_kt", "case_of", "phase_advance", "bf16_chunk_pos",
-              "shape_field", "bf16_prologue_wait", "bf16_mid_wait", "frag_col", "group_blocks"):
+              "shape_field", "bf16_prologue_wait", "bf16_mid_wait", "frag_col", "group_blocks")
+
+
+def compile_shim(d):
+    """The host shim over kpipe.h, lds_layout.h and b_layout.h, built with
+    g++ into directory d."""
+    src = os.path.join(str(d), "shim.cpp")
+    with open(src, "w") as f:
+        f.write(SHIM)
+    lib = os.path.join(str(d), "libshim.so")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-shared", "-fPIC", "-I", CSRC, src, "-o", lib], check=True)
+    L = ctypes.CDLL(lib)
+    for f in SHIM_FUNCS:
         getattr(L, f).restype = ctypes.c_int
     return L
+
+
+@pytest.fixture(scope="module")
+def shim(tmp_path_factory):
+    return compile_shim(tmp_path_factory.mktemp("shim"))
 
 
 # ---------------------------------------------------------------- schedule
@@ -85,13 +94,7 @@ def _shapes():
     shim (the numbers the kernel's waits are built from)."""
     import tempfile
 
-    d = tempfile.mkdtemp()
-    src = os.path.join(d, "shim.cpp")
-    open(src, "w").write(SHIM)
-    lib = os.path.join(d, "libshim.so")
-    subprocess.run(["g++", "-std=c++17", "-O1", "-shared", "-fPIC", "-I", CSRC, src, "-o", lib], check=True)
-    L = ctypes.CDLL(lib)
-    L.shape_field.restype = ctypes.c_int
+    L = compile_shim(tempfile.mkdtemp())
     return {name: tuple(L.shape_field(mid, f) for f in (3, 4, 5)) for name, mid in MODE_IDS.items()}
 
 

@@ -19,10 +19,11 @@ typedef __attribute__((address_space(3))) char lds_char;
 // zero and stores past the end are dropped, which is how the kernels mask
 // the partial last row and column tiles.  Word 3 (0x00020000) selects the
 // 32-bit untyped format used for raw buffer access on gfx9-family parts.
-// Every descriptor the kernels build is wave-uniform; the extent goes
-// through readfirstlane so that the compiler knows it too (where it cannot
-// prove it, it wraps each load in a loop over the distinct descriptors of
-// the wave's lanes).
+// Every descriptor the kernels build is wave-uniform: its base is a kernel
+// argument and its extent goes through readfirstlane, so that the compiler
+// knows it too (where it cannot prove it, it wraps each load in a loop over
+// the distinct descriptors of the wave's lanes).  Tile-dependent positions
+// belong in the per-lane offset, not in the base.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
                                              __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);

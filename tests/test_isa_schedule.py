@@ -30,7 +30,9 @@ the code as well, so the check can never pass vacuously.
 
 Loads of the gathered mode's ready flags (global_load) have to be waited for
 (vmcnt(0)) before any further load or barrier, which then completes every
-load before them.
+load before them.  A loop the compiler builds over the distinct values of an
+operand it cannot prove uniform (readfirstlane / exec-mask loops around a
+load) fails the audit: every buffer descriptor is uniform by construction.
 
 The mutants at the end edit the disassembly text and must be caught: a DMA
 moved across its barrier, a window whose waits are all relaxed to vmcnt(63)
@@ -56,6 +58,7 @@ TARGET = re.compile(r"<\S+\+0x([0-9a-f]+)>\s*$")
 VMCNT = re.compile(r"vmcnt\((\d+)\)")
 LGKMCNT = re.compile(r"lgkmcnt\((\d+)\)")
 VMCNT_MAX = 63
+MAX_WINDOW = 256  # far more loads than any window of the schedule has
 
 
 def parse(text):
@@ -118,12 +121,21 @@ def windows(insns):
                     bad.append(f"{addr:x}: barrier with a flag load outstanding")
                 out.setdefault((prev, loads), set()).add((eff, lgkm_ok))
                 prev, loads, lgkm_ok = loads, "", True
+            if len(loads) > MAX_WINDOW:
+                bad.append(f"{addr:x}: more than {MAX_WINDOW} loads without a barrier (a loop of loads)")
+                break
             if mn == "s_endpgm":
                 break
-            if mn == "s_branch":
+            if mn == "s_cbranch_execnz" and tgt <= addr and insns[i - 1][1] == "s_xor_b64" \
+                    and insns[i - 1][2].startswith("exec, exec"):
+                # a loop over the distinct values of a VGPR held in the wave's
+                # lanes (s_and_saveexec ... s_xor exec ... back): the compiler
+                # could not prove an operand uniform
+                bad.append(f"{addr:x}: loop over the lanes' values of a non-uniform operand")
+            elif mn == "s_branch":
                 stack.append((at[tgt], prev, loads, eff, lgkm_ok, poll))
                 break
-            if mn.startswith("s_cbranch"):
+            elif mn.startswith("s_cbranch"):
                 stack.append((at[tgt], prev, loads, eff, lgkm_ok, poll))
             i += 1
     return out, bad
@@ -318,3 +330,17 @@ def test_audit_catches_a_model_count_below_the_code(L, fp8_text):
 
     found, bad = windows(mutate(fp8_text, sym, lambda b: b))
     assert audit(found, fp8_model(L, MUTANT_KERNEL[0], MUTANT_KERNEL[1], events=events))
+
+
+def test_audit_catches_a_loop_over_lane_values():
+    """The compiler's loop over the distinct values of a VGPR operand
+    (readfirstlane, s_and_saveexec, the load, s_xor exec, back) is rejected."""
+    insns = [(0x0, "s_mov_b64", "s[2:3], exec", None),
+             (0x4, "v_readfirstlane_b32", "s4, v10", None),
+             (0x8, "s_and_saveexec_b64", "s[0:1], s[0:1]", None),
+             (0xc, "buffer_load_dwordx4", "v3, s[4:7], 0 offen lds", None),
+             (0x14, "s_xor_b64", "exec, exec, s[0:1]", None),
+             (0x18, "s_cbranch_execnz", "65530", 0x4),
+             (0x1c, "s_endpgm", "", None)]
+    _, bad = windows(insns)
+    assert any("non-uniform" in b for b in bad)

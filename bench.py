@@ -257,7 +257,7 @@ def copy_calibration(torch):
     torch.cuda.empty_cache()
 
 
-KERNEL_SOURCES = ("gemm_a8w8.hip", "common.h", "kpipe.h", "lds_layout.h", "tile_order.h")
+KERNEL_SOURCES = ("gemm_a8w8.hip", "common.h", "kpipe.h", "lds_layout.h", "tile_order.h", "b_layout.h")
 
 
 def kernel_source_hash():

@@ -228,7 +228,6 @@ struct Ctx {
     int sxa_tail[2];
     int sxa_shift[2];
     int sxb_raw[2];      // B scale bytes of 4 columns as loaded, per K tile
-    int sxb_lone[2];     // whether the B event's tile ends its wave's columns in a lone block (uniform)
     int sxb[C::NBW];     // B scale of this lane's fragment row in each block (byte 0), current step
     // blockscale: A scales of this lane's MB rows and the wave's B block scale;
     // the products of the last two row blocks, before they are scaled in
@@ -329,17 +328,23 @@ __device__ __forceinline__ void b_scales(Ctx<MODE>& x, TileRef r, int kt) {
         x.sxa[T] = __builtin_amdgcn_raw_buffer_load_b128(rsa, base, 0, 0);
         x.sxa_tail[T] = __builtin_amdgcn_raw_buffer_load_b32(rsa, base + 16, 0, 0);
         x.sxa_shift[T] = off & 3;
-        // B: lane (i, g) loads the dword of columns 4i .. 4i+3 of the wave's
-        // WN for K group 4kt + g (N is a multiple of 16); the step that uses
-        // them hands each lane the bytes of the columns its fragment rows feed
-        // (with WN = 32, lanes i >= 8 load a neighbour's columns, unused)
-        const int boff = (4 * kt + x.g) * x.N + n0 + C::WN * x.w + 4 * x.i;
-        x.sxb_raw[T] = __builtin_amdgcn_raw_buffer_load_b32(rsb, boff, 0, 0);
-        // a lone block: the last of a group with an odd block count, whose
-        // rows keep their order (b_layout.h); a wave's lone block is its
-        // block 0 or 2 (64-column waves) or its block 0 (32-column waves)
+        // B: lane (i, g) loads the dword of columns c .. c+3 of the wave's WN
+        // for K group 4kt + g (N is a multiple of 16), c = 4i; the step that
+        // uses them hands each lane the bytes of the columns its fragment rows
+        // feed (realign_mx; with WN = 32, lanes i >= 8 load a neighbour's
+        // columns, unused).  The step's broadcasts give bank q of block j the
+        // dword of lane 8 (j/2) + j%2 + 2q, which holds columns 32 (j/2) +
+        // 4 (j%2) + 8q .. + 3 of a paired block (b_layout.h).  A lone block
+        // j (the last of a group with an odd block count, rows in order; a
+        // wave's block 0 or 2, or block 0 of a 32-column wave) needs columns
+        // 16 j + 4q there instead: its four source lanes 4j + 2q load
+        // column c = 2i + 8j, so that every step uses the same broadcasts.
         const int p = bl::group_blocks((n0 + C::WN * x.w) >> 6, x.N >> 4);
-        x.sxb_lone[T] = C::NBW == 4 ? (p & 1) * p : (2 * (x.w & 1) + 1 == p);
+        const int lone = C::NBW == 4 ? ((p & 1) ? p - 1 : -1) : (2 * (x.w & 1) + 1 == p ? 0 : -1);
+        const bool remap = lone >= 0 && (x.i & 1) == 0 && (x.i >> 3) == (lone >> 1);
+        const int col = remap ? 2 * x.i + 8 * lone : 4 * x.i;
+        const int boff = (4 * kt + x.g) * x.N + n0 + C::WN * x.w + col;
+        x.sxb_raw[T] = __builtin_amdgcn_raw_buffer_load_b32(rsb, boff, 0, 0);
     } else if constexpr (MODE == MODE_BLOCKSCALE) {
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x.sa, valid ? (uint32_t)x.KI * (uint32_t)x.M * 4u : 0u);
         const __amdgpu_buffer_rsrc_t rsb =
@@ -545,10 +550,9 @@ __device__ __forceinline__ int row_gather4(int src) {
 // q holds the bytes of rows 4q..4q+3, and give lane (i, g) the B-scale byte
 // of the column its fragment row i feeds in each block (b_layout.h), which
 // lane (src, g) loaded as byte i % 4 of its dword: for the wave's block j and
-// bank q = i / 4, src = 8 (j / 2) + 2q + j % 2 (a paired block: columns
-// 8q .. 8q + 7 and 32 + 8q .. of the wave's), or 4j + q (a lone block:
-// columns 16 j + 4q ..).  DPP row broadcasts: vector ops, where an LDS
-// crossbar permute would cost matrix time.
+// bank q = i / 4, src = 8 (j / 2) + 2q + j % 2 (b_scales chose what each
+// source lane loads, lone blocks included).  DPP row broadcasts: vector ops,
+// where an LDS crossbar permute would cost matrix time.
 template <int MODE, int T>
 __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
     if constexpr (kMx<MODE>) {
@@ -561,16 +565,11 @@ __device__ __forceinline__ void realign_mx(Ctx<MODE>& x) {
                              (int)__builtin_amdgcn_alignbyte(w[3], w[2], sh), (int)__builtin_amdgcn_alignbyte(t, w[3], sh)};
         }
         const int byte = 8 * (x.i & 3);
-        const int raw = x.sxb_raw[T], lone = x.sxb_lone[T];
+        const int raw = x.sxb_raw[T];
         static_for<0, Cfg<MODE>::NBW>([&](auto Jc) {
             constexpr int j = decltype(Jc)::value;
             constexpr int b = 8 * (j / 2) + (j % 2);
-            int v = row_gather4<b, b + 2, b + 4, b + 6>(raw);
-            if constexpr (j % 2 == 0) {
-                // block j is lone when the wave's group ends with it
-                if (lone == (Cfg<MODE>::NBW == 4 ? j + 1 : 1)) v = row_gather4<4 * j, 4 * j + 1, 4 * j + 2, 4 * j + 3>(raw);
-            }
-            x.sxb[j] = (int)((uint32_t)v >> byte);
+            x.sxb[j] = (int)((uint32_t)row_gather4<b, b + 2, b + 4, b + 6>(raw) >> byte);
         });
     }
 }

@@ -36,8 +36,8 @@ DMM_OK, DMM_EINVAL, DMM_ENODEV, DMM_ELAUNCH = 0, 1, 2, 3
 EXPORTS = (
     "dmm_status_str", "dmm_last_error", "quantize_per_token", "quantize_per_token_bf16", "quantize_blockscale_a",
     "quantize_blockscale_b", "quantize_mxfp8", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile",
-    "gemm_a8w8_ptpc_gathered", "gemm_a8w8_blockscale", "gemm_a8w8_mxfp8", "gemm_a8w8_mxfp8_tile", "gemm_bf16",
-    "gemm_bf16_tile",
+    "gemm_a8w8_ptpc_gathered", "gemm_a8w8_blockscale", "gemm_a8w8_blockscale_tile", "gemm_a8w8_mxfp8",
+    "gemm_a8w8_mxfp8_tile", "gemm_bf16", "gemm_bf16_tile",
 )
 
 _lib = None
@@ -64,6 +64,7 @@ def lib():
             getattr(L, name).argtypes = [P, P, P, P, P, I64, I64, I64, P]
         L.gemm_a8w8_ptpc_tile.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
         L.gemm_a8w8_mxfp8_tile.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
+        L.gemm_a8w8_blockscale_tile.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
         L.gemm_a8w8_ptpc_gathered.argtypes = [P, P, P, P, P, I64, I64, I64, P, I64, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_uint32, I64, P, P]
         L.gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
@@ -246,15 +247,24 @@ def gemm_a8w8_ptpc_gathered(a, b_shuf, a_scale, b_scale, flags, src_rows, nchunk
     return out, status
 
 
-def gemm_a8w8_blockscale(a, b_shuf, a_scale, b_scale, out=None):
-    """Blockscale GEMM: a_scale [K/128, M] fp32, b_scale [ceil(N/128), K/128] fp32."""
+BLOCKSCALE_TILES = {"128x256": 1, "128x128": 2}
+
+
+def gemm_a8w8_blockscale(a, b_shuf, a_scale, b_scale, out=None, tile="auto"):
+    """Blockscale GEMM: a_scale [K/128, M] fp32, b_scale [ceil(N/128), K/128] fp32.
+    tile: "auto" (the library's choice), "128x256" or "128x128" (same result)."""
     au, bu, out, m, n, k = _gemm_args(a, b_shuf, out)
     _require(a_scale, "a_scale", torch.float32, 2)
     _require(b_scale, "b_scale", torch.float32, 2)
     _shape(a_scale, (k // 128, m), "a_scale")
     _shape(b_scale, ((n + 127) // 128, k // 128), "b_scale")
-    _check(lib().gemm_a8w8_blockscale(_ptr(au), _ptr(bu), _ptr(a_scale), _ptr(b_scale), _ptr(out), m, n, k,
-                                      _stream()))
+    args = (_ptr(au), _ptr(bu), _ptr(a_scale), _ptr(b_scale), _ptr(out), m, n, k)
+    if tile == "auto":
+        _check(lib().gemm_a8w8_blockscale(*args, _stream()))
+    else:
+        if tile not in BLOCKSCALE_TILES:
+            raise ValueError(f"tile must be 'auto' or one of {sorted(BLOCKSCALE_TILES)} (got {tile!r})")
+        _check(lib().gemm_a8w8_blockscale_tile(*args, BLOCKSCALE_TILES[tile], _stream()))
     return out
 
 

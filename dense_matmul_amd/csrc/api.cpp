@@ -229,6 +229,13 @@ dmm_status gemm_a8w8_blockscale(const uint8_t* a, const uint8_t* b_shuf, const f
     return gemm_common(1, 0, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
 }
 
+dmm_status gemm_a8w8_blockscale_tile(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale,
+                                     const float* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k, int tile,
+                                     void* stream) {
+    REQUIRE(tile >= 0 && tile <= 2, "tile must be 0 (auto), 1 (128x256) or 2 (128x128) (got %d)", tile);
+    return gemm_common(1, tile, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
+}
+
 dmm_status gemm_a8w8_mxfp8(const uint8_t* a, const uint8_t* b_shuf, const uint8_t* a_scale, const uint8_t* b_scale,
                            uint16_t* c, int64_t m, int64_t n, int64_t k, void* stream) {
     return gemm_common(2, 0, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);

@@ -54,8 +54,17 @@ namespace dmm {
 
 // MODE_PTPC_N: ptpc on the 128 x 256 tile of eight waves (see Cfg);
 // MODE_PTPC_G: ptpc over a gathered A (Gather), 256 x 256 tiles;
-// MODE_MXFP8_N: mxfp8 on the 256 x 128 tile of four waves.
-enum { MODE_PTPC = 0, MODE_BLOCKSCALE = 1, MODE_MXFP8 = 2, MODE_PTPC_N = 3, MODE_PTPC_G = 4, MODE_MXFP8_N = 5 };
+// MODE_MXFP8_N: mxfp8 on the 256 x 128 tile of four waves;
+// MODE_BLOCKSCALE_N: blockscale on a 128 x 128 tile of four waves.
+enum {
+    MODE_PTPC = 0,
+    MODE_BLOCKSCALE = 1,
+    MODE_MXFP8 = 2,
+    MODE_PTPC_N = 3,
+    MODE_PTPC_G = 4,
+    MODE_MXFP8_N = 5,
+    MODE_BLOCKSCALE_N = 6
+};
 
 template <int MODE>
 constexpr bool kWidePtpc = MODE == MODE_PTPC || MODE == MODE_PTPC_G;
@@ -63,6 +72,8 @@ template <int MODE>
 constexpr bool kPtpc = kWidePtpc<MODE> || MODE == MODE_PTPC_N;
 template <int MODE>
 constexpr bool kMx = MODE == MODE_MXFP8 || MODE == MODE_MXFP8_N;
+template <int MODE>
+constexpr bool kBlock = MODE == MODE_BLOCKSCALE || MODE == MODE_BLOCKSCALE_N;
 
 constexpr int BK = 128;
 
@@ -143,10 +154,12 @@ constexpr bool store_nt_only(int k) { return k >= kLongK; }
 // on a 256 x 128 tile of four waves, each owning all 256 rows and 32
 // columns (matrix ops straight into VGPR accumulators): A, the operand that
 // goes through LDS, is twice the size of B in each K tile.
+// MODE_BLOCKSCALE_N runs the blockscale waves four to a 128 x 128 tile (one
+// per SIMD), which doubles the tile count of grids that would leave CUs
+// idle.
 template <int MODE>
 struct Cfg {
     static constexpr sched::Shape S = sched::shape_of(MODE);  // kpipe.h
-    static constexpr bool NARROW = MODE == MODE_BLOCKSCALE || MODE == MODE_PTPC_N;  // 128 x 256, 8 waves
     static constexpr int MB = S.MB;        // 16-row blocks per wave
     static constexpr int NBW = S.NBW;      // 16-column blocks per wave
     static constexpr int WAVES = S.WAVES;  // waves per workgroup
@@ -345,7 +358,7 @@ __device__ __forceinline__ void b_scales(Ctx<MODE>& x, TileRef r, int kt) {
         const int col = remap ? 2 * x.i + 8 * lone : 4 * x.i;
         const int boff = (4 * kt + x.g) * x.N + n0 + C::WN * x.w + col;
         x.sxb_raw[T] = __builtin_amdgcn_raw_buffer_load_b32(rsb, boff, 0, 0);
-    } else if constexpr (MODE == MODE_BLOCKSCALE) {
+    } else if constexpr (kBlock<MODE>) {
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x.sa, valid ? (uint32_t)x.KI * (uint32_t)x.M * 4u : 0u);
         const __amdgpu_buffer_rsrc_t rsb =
             make_rsrc(x.sb, valid ? (uint32_t)((x.N + 127) / 128) * (uint32_t)x.KI * 4u : 0u);
@@ -522,7 +535,7 @@ __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
 // make every later read of an accumulator depend on it.
 template <int MODE>
 __device__ __forceinline__ void mfma_drain(Ctx<MODE>& x) {
-    if constexpr (MODE != MODE_BLOCKSCALE) {
+    if constexpr (!kBlock<MODE>) {
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
         for (int mb = 0; mb < Cfg<MODE>::MB; ++mb)
@@ -1218,6 +1231,17 @@ int mxfp8_tile_for(int m, int n) {
     return half_tile_wins(wide, half, kMxfp8HalfCost) ? 2 : 1;
 }
 
+// blockscale: the 128 x 128 tile of four waves (one per SIMD, so no second
+// wave hides the fold's result latency) costs 0.64 of a 128 x 256 tile
+// (measured at 16384 x 7168 x 2048: 28 waves of the small tile 328 us, 14
+// waves of the wide one 256 us).
+constexpr double kBlockscaleHalfCost = 0.64;
+int blockscale_tile_for(int m, int n) {
+    const long wide = (long)((m + 127) / 128) * ((n + 255) / 256);
+    const long half = (long)((m + 127) / 128) * ((n + 127) / 128);
+    return half_tile_wins(wide, half, kBlockscaleHalfCost) ? 2 : 1;
+}
+
 hipError_t launch_gemm_a8w8(int mode, int tile, const uint8_t* a, const uint8_t* b, const void* sa, const void* sb,
                             uint16_t* c, int m, int n, int k, hipStream_t stream) {
     GemmArgs p{a, b, sa, sb, c, m, n, k, 0, 0};
@@ -1227,6 +1251,7 @@ hipError_t launch_gemm_a8w8(int mode, int tile, const uint8_t* a, const uint8_t*
     if (mode == MODE_MXFP8 && (tile == 0 ? mxfp8_tile_for(m, n) : tile) == 2) mode = MODE_MXFP8_N;
     if (mode == MODE_MXFP8) return launch_gemm<MODE_MXFP8>(p, stream);
     if (mode == MODE_MXFP8_N) return launch_gemm<MODE_MXFP8_N>(p, stream);
+    if ((tile == 0 ? blockscale_tile_for(m, n) : tile) == 2) return launch_gemm<MODE_BLOCKSCALE_N>(p, stream);
     return launch_gemm<MODE_BLOCKSCALE>(p, stream);
 }
 

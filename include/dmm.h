@@ -169,6 +169,17 @@ dmm_status gemm_a8w8_blockscale(const uint8_t* a, const uint8_t* b_shuf, const f
                                 const float* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k,
                                 void* stream);
 
+/* blockscale with an explicit output-tile shape, the same result as
+ * gemm_a8w8_blockscale: tile 1 = 128 x 256 (eight waves, two per SIMD),
+ * 2 = 128 x 128 (four waves), 0 = the choice gemm_a8w8_blockscale makes
+ * (128 x 128 when its waves over the compute units cost less than the
+ * 128 x 256 tile's, by the rule gemm_a8w8_mxfp8_tile describes; the pages
+ * tune one configuration per shape: aiter PR 6539, Motivation and the tuned
+ * rows of its review thread).  Other values of tile return DMM_EINVAL. */
+dmm_status gemm_a8w8_blockscale_tile(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale,
+                                     const float* b_scale, uint16_t* c, int64_t m, int64_t n, int64_t k, int tile,
+                                     void* stream);
+
 /* mxfp8: a_scale [k/32][m] and b_scale [k/32][n] E8M0 bytes, one per 32
  * consecutive K values.
  *   C[m, n] = bf16(sum_g 2^(a_scale[g][m]-127) 2^(b_scale[g][n]-127) sum_{k in g} A B).

@@ -31,7 +31,7 @@ def L():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("quantize_per_token", "quantize_per_token_bf16", "preshuffle_b", "gemm_a8w8_ptpc", "gemm_a8w8_ptpc_tile", "gemm_a8w8_ptpc_gathered",
-              "gemm_a8w8_blockscale",
+              "gemm_a8w8_blockscale", "gemm_a8w8_blockscale_tile",
               "gemm_a8w8_mxfp8", "gemm_a8w8_mxfp8_tile",
               "gemm_bf16", "gemm_bf16_tile", "quantize_blockscale_a", "quantize_blockscale_b", "quantize_mxfp8", "dmm_status_str",
               "dmm_last_error"):
@@ -43,6 +43,17 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_function(L):
     for name in declared_functions():
         assert hasattr(L, name), f"libdmm.so does not export {name}"
+
+
+def test_binding_declares_every_signature(L):
+    """Every function the binding exports has its ctypes argument types set
+    (an unset one would pass 64-bit sizes as 32-bit ints), and the list is
+    exactly the header's."""
+    import dense_matmul_amd as dmm
+
+    assert set(dmm.EXPORTS) == set(declared_functions())
+    for name in dmm.EXPORTS:
+        assert getattr(L, name).argtypes is not None, name
 
 
 def test_status_strings(L):
@@ -64,15 +75,16 @@ def test_gemm_shape_rules(L, m, n, k, why):
         assert why in L.dmm_last_error().decode()
 
 
-def test_ptpc_tile_rule(L):
-    """tile is 0 (auto), 1 (256x256) or 2 (128x256); anything else is an
-    argument error, reported before any HIP call."""
-    f = L.gemm_a8w8_ptpc_tile
+@pytest.mark.parametrize("name", ["gemm_a8w8_ptpc_tile", "gemm_a8w8_blockscale_tile", "gemm_a8w8_mxfp8_tile"])
+def test_tile_rule(L, name):
+    """tile is 0 (auto), 1 (the wide tile) or 2 (the half-size one);
+    anything else is an argument error, reported before any HIP call."""
+    f = getattr(L, name)
     f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_void_p]
     for tile in (-1, 3, 256):
         assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 64, 256, 256, tile, None) == 1
         assert b"tile must be" in L.dmm_last_error()
-    # shape rules apply as for gemm_a8w8_ptpc
+    # shape rules apply as for the call without a tile
     assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 64, 24, 256, 2, None) == 1
 
 

@@ -40,7 +40,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 ONE = 0x38  # E4M3 code of 1.0
-MODES = ["ptpc_w", "ptpc_n", "blockscale", "mxfp8", "mxfp8_n"]
+MODES = ["ptpc_w", "ptpc_n", "blockscale", "blockscale_n", "mxfp8", "mxfp8_n"]
 
 
 @pytest.fixture(scope="module")
@@ -77,8 +77,8 @@ def run(dmm, mode, qa, qb, sa, sb):
     a, s_a, s_b = dev(qa), dev(sa), dev(sb)
     if mode in ("ptpc_w", "ptpc_n"):
         c = dmm.gemm_a8w8_ptpc(a, b_shuf, s_a, s_b, tile={"ptpc_w": "256x256", "ptpc_n": "128x256"}[mode])
-    elif mode == "blockscale":
-        c = dmm.gemm_a8w8_blockscale(a, b_shuf, s_a, s_b)
+    elif mode.startswith("blockscale"):
+        c = dmm.gemm_a8w8_blockscale(a, b_shuf, s_a, s_b, tile={"blockscale": "128x256", "blockscale_n": "128x128"}[mode])
     else:
         c = dmm.gemm_a8w8_mxfp8(a, b_shuf, s_a, s_b, tile={"mxfp8": "256x256", "mxfp8_n": "256x128"}[mode])
     torch.cuda.synchronize()
@@ -97,7 +97,7 @@ def a_scales(mode, m, k, seed):
         e = rng.integers(120, 135, size=(k // 32, m)).astype(np.uint8)
         full = np.ldexp(np.float32(1), e.astype(np.int32) - 127).astype(np.float32)  # exact powers of two
         return e, np.repeat(full.T, 32, axis=1)
-    if mode == "blockscale":
+    if mode.startswith("blockscale"):
         s = rng.uniform(0.5, 2.0, size=(k // 128, m)).astype(np.float32)
         return s, np.repeat(s.T, 128, axis=1)
     s = rng.uniform(0.5, 2.0, size=(m,)).astype(np.float32)
@@ -107,7 +107,7 @@ def a_scales(mode, m, k, seed):
 def unit_b_scales(mode, n, k):
     if mode.startswith("mxfp8"):
         return np.full((k // 32, n), 127, np.uint8)
-    if mode == "blockscale":
+    if mode.startswith("blockscale"):
         return np.ones(((n + 127) // 128, k // 128), np.float32)
     return np.ones((n,), np.float32)
 
@@ -179,7 +179,7 @@ def test_doubling_a_scales_doubles_c(dmm, mode):
     N(0,1) data where the sums are inexact."""
     m, n, k = 300, 1168, 1792
     announce("doubling", mode, m, n, k)
-    base = "ptpc" if mode.startswith("ptpc") else "mxfp8" if mode.startswith("mxfp8") else mode
+    base = "ptpc" if mode.startswith("ptpc") else "mxfp8" if mode.startswith("mxfp8") else "blockscale"
     a = inputs.normal((m, k), 930)
     b = inputs.normal((n, k), 931)
     quant = {"ptpc": (oracle.quantize_per_token, oracle.quantize_per_token),

@@ -170,12 +170,14 @@ def test_preshuffle_is_the_documented_permutation(dmm, n, k):
 PTPC_TILE = {"ptpc": "auto", "ptpc_w": "256x256", "ptpc_n": "128x256"}
 # mxfp8 likewise: "mxfp8" forces the 256x256 tile, "mxfp8_n" the 256x128 one
 MXFP8_TILE = {"mxfp8": "256x256", "mxfp8_n": "256x128", "mxfp8_auto": "auto"}
+# blockscale: "blockscale" forces the 128x256 tile, "blockscale_n" the 128x128 one
+BLOCKSCALE_TILE = {"blockscale": "128x256", "blockscale_n": "128x128", "blockscale_auto": "auto"}
 MODE_ID = {"ptpc": 0, "blockscale": 1, "mxfp8": 2}
-GEMM_MODES = ["ptpc_w", "ptpc_n", "blockscale", "mxfp8", "mxfp8_n"]
+GEMM_MODES = ["ptpc_w", "ptpc_n", "blockscale", "blockscale_n", "mxfp8", "mxfp8_n"]
 
 
 def base_mode(mode):
-    return "ptpc" if mode in PTPC_TILE else "mxfp8" if mode in MXFP8_TILE else mode
+    return "ptpc" if mode in PTPC_TILE else "mxfp8" if mode in MXFP8_TILE else "blockscale"
 
 
 def gemm_fn(dmm, mode):
@@ -183,11 +185,11 @@ def gemm_fn(dmm, mode):
         return lambda *args, **kw: dmm.gemm_a8w8_ptpc(*args, tile=PTPC_TILE[mode], **kw)
     if mode in MXFP8_TILE:
         return lambda *args, **kw: dmm.gemm_a8w8_mxfp8(*args, tile=MXFP8_TILE[mode], **kw)
-    return dmm.gemm_a8w8_blockscale
+    return lambda *args, **kw: dmm.gemm_a8w8_blockscale(*args, tile=BLOCKSCALE_TILE[mode], **kw)
 
 
 def tile_rows(mode):
-    return 128 if mode in ("blockscale", "ptpc_n") else 256
+    return 128 if mode in ("blockscale", "blockscale_n", "ptpc_n") else 256
 
 
 def quantised_operands(mode, m, n, k, seed_a, seed_b):
@@ -231,8 +233,9 @@ def exact_operands(mode, m, n, k, seed):
 
 
 # N % 64 = 16, 16, 16, 0, 16, 48, 32, 32: every kind of last column group
+# K = 4096 takes the other C store policy of the 256-wide tiles
 EXACT_SHAPES = [(1, 16, 128), (17, 272, 256), (300, 1168, 384), (256, 256, 512), (513, 528, 640), (64, 48, 1792),
-                (130, 1120, 256), (40, 32, 128)]
+                (130, 1120, 256), (40, 32, 128), (260, 272, 4096)]
 
 
 @pytest.mark.parametrize("mode", GEMM_MODES)
@@ -289,7 +292,7 @@ def run_poisoned(dmm, mode, qa, qb, sa, sb, launches, hog=False):
     return outs
 
 
-@pytest.mark.parametrize("mode", ["ptpc", "ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale"])
+@pytest.mark.parametrize("mode", ["ptpc", "ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale", "blockscale_n"])
 @pytest.mark.parametrize("m,n,k,seed_a,seed_b", [(4096, 7168, 256, 11, 12), (16384, 7168, 512, 21, 22)])
 def test_race_shapes_bit_stable_and_correct(dmm, mode, m, n, k, seed_a, seed_b):
     """The pages' race shapes (mori PR 785, Test table), in every mode and
@@ -308,7 +311,7 @@ def test_race_shapes_bit_stable_and_correct(dmm, mode, m, n, k, seed_a, seed_b):
     check_close(outs[0][rows], ref, f"{mode} {m}x{n}x{k} sampled rows", base_mode(mode), (qa, qb, sa, sb), rows)
 
 
-@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale"])
+@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale", "blockscale_n"])
 def test_bit_stable_under_concurrent_copy(dmm, mode):
     """Same 20-launch identity with an HBM copy loop on a second stream."""
     m, n, k = 4096, 7168, 256
@@ -375,7 +378,7 @@ def test_invalid_arguments_raise_value_error(dmm):
                            torch.ones(16, dtype=torch.float32, device=DEV))
 
 
-@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale"])
+@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale", "blockscale_n"])
 @pytest.mark.parametrize("k", [128, 256, 384, 512, 640])
 def test_many_tiles_per_workgroup_every_k_phase(dmm, mode, k):
     """More tiles than CUs, so every workgroup runs 2-3 tiles back to back,

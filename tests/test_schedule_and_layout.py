@@ -86,7 +86,8 @@ def shim(tmp_path_factory):
 
 # ---------------------------------------------------------------- schedule
 # the kernel's modes (kpipe.h, shape_of): name -> mode id
-MODE_IDS = {"ptpc": 0, "blockscale": 1, "mxfp8": 2, "ptpc_128x256": 3, "ptpc_gathered": 4, "mxfp8_256x128": 5}
+MODE_IDS = {"ptpc": 0, "blockscale": 1, "mxfp8": 2, "ptpc_128x256": 3, "ptpc_gathered": 4, "mxfp8_256x128": 5,
+            "blockscale_128x128": 6}
 
 
 def _shapes():
@@ -106,7 +107,7 @@ def test_mode_shapes_are_the_documented_loads():
     = 2 MB / waves A DMAs and NB = 2 NBW B fragment halves (+ 3 scale loads
     for mxfp8 and blockscale); the ptpc tiles add 2 epilogue-scale DMAs."""
     assert MODES == {"ptpc": (8, 8, 2), "blockscale": (2, 7, 0), "mxfp8": (8, 11, 0), "ptpc_128x256": (2, 4, 2),
-                     "ptpc_gathered": (8, 8, 2), "mxfp8_256x128": (8, 7, 0)}
+                     "ptpc_gathered": (8, 8, 2), "mxfp8_256x128": (8, 7, 0), "blockscale_128x128": (4, 7, 0)}
 
 
 def program(L, KI, ntiles, NA, NB, NSC, wait_fn=None):
@@ -279,8 +280,8 @@ def test_checker_catches_a_missing_war_barrier(shim):
 
 
 # ------------------------------------------------------------------ layout
-# (row blocks per stage / 16, waves): ptpc and mxfp8, blockscale
-LAYOUTS = [(16, 4), (8, 8)]
+# (row blocks per stage / 16, waves): ptpc and mxfp8, the 8-wave 128-row tiles, blockscale 128 x 128
+LAYOUTS = [(16, 4), (8, 8), (8, 4)]
 
 
 def dma_blocks(MB, waves):

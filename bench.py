@@ -288,6 +288,18 @@ def traffic_from_profiles(kernel_tag):
     return d.get("bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(m, n, k, rows_n, gpu_c=None):
     """The oracle, untouched, on ``rows_n`` evenly spaced rows of the headline
     workload (all of it by default) with every thread of this process's CPU
@@ -301,8 +313,10 @@ def cpu_baseline(m, n, k, rows_n, gpu_c=None):
 
     a = inputs.normal((m, k), 31)
     b = inputs.normal((n, k), 32)
+    tq = time.perf_counter()
     qa, sa = oracle.quantize_per_token(a)
     qb, sb = oracle.quantize_per_token(b)
+    tq = time.perf_counter() - tq
     rows_n = min(rows_n, m)
     rows = np.linspace(0, m - 1, rows_n).astype(np.int64) if rows_n < m else None
     # every host thread of this process's CPU share (OMP_NUM_THREADS caps it
@@ -314,7 +328,10 @@ def cpu_baseline(m, n, k, rows_n, gpu_c=None):
     flops = 2.0 * rows_n * n * k
     res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
            "sample": (f"{rows_n} evenly spaced rows of {m}" if rows_n < m else f"all {m} rows") +
-                     f" (all {n} columns, K={k}), GEMM only, {dt:.1f} s"}
+                     f" (all {n} columns, K={k}), GEMM only, {dt:.1f} s",
+           "cpu_model": cpu_model(),
+           # the quantisation of both operands, timed apart from the GEMM (one thread)
+           "quantize": {"s": round(tq, 3), "GB/s": round((m + n) * k * 5 / tq / 1e9, 2), "threads": 1}}
     if gpu_c is not None:
         from oracle import tolerance
 

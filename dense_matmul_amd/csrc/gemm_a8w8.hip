@@ -112,8 +112,8 @@ constexpr int kDppRowNewBcast = 0x150;  // + k: lane k of each 16-lane row to th
 // same wave's next store).  Non-temporal (nt) keeps C from displacing the A
 // and B panels in the L2, which pays when K is long; with short K the C
 // write dominates and device scope (sc1) on top of nt writes the lines out
-// faster (measured: 4096 x 7168 x 256 14.2 vs 20.7 us, 32768 x 7168 x 1792
-// 318.6 vs 319.0 us, 32768 x 6288 x 7168 1082 vs 1011 us).
+// faster (measured, nt + sc1 vs nt: 4096 x 7168 x 256 14.3 vs 20.7 us,
+// 32768 x 7168 x 1792 318.6 vs 319.0 us, 32768 x 6288 x 7168 1082 vs 1011 us).
 constexpr int kStoreNt = 2;
 constexpr int kStoreNtSc1 = 18;
 constexpr int kLongK = 4096;  // K at or above which the stores are nt only
@@ -152,8 +152,8 @@ constexpr bool store_nt_only(int k) { return k >= kLongK; }
 // ptpc on that narrow tile (matrix ops straight into VGPR accumulators),
 // which doubles the tile count of small problems.  MODE_MXFP8_N runs mxfp8
 // on a 256 x 128 tile of four waves, each owning all 256 rows and 32
-// columns (matrix ops straight into VGPR accumulators): A, the operand that
-// goes through LDS, is twice the size of B in each K tile.
+// columns (128 AGPR accumulators): A, the operand that goes through LDS, is
+// twice the size of B in each K tile.
 // MODE_BLOCKSCALE_N runs the blockscale waves four to a 128 x 128 tile (one
 // per SIMD), which doubles the tile count of grids that would leave CUs
 // idle.

@@ -75,8 +75,8 @@ def parse():
                         "instruction interleaved with the matrix ops costs)")
     p.add_argument("--no-ceiling", action="store_true", help="skip the calibration-kernel context")
     p.add_argument("--workload", default=None,
-                   help="run only this workload (a key of dense_matmul_amd.inputs.WORKLOADS): --warmup then "
-                        "--steps eager launches, one short JSON line; for rocprofv3")
+                   help="run only this workload (a key of dense_matmul_amd.inputs.WORKLOADS, or a quantiser of "
+                        "QUANTISERS): --warmup then --steps eager launches, one short JSON line; for rocprofv3")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 1 GiB HBM copy kernel 3 times (the reference dispatch for "
                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -512,12 +512,43 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
+# The quantisers on the configured shapes' operands: name -> (binding
+# function, rows, cols, scale bytes).  Algorithmic bytes = fp32 in + codes +
+# scales.
+QUANTISERS = {
+    "quantize_per_token_32768x1792": ("quantize_per_token", 32768, 1792, lambda r, c: 4 * r),
+    "quantize_per_token_32768x7168": ("quantize_per_token", 32768, 7168, lambda r, c: 4 * r),
+    "quantize_per_token_7168x1792": ("quantize_per_token", 7168, 1792, lambda r, c: 4 * r),
+    "quantize_blockscale_a_16384x2048": ("quantize_blockscale_a", 16384, 2048, lambda r, c: 4 * r * c // 128),
+    "quantize_blockscale_b_7168x2048": ("quantize_blockscale_b", 7168, 2048,
+                                        lambda r, c: 4 * ((r + 127) // 128) * (c // 128)),
+    "quantize_mxfp8_32768x1792": ("quantize_mxfp8", 32768, 1792, lambda r, c: r * c // 32),
+    "quantize_mxfp8_7168x1792": ("quantize_mxfp8", 7168, 1792, lambda r, c: r * c // 32),
+}
+
+
+def quantiser_bytes(name):
+    _, rows, cols, scale_bytes = QUANTISERS[name]
+    return 5 * rows * cols + scale_bytes(rows, cols)
+
+
 def run_workload(dmm, torch, name, steps, warmup):
-    """One named workload: operands as the bench builds them, ``warmup``
-    launches, then ``steps`` launches, eagerly on the current stream (so a
-    profiler sees each dispatch), then a synchronisation."""
+    """One named workload (a GEMM of inputs.WORKLOADS or a quantiser of
+    QUANTISERS): operands as the bench builds them, ``warmup`` launches,
+    then ``steps`` launches, eagerly on the current stream (so a profiler
+    sees each dispatch), then a synchronisation."""
     from dense_matmul_amd import inputs
 
+    if name in QUANTISERS:
+        fname, rows, cols, _ = QUANTISERS[name]
+        x = torch.from_numpy(inputs.normal((rows, cols), 3)).to("cuda:0")
+        fn = lambda: getattr(dmm, fname)(x)
+        repeat(fn, warmup)
+        torch.cuda.synchronize()
+        ms = event_ms(lambda: repeat(fn, steps), steps)
+        print(json.dumps({"workload": name, "launches": steps, "us_per_launch": round(ms * 1e3, 2),
+                          "alg_GB/s": round(quantiser_bytes(name) / (ms * 1e-3) / 1e9)}), flush=True)
+        return
     mode, m, n, k, seed_a, seed_b = inputs.WORKLOADS[name]
     if mode == "bf16":
         a32, b_kn = inputs.bf16_operands(m, k, n, seed_a)
@@ -575,20 +606,13 @@ def extra_shapes(dmm, torch, args):
     from dense_matmul_amd import inputs
 
     # the quantisers (run before the GEMM, not in its time), on the configured
-    # shapes' operands: algorithmic bytes = fp32 in + codes + scales
-    for name, fn, rows, cols, extra_bytes in [
-            ("quantize_per_token_32768x1792", dmm.quantize_per_token, 32768, 1792, lambda r, c: 4 * r),
-            ("quantize_per_token_32768x7168", dmm.quantize_per_token, 32768, 7168, lambda r, c: 4 * r),
-            ("quantize_per_token_7168x1792", dmm.quantize_per_token, 7168, 1792, lambda r, c: 4 * r),
-            ("quantize_blockscale_a_16384x2048", dmm.quantize_blockscale_a, 16384, 2048, lambda r, c: 4 * r * c // 128),
-            ("quantize_blockscale_b_7168x2048", dmm.quantize_blockscale_b, 7168, 2048,
-             lambda r, c: 4 * ((r + 127) // 128) * (c // 128)),
-            ("quantize_mxfp8_32768x1792", dmm.quantize_mxfp8, 32768, 1792, lambda r, c: r * c // 32),
-            ("quantize_mxfp8_7168x1792", dmm.quantize_mxfp8, 7168, 1792, lambda r, c: r * c // 32)]:
+    # shapes' operands
+    for name, (fname, rows, cols, _) in QUANTISERS.items():
+        fn = getattr(dmm, fname)
         x = torch.from_numpy(inputs.normal((rows, cols), 3)).to("cuda:0")
         t = timed_arms({"q_eager": lambda: fn(x)}, 100, 20, warm_s)
         ms = t["q_eager"]["median"]
-        gbs = (5 * rows * cols + extra_bytes(rows, cols)) / (ms * 1e-3) / 1e9
+        gbs = quantiser_bytes(name) / (ms * 1e-3) / 1e9
         res[name] = {"us": round(ms * 1e3, 1), "alg_GB/s": round(gbs), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
         del x
         torch.cuda.empty_cache()

@@ -48,6 +48,47 @@ __device__ __forceinline__ uint32_t pack4(v4f v, float s) {
     return e4m3_code(v[0] / s) | (e4m3_code(v[1] / s) << 8) | (e4m3_code(v[2] / s) << 16) | (e4m3_code(v[3] / s) << 24);
 }
 
+// The hardware conversion v_cvt_pk_fp8_f32 (OCP E4M3, round to nearest even)
+// returns e4m3_code's byte for every fp32 input of magnitude below 464 (the
+// two were compared over all 2^32 bit patterns on gfx950); at 464 and above,
+// for infinities and for NaN they differ, so those inputs never reach it.
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// Quantisation by a scale s: the code of each value v is e4m3_code of the
+// quotient v / s rounded to fp32.  A correctly rounded fp32 division costs
+// about ten instructions per value; instead y = v * r, with r = 1 / s
+// rounded once, is within 3 fp32 ulps of the rounded quotient (two
+// roundings of relative size at most 2^-24 in y, one more in the quotient).
+// Two values that close round to the same E4M3 code unless an E4M3 rounding
+// midpoint lies between them, and a midpoint has its fp32 fraction bits 19..0
+// equal to 0x80000 wherever |y| >= 2^-6 (three fraction bits survive), so y
+// is encoded directly when it is zero, or when 2^-6 <= |y| < 464 and those
+// bits are more than 5 ulps from 0x80000.  Every other value -- tiny, near a
+// midpoint, non-finite, or under a scale whose reciprocal is not normal (r
+// is NaN then, and so is y) -- takes the division.
+struct DivQuant {
+    float s, r;
+    __device__ __forceinline__ explicit DivQuant(float scale)
+        : s(scale), r(scale >= 0x1p-126f && scale <= 0x1p126f ? 1.0f / scale : __builtin_nanf("")) {}
+    // 1 if y may be encoded directly (bitwise operators throughout: one
+    // flag per lane, no branch per value)
+    __device__ __forceinline__ static uint32_t direct(float y) {
+        const uint32_t au = __builtin_bit_cast(uint32_t, y) & 0x7FFFFFFFu;
+        const uint32_t in_range = au - 0x3C800000u < 0x43E80000u - 0x3C800000u;  // 2^-6 <= |y| < 464
+        const uint32_t far_mid = (au & 0xFFFFFu) - 0x7FFFBu > 10u;                // > 5 ulps from a midpoint
+        return (uint32_t)(au == 0) | (in_range & far_mid);
+    }
+    __device__ __forceinline__ uint32_t pack(v4f v) const {
+        const float y0 = v[0] * r, y1 = v[1] * r, y2 = v[2] * r, y3 = v[3] * r;
+        uint32_t w = cvt4(y0, y1, y2, y3);
+        if (!(direct(y0) & direct(y1) & direct(y2) & direct(y3))) w = pack4(v, s);
+        return w;
+    }
+};
+
 // ------------------------------------------------------------- per token
 // One wave per row; 4 rows per workgroup.  cols % 16 == 0.
 // Four consecutive values of a row as fp32: fp32 rows load 16 bytes, bf16
@@ -82,25 +123,28 @@ __global__ void __launch_bounds__(256) quantize_rows_reg_kernel(const In* __rest
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
     }
     const float s = amax_to_scale(wave_max(amax));
+    const DivQuant dq(s);
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
         const int c = lane + 64 * j;
-        if (c < n4) qr[c] = pack4(v[j], s);
+        if (c < n4) qr[c] = dq.pack(v[j]);
     }
     if (lane == 0) scale[row] = s;
 }
 
-// Rows of 2049 .. 7168 columns: two waves per row, each holding every other
-// 64-chunk slice of it (NC chunks per lane), their maxima combined through
-// LDS; half the registers of one wave per row, so twice the rows in flight.
-template <typename In, int NC>
-__global__ void __launch_bounds__(256) quantize_rows_pair_kernel(const In* __restrict__ x, uint8_t* __restrict__ q,
-                                                                 float* __restrict__ scale, int rows, int cols) {
+// Rows of 2049 .. 7168 columns: W (2 or 4) waves per row, wave h holding
+// the 64-chunk slices h, h + W, h + 2W, ... of it (NC chunks per lane), their
+// maxima combined through LDS; 1/W of the registers of one wave per row, so
+// W times the rows in flight.
+template <typename In, int NC, int W>
+__global__ void __launch_bounds__(256) quantize_rows_split_kernel(const In* __restrict__ x, uint8_t* __restrict__ q,
+                                                                  float* __restrict__ scale, int rows, int cols) {
+    static_assert(W == 2 || W == 4, "two or four waves per row");
     __shared__ float red[4];
-    const int w = threadIdx.x >> 6, h = w & 1;
-    const int row = blockIdx.x * 2 + (w >> 1);
+    const int w = threadIdx.x >> 6, h = w % W, first = w - h;
+    const int row = blockIdx.x * (4 / W) + w / W;
     const int lane = threadIdx.x & 63;
-    const bool live = row < rows;  // both waves of a pair agree; every wave reaches the barrier
+    const bool live = row < rows;  // the W waves of a row agree; every wave reaches the barrier
     const In* xr = x + (size_t)(live ? row : 0) * cols;
     uint32_t* qr = (uint32_t*)(q + (size_t)(live ? row : 0) * cols);
     const int n4 = cols / 4;
@@ -108,19 +152,23 @@ __global__ void __launch_bounds__(256) quantize_rows_pair_kernel(const In* __res
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-        const int c = lane + 64 * (2 * j + h);
+        const int c = lane + 64 * (W * j + h);
         v[j] = live && c < n4 ? load4(xr, c) : (v4f){0.f, 0.f, 0.f, 0.f};
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
     }
     amax = wave_max(amax);
     if (lane == 0) red[w] = amax;
     __syncthreads();
-    const float s = amax_to_scale(fmaxf(red[w & 2], red[(w & 2) + 1]));
+    float m = red[first];
+#pragma unroll
+    for (int o = 1; o < W; ++o) m = fmaxf(m, red[first + o]);
+    const float s = amax_to_scale(m);
     if (!live) return;
+    const DivQuant dq(s);
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-        const int c = lane + 64 * (2 * j + h);
-        if (c < n4) qr[c] = pack4(v[j], s);
+        const int c = lane + 64 * (W * j + h);
+        if (c < n4) qr[c] = dq.pack(v[j]);
     }
     if (lane == 0 && h == 0) scale[row] = s;
 }
@@ -140,7 +188,8 @@ __global__ void __launch_bounds__(256) quantize_rows_kernel(const In* __restrict
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     }
     const float s = amax_to_scale(wave_max(amax));
-    for (int c = lane; c < n4; c += 64) qr[c] = pack4(load4(xr, c), s);
+    const DivQuant dq(s);
+    for (int c = lane; c < n4; c += 64) qr[c] = dq.pack(load4(xr, c));
     if (lane == 0) scale[row] = s;
 }
 
@@ -162,7 +211,7 @@ __global__ void __launch_bounds__(256) quantize_blockscale_a_kernel(const float*
         float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
         const float s = amax_to_scale(group_max(a, 32));
         if (valid) {
-            qr[c] = pack4(v, s);
+            qr[c] = DivQuant(s).pack(v);
             if ((lane & 31) == 0) scale[(size_t)(c / 32) * m + row] = s;
         }
     }
@@ -193,10 +242,11 @@ __global__ void __launch_bounds__(256) quantize_blockscale_b_kernel(const float*
     if ((t & 63) == 0) red[t >> 6] = amax;
     __syncthreads();
     const float s = amax_to_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    const DivQuant dq(s);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int r = r0 + 8 * j;
-        if (r < rows) *(uint32_t*)(q + (size_t)(nb * 128 + r) * k + kb * 128 + col4 * 4) = pack4(v[j], s);
+        if (r < rows) *(uint32_t*)(q + (size_t)(nb * 128 + r) * k + kb * 128 + col4 * 4) = dq.pack(v[j]);
     }
     if (t == 0) scale[(size_t)nb * kblocks + kb] = s;
 }
@@ -235,8 +285,15 @@ __global__ void __launch_bounds__(256) quantize_mxfp8_kernel(const float* __rest
         float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
         const int e = mx_exp(group_max(a, 8));
         if (valid) {
-            qr[c] = e4m3_code(__builtin_ldexpf(v[0], -e)) | (e4m3_code(__builtin_ldexpf(v[1], -e)) << 8) |
-                    (e4m3_code(__builtin_ldexpf(v[2], -e)) << 16) | (e4m3_code(__builtin_ldexpf(v[3], -e)) << 24);
+            // scaling by 2^-e is exact (or one rounding into the subnormals)
+            // and leaves |q| <= 448 for finite v; NaN and infinities (the bit
+            // test below is false for both) take the bit-arithmetic encoder
+            const float q0 = __builtin_ldexpf(v[0], -e), q1 = __builtin_ldexpf(v[1], -e);
+            const float q2 = __builtin_ldexpf(v[2], -e), q3 = __builtin_ldexpf(v[3], -e);
+            auto small = [](float f) { return (__builtin_bit_cast(uint32_t, f) & 0x7FFFFFFFu) < 0x43E80000u; };
+            qr[c] = small(q0) && small(q1) && small(q2) && small(q3)
+                        ? cvt4(q0, q1, q2, q3)
+                        : e4m3_code(q0) | (e4m3_code(q1) << 8) | (e4m3_code(q2) << 16) | (e4m3_code(q3) << 24);
             if ((lane & 7) == 0) scale[(size_t)(c / 8) * rows + row] = (uint8_t)(e + 127);
         }
     }
@@ -269,16 +326,16 @@ __global__ void __launch_bounds__(256) preshuffle_b_kernel(const uint8_t* __rest
 }
 
 // -------------------------------------------------------------- launch
-// Per-token quantisation: one wave per row held in registers up to 2048
-// columns, a pair of waves per row up to 7168 (8 or 14 chunks per lane of
-// each), the two-pass kernel beyond.
+// Per-token quantisation, rows held in registers up to 7168 columns: one
+// wave per row up to 2048 columns, two up to 4096 (8 chunks per lane each),
+// four up to 7168 (7 each); the two-pass kernel beyond.
 template <typename In>
 static hipError_t launch_rows(const In* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st) {
-    const dim3 g4((rows + 3) / 4), g2((rows + 1) / 2), b(256);
+    const dim3 g4((rows + 3) / 4), g2((rows + 1) / 2), g1(rows), b(256);
     const int chunks = (cols / 4 + 63) / 64;  // 64-lane slices of 16-byte chunks in a row
     if (chunks <= 8) hipLaunchKernelGGL((quantize_rows_reg_kernel<In, 8>), g4, b, 0, st, x, q, s, rows, cols);
-    else if (chunks <= 16) hipLaunchKernelGGL((quantize_rows_pair_kernel<In, 8>), g2, b, 0, st, x, q, s, rows, cols);
-    else if (chunks <= 28) hipLaunchKernelGGL((quantize_rows_pair_kernel<In, 14>), g2, b, 0, st, x, q, s, rows, cols);
+    else if (chunks <= 16) hipLaunchKernelGGL((quantize_rows_split_kernel<In, 8, 2>), g2, b, 0, st, x, q, s, rows, cols);
+    else if (chunks <= 28) hipLaunchKernelGGL((quantize_rows_split_kernel<In, 7, 4>), g1, b, 0, st, x, q, s, rows, cols);
     else hipLaunchKernelGGL(quantize_rows_kernel<In>, g4, b, 0, st, x, q, s, rows, cols);
     return hipGetLastError();
 }

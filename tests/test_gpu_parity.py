@@ -127,6 +127,84 @@ def test_quantize_mxfp8_bitexact(dmm, rows, k, seed):
     assert np.array_equal(q.view(torch.uint8).cpu().numpy(), oq)
 
 
+def e4m3_grid():
+    """The non-negative finite E4M3 values in increasing order: 7 subnormal
+    steps of 2^-9, then (1 + f/8) 2^(e-7) for exponent fields 1..15 (the
+    all-ones fraction of field 15 is NaN)."""
+    vals = [c / 512.0 for c in range(8)]
+    vals += [(1 + f / 8.0) * 2.0 ** (e - 7) for e in range(1, 16) for f in range(8) if not (e == 15 and f == 7)]
+    return np.array(vals)
+
+
+def nudged(values, ulps):
+    """float32 values moved by each of ``ulps`` units in the last place
+    (values > 0, so a step of the bit pattern is a step of one ulp)."""
+    b = np.asarray(values, np.float32).view(np.int32)
+    return np.concatenate([(b + u).view(np.float32) for u in ulps])
+
+
+def midpoint_matrix(rows_per_scale, k, group, amax_of, scales, seed):
+    """Rows in bands of ``rows_per_scale``, band i quantised under scale
+    ``scales[i]``: every ``group`` values along a row start with the group's
+    maximum amax_of(scale) (so the group's scale is the band's) and the rest
+    are drawn from values whose quotient by that scale lands within 6 ulps
+    of an E4M3 rounding midpoint or grid point, with either sign, plus zeros
+    and values under 2^-6 of the scale."""
+    grid = e4m3_grid()
+    mids = (grid[:-1] + grid[1:]) / 2
+    rng = np.random.default_rng(seed)
+    x = np.empty((rows_per_scale * len(scales), k), np.float32)
+    for i, sc in enumerate(scales):
+        pool = nudged(np.concatenate([mids, grid[1:]]) * sc, range(-6, 7))
+        pool = np.concatenate([pool, np.float32(sc) * np.array([0.0, 2.0 ** -7, 2.0 ** -11, 1e-3], np.float32)])
+        band = rng.choice(pool, size=(rows_per_scale, k)) * rng.choice(np.array([-1, 1], np.float32), (rows_per_scale, k))
+        band[:, ::group] = np.float32(amax_of(sc))
+        x[i * rows_per_scale:(i + 1) * rows_per_scale] = band
+    return x
+
+
+# scales of no special form, a power of two, and a subnormal one (the scale
+# of a group whose maximum is 1e-38 is below 2^-126)
+DIV_SCALES = [1.3, 0.0071, 97.31, 2.0, 3.0e-30, 1e-38 / 448]
+
+
+def test_quantizers_near_rounding_midpoints_bitexact(dmm):
+    """Quotients within a few ulps of E4M3 rounding midpoints: the GPU
+    quantisers encode v / s through a product with the reciprocal and the
+    hardware converter, and fall back to the division only near midpoints,
+    so these are the values where a wrong window or a wrong rounding would
+    show.  Codes and scales must match the oracle bitwise."""
+    x = midpoint_matrix(128, 3328, 128, lambda sc: np.float32(448.0 * sc), DIV_SCALES, 31)
+    announce("quantizers near midpoints", x.shape)
+    for name in ("quantize_per_token", "quantize_blockscale_a", "quantize_blockscale_b"):
+        q, s = getattr(dmm, name)(to_dev(x))
+        oq, os_ = getattr(oracle, name)(x)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32)), name
+        got = q.view(torch.uint8).cpu().numpy()
+        bad = np.argwhere(got != oq)
+        assert bad.size == 0, (name, len(bad), [(int(r), int(c), float(x[r, c]), int(got[r, c]), int(oq[r, c]))
+                                                 for r, c in bad[:5]])
+    # bf16 input: the same values rounded to bf16 (a coarser set, still near midpoints)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    q, s = dmm.quantize_per_token(xb.to(DEV))
+    oq, os_ = oracle.quantize_per_token(xb.to(torch.float32).numpy())
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), oq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
+def test_quantize_mxfp8_near_rounding_midpoints_bitexact(dmm):
+    """mxfp8 scales by a power of two exactly, so values at E4M3 midpoints
+    times the group's power of two are exact ties (round to even) and their
+    ulp neighbours fall either side; the hardware converter must encode them
+    as the oracle does."""
+    x = midpoint_matrix(32, 3328, 32, lambda sc: np.float32(448.0 * sc), [2.0 ** -3, 2.0 ** 5, 2.0 ** -60], 32)
+    announce("quantize_mxfp8 near midpoints", x.shape)
+    q, e = dmm.quantize_mxfp8(to_dev(x))
+    oq, oe = oracle.quantize_mxfp8(x)
+    assert np.array_equal(e.cpu().numpy(), oe)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), oq)
+
+
 # ------------------------------------------------------------ preshuffle
 def documented_src_row(j, r, n):
     """B row held by fragment row r of block j, as include/dmm.h and

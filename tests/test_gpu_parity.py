@@ -163,9 +163,10 @@ def midpoint_matrix(rows_per_scale, k, group, amax_of, scales, seed):
     return x
 
 
-# scales of no special form, a power of two, and a subnormal one (the scale
-# of a group whose maximum is 1e-38 is below 2^-126)
-DIV_SCALES = [1.3, 0.0071, 97.31, 2.0, 3.0e-30, 1e-38 / 448]
+# scales of no special form, a power of two, one near the top of the fp32
+# range (maximum 2.7e38), and a subnormal one (the scale of a group whose
+# maximum is 1e-38 is below 2^-126)
+DIV_SCALES = [1.3, 0.0071, 97.31, 2.0, 3.0e-30, 6.0e35, 1e-38 / 448]
 
 
 def test_quantizers_near_rounding_midpoints_bitexact(dmm):
@@ -197,7 +198,7 @@ def test_quantize_mxfp8_near_rounding_midpoints_bitexact(dmm):
     times the group's power of two are exact ties (round to even) and their
     ulp neighbours fall either side; the hardware converter must encode them
     as the oracle does."""
-    x = midpoint_matrix(32, 3328, 32, lambda sc: np.float32(448.0 * sc), [2.0 ** -3, 2.0 ** 5, 2.0 ** -60], 32)
+    x = midpoint_matrix(32, 3328, 32, lambda sc: np.float32(448.0 * sc), [2.0 ** -3, 2.0 ** 5, 2.0 ** -60, 2.0 ** 118], 32)
     announce("quantize_mxfp8 near midpoints", x.shape)
     q, e = dmm.quantize_mxfp8(to_dev(x))
     oq, oe = oracle.quantize_mxfp8(x)

@@ -76,7 +76,7 @@ def parse():
     p.add_argument("--no-ceiling", action="store_true", help="skip the calibration-kernel context")
     p.add_argument("--workload", default=None,
                    help="run only this workload (a key of dense_matmul_amd.inputs.WORKLOADS, or a quantiser of "
-                        "QUANTISERS): --warmup then --steps eager launches, one short JSON line; for rocprofv3")
+                        "QUANTISERS, PRESHUFFLES): --warmup then --steps eager launches, one short JSON line; for rocprofv3")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 1 GiB HBM copy kernel 3 times (the reference dispatch for "
                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -527,9 +527,31 @@ QUANTISERS = {
 }
 
 
+# The one-time B preshuffle on the headline's B: name -> (N, K); it reads
+# and writes N K bytes.
+PRESHUFFLES = {"preshuffle_b_7168x1792": (7168, 1792)}
+
+
 def quantiser_bytes(name):
+    if name in PRESHUFFLES:
+        n, k = PRESHUFFLES[name]
+        return 2 * n * k
     _, rows, cols, scale_bytes = QUANTISERS[name]
     return 5 * rows * cols + scale_bytes(rows, cols)
+
+
+def prep_fn(dmm, torch, name):
+    """A launch of quantiser or preshuffle ``name`` on its synthetic input."""
+    from dense_matmul_amd import inputs
+
+    if name in PRESHUFFLES:
+        n, k = PRESHUFFLES[name]
+        b = torch.from_numpy(inputs.normal((n, k), 4)).to("cuda:0").to(torch.float8_e4m3fn)
+        out = torch.empty_like(b)
+        return lambda: dmm.preshuffle_b(b, out=out)
+    fname, rows, cols, _ = QUANTISERS[name]
+    x = torch.from_numpy(inputs.normal((rows, cols), 3)).to("cuda:0")
+    return lambda: getattr(dmm, fname)(x)
 
 
 def run_workload(dmm, torch, name, steps, warmup):
@@ -539,10 +561,8 @@ def run_workload(dmm, torch, name, steps, warmup):
     sees each dispatch), then a synchronisation."""
     from dense_matmul_amd import inputs
 
-    if name in QUANTISERS:
-        fname, rows, cols, _ = QUANTISERS[name]
-        x = torch.from_numpy(inputs.normal((rows, cols), 3)).to("cuda:0")
-        fn = lambda: getattr(dmm, fname)(x)
+    if name in QUANTISERS or name in PRESHUFFLES:
+        fn = prep_fn(dmm, torch, name)
         repeat(fn, warmup)
         torch.cuda.synchronize()
         ms = event_ms(lambda: repeat(fn, steps), steps)
@@ -607,14 +627,13 @@ def extra_shapes(dmm, torch, args):
 
     # the quantisers (run before the GEMM, not in its time), on the configured
     # shapes' operands
-    for name, (fname, rows, cols, _) in QUANTISERS.items():
-        fn = getattr(dmm, fname)
-        x = torch.from_numpy(inputs.normal((rows, cols), 3)).to("cuda:0")
-        t = timed_arms({"q_eager": lambda: fn(x)}, 100, 20, warm_s)
+    for name in list(QUANTISERS) + list(PRESHUFFLES):
+        fn = prep_fn(dmm, torch, name)
+        t = timed_arms({"q_eager": fn}, 100, 20, warm_s)
         ms = t["q_eager"]["median"]
         gbs = quantiser_bytes(name) / (ms * 1e-3) / 1e9
         res[name] = {"us": round(ms * 1e3, 1), "alg_GB/s": round(gbs), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
-        del x
+        del fn
         torch.cuda.empty_cache()
 
     m, k, n = 4096, 1024, 896

@@ -72,7 +72,7 @@ def parse():
                    help="rows of the headline the oracle computes (default: all of them)")
     p.add_argument("--calibrate", action="store_true",
                    help="also time every variant of the matrix-op calibration kernel (what each kind of "
-                        "instruction interleaved with the matrix ops costs)")
+                        "instruction interleaved with the matrix ops costs) and the per-CU load and store rates")
     p.add_argument("--no-ceiling", action="store_true", help="skip the calibration-kernel context")
     p.add_argument("--workload", default=None,
                    help="run only this workload (a key of dense_matmul_amd.inputs.WORKLOADS, or a quantiser of "
@@ -360,11 +360,17 @@ def calib_lib():
     if _calib is None:
         if not os.path.exists(CALIB_LIB):
             raise ImportError(f"{CALIB_LIB} is not built")
+        # torch first: the library must bind to the HIP runtime torch loads
+        # (the same soname), not bring in a second copy that finds no device
+        import torch  # noqa: F401
+
         L = ctypes.CDLL(CALIB_LIB)
         P, I64 = ctypes.c_void_p, ctypes.c_int64
         L.calib_mfma_ceiling_fp8.argtypes = [P, I64, P, I64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.POINTER(ctypes.c_int), P]
         L.calib_mfma_ceiling_fp8.restype = ctypes.c_int
+        L.calib_memory_rate.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+        L.calib_memory_rate.restype = ctypes.c_int
         L.calib_last_error.argtypes = []
         L.calib_last_error.restype = ctypes.c_char_p
         _calib = L
@@ -412,6 +418,61 @@ def mfma_ceiling(torch, frag, all_variants=False, iters=1200, launches=50):
         res["one_wave_per_simd_variants_TFLOP/s"] = {v: rate(1, v) for v in CALIB_VARIANTS}
         res["two_waves_per_simd_variants_TFLOP/s"] = {v: rate(2, v) for v in CALIB_VARIANTS if v != "scaled"}
     del out
+    return res
+
+
+MEMORY_KINDS = {"loads_vgpr": 0, "loads_lds": 1, "stores_lines": 2, "stores_epilogue": 3}
+
+
+def memory_rate(torch, buf, region, kind, nt_sc1=False, grid=None, iters=256, launches=5):
+    """Per-CU rate of one kind of 1 KiB vector-memory instruction (the
+    calibration library's memory-rate kernel): each of ``grid`` workgroups
+    (default: one per CU) streams through its own ``region`` bytes of
+    ``buf``.  Returns (bytes per shader cycle per CU from the workgroups'
+    s_memtime, aggregate TB/s from HIP events), from the last of
+    ``launches`` launches after one warm-up."""
+    L = calib_lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = cus if grid is None else grid
+    cyc = torch.zeros(2 * grid, dtype=torch.int64, device=buf.device)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        e = L.calib_memory_rate(ctypes.c_void_p(buf.data_ptr()), buf.numel(), int(region), int(iters),
+                                MEMORY_KINDS[kind], int(nt_sc1), int(grid), ctypes.c_void_p(cyc.data_ptr()),
+                                ctypes.c_void_p(st))
+        if e != 0:
+            raise (ValueError if e == 1 else RuntimeError)(L.calib_last_error().decode())
+
+    run()
+    ms = event_ms(lambda: repeat(run, launches), launches)
+    c = cyc.view(grid, 2).cpu()
+    cycles = float((c[:, 1] - c[:, 0]).double().mean())
+    per_cu = 4.0 * iters * 16 * 1024
+    return round(per_cu / cycles, 1), round(per_cu * grid / (ms * 1e-3) / 1e12, 2)
+
+
+def memory_calibration(torch):
+    """Loads and stores per CU and in aggregate (1 KiB instructions, sixteen
+    in flight per wave): loads from a region per CU that the L2 holds
+    (64 KiB), one that only the last-level cache holds (256 KiB: 8 MiB per
+    XCD), and one streamed from HBM (4 MiB); stores of whole lines and in the
+    fp8 GEMM's epilogue pattern, default and non-temporal device-scope
+    policy, on every CU and on one CU per XCD."""
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(1)
+    res = {"unit": "[bytes per shader cycle per CU, aggregate TB/s]",
+           "kind": "calibration kernel: 4 waves per CU, 1 KiB per instruction, 16 in flight per wave"}
+    for kind in ("loads_vgpr", "loads_lds"):
+        for name, region in (("L2_64KiB_per_CU", 64 << 10), ("MALL_256KiB_per_CU", 256 << 10), ("HBM_4MiB_per_CU", 4 << 20)):
+            res[f"{kind}_{name}"] = memory_rate(torch, buf, region, kind)
+    for kind in ("stores_lines", "stores_epilogue"):
+        for nt in (False, True):
+            pol = "nt_sc1" if nt else "default"
+            res[f"{kind}_{pol}_all_CUs"] = memory_rate(torch, buf, 4 << 20, kind, nt_sc1=nt)
+            res[f"{kind}_{pol}_8_CUs"] = memory_rate(torch, buf, 4 << 20, kind, nt_sc1=nt, grid=8)
+    del buf
+    torch.cuda.empty_cache()
     return res
 
 
@@ -505,6 +566,8 @@ def main():
                 tflops / ceiling["one_wave_per_simd_TFLOP/s"], 4))
         except ImportError as e:
             rec["mfma_ceiling"] = {"error": str(e)}
+    if args.calibrate:
+        rec["memory_calibration"] = memory_calibration(torch)
     if args.extra:
         rec["extra"] = extra_shapes(dmm, torch, args)
     if not args.no_cpu:

@@ -7,6 +7,9 @@
 // that the GEMM's own figure can be read against what the part reaches under
 // load (clock included).
 //
+// A second kernel measures the per-CU rates of vector-memory loads and
+// stores (calib_memory_rate).
+//
 // This is measurement tooling for the benchmark, built into its own library
 // (libdmm_calib.so) with its own C entry point; it is not part of libdmm and
 // not a step of the GEMM.
@@ -202,6 +205,83 @@ static void launch_var(int var, int grid, const v8i* f, float* out, int out_len,
     }
 }
 
+
+// ------------------------------------------------------------------ memory
+// Per-CU vector-memory rates, the other resource the GEMMs run into: one
+// workgroup of four waves per CU streams 1 KiB buffer instructions (16 bytes
+// per lane) through its own region of the caller's buffer, sixteen in flight
+// per wave.  Loads go into VGPRs or through the direct-to-LDS path; stores
+// write their region in whole 128-byte lines or in the pattern of the fp8
+// GEMM's 256-wide epilogue (each instruction 64 bytes of each of 16 rows,
+// rows 14336 bytes apart: N = 7168 bf16).  Wave 0 records s_memtime (shader
+// cycles) at its start and end.
+enum { MEM_LOAD_VGPR = 0, MEM_LOAD_LDS = 1, MEM_STORE_LINES = 2, MEM_STORE_EPILOGUE = 3, MEM_NKINDS = 4 };
+constexpr uint32_t kEpiRowBytes = 14336;
+constexpr uint32_t kEpiBlocks = 17;  // 16-row blocks the epilogue pattern cycles through (< 4 MiB)
+
+// 96 KiB: more than half the CU's LDS, so no CU holds two workgroups
+__shared__ __attribute__((aligned(1024))) v4i g_mem_lds[6 * 1024];
+
+template <int KIND, int AUX>
+__global__ void __launch_bounds__(256, 1) memory_rate_kernel(uint8_t* buf, uint32_t region, int iters, uint64_t* cyc) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(buf + (size_t)blockIdx.x * region, region);
+    lds_char* wl = (lds_char*)g_mem_lds + w * 16384;
+    const v4i val = (v4i){lane, w, (int)blockIdx.x, 7};
+    v4i r[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = (v4i){0, 0, 0, 0};
+    if (threadIdx.x == 0) g_mem_lds[0] = val;  // every kind holds the LDS block
+    __syncthreads();
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    uint32_t k = (uint32_t)w * 16u;  // instruction index: the four waves interleave in the region
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t kk = k + (uint32_t)j;
+            if constexpr (KIND == MEM_STORE_EPILOGUE) {
+                const int vo = (int)((kk % (kEpiRowBytes / 64u)) * 64u + ((kk / (kEpiRowBytes / 64u)) % kEpiBlocks) * 16u *
+                               kEpiRowBytes) + (lane >> 2) * (int)kEpiRowBytes + (lane & 3) * 16;
+                __builtin_amdgcn_raw_buffer_store_b128(val, rs, vo, 0, AUX);
+            } else {
+                const int vo = (int)((kk * 1024u) & (region - 1u)) + 16 * lane;
+                if constexpr (KIND == MEM_STORE_LINES) {
+                    __builtin_amdgcn_raw_buffer_store_b128(val, rs, vo, 0, AUX);
+                } else if constexpr (KIND == MEM_LOAD_VGPR) {
+                    asm volatile("" ::"v"(r[j]));  // the previous result is used: sixteen loads in flight
+                    r[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0);
+                } else {
+                    lds_dma16(rs, wl + 1024 * j, vo);
+                }
+            }
+        }
+        k += 64u;
+    }
+    wait_vm_lgkm0<0>();
+    __syncthreads();
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) asm volatile("" ::"v"(r[j]));
+    if (threadIdx.x == 0) {
+        cyc[2 * blockIdx.x] = t0;
+        cyc[2 * blockIdx.x + 1] = t1;
+    }
+}
+
+template <int KIND = 0>
+static void launch_mem(int kind, bool nt_sc1, int grid, uint8_t* buf, uint32_t region, int iters, uint64_t* cyc,
+                       hipStream_t st) {
+    if constexpr (KIND < MEM_NKINDS) {
+        if (kind != KIND) {
+            launch_mem<KIND + 1>(kind, nt_sc1, grid, buf, region, iters, cyc, st);
+        } else if (nt_sc1) {
+            hipLaunchKernelGGL((memory_rate_kernel<KIND, 18>), dim3(grid), dim3(256), 0, st, buf, region, iters, cyc);
+        } else {
+            hipLaunchKernelGGL((memory_rate_kernel<KIND, 0>), dim3(grid), dim3(256), 0, st, buf, region, iters, cyc);
+        }
+    }
+}
+
 }  // namespace dmm
 
 namespace {
@@ -250,6 +330,43 @@ int calib_mfma_ceiling_fp8(const uint8_t* frag, int64_t frag_bytes, float* out, 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(3, hipGetErrorString(e));
     if (workgroups) *workgroups = cus;
+    g_calib_err[0] = 0;
+    return 0;
+}
+
+// One launch of the memory-rate kernel: `grid` workgroups (1 .. the CU
+// count), workgroup g on bytes [g region, (g+1) region) of buf, each of its
+// four waves issuing 16 iters 1 KiB instructions of `kind` (0 loads into
+// VGPRs, 1 loads into LDS, 2 stores of whole lines, 3 stores in the GEMM
+// epilogue's half-line pattern) with the default cache policy, or for
+// stores with nt_sc1 the non-temporal device-scope one the GEMM uses at
+// K < 4096.  cycles (device, 2 grid uint64) receives each workgroup's
+// s_memtime at start and end.  region: a power of two, at least 64 KiB (4 MiB
+// for kind 3) and at most 1 GiB; buf (device, 16-byte aligned) must hold
+// grid * region bytes.  Returns 0, 1 for a rule broken (before any HIP
+// call), 3 when the HIP runtime reports an error.
+int calib_memory_rate(uint8_t* buf, int64_t buf_bytes, int64_t region, int iters, int kind, int nt_sc1, int grid,
+                      uint64_t* cycles, void* stream) {
+    auto fail = [](int code, const char* msg) {
+        snprintf(g_calib_err, sizeof g_calib_err, "%s", msg);
+        return code;
+    };
+    if (buf == nullptr || ((uintptr_t)buf & 15u)) return fail(1, "buf: pointer is null or not 16-byte aligned");
+    if (cycles == nullptr || ((uintptr_t)cycles & 7u)) return fail(1, "cycles: pointer is null or not 8-byte aligned");
+    if (kind < 0 || kind >= dmm::MEM_NKINDS) return fail(1, "kind must be in [0, 3]");
+    const int64_t min_region = kind == dmm::MEM_STORE_EPILOGUE ? (int64_t)4 << 20 : (int64_t)64 << 10;
+    if (region < min_region || region > ((int64_t)1 << 30) || (region & (region - 1)))
+        return fail(1, "region must be a power of two in [64 KiB (4 MiB for kind 3), 1 GiB]");
+    if (iters < 1 || iters > (1 << 16)) return fail(1, "iters must be in [1, 2^16]");
+    int dev = 0, cus = 0;
+    const hipError_t ed = hipGetDevice(&dev);
+    const hipError_t ea = ed == hipSuccess ? hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) : ed;
+    if (ea != hipSuccess) return fail(3, hipGetErrorString(ea));
+    if (grid < 1 || grid > cus) return fail(1, "grid must be in [1, the CU count]");
+    if (buf_bytes < (int64_t)grid * region) return fail(1, "buf must hold grid * region bytes");
+    dmm::launch_mem(kind, nt_sc1 != 0, grid, buf, (uint32_t)region, iters, cycles, (hipStream_t)stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(3, hipGetErrorString(e));
     g_calib_err[0] = 0;
     return 0;
 }

@@ -1,7 +1,8 @@
-"""The benchmark's matrix-op calibration kernel (libdmm_calib.so, built beside
-libdmm but not part of its C ABI): argument rules on the CPU, and on the GPU
-that every variant runs on every compute unit, reports its FLOPs and is
-deterministic."""
+"""The benchmark's calibration kernels (libdmm_calib.so, built beside libdmm
+but not part of its C ABI): argument rules on the CPU, and on the GPU that
+every matrix-op variant runs on every compute unit, reports its FLOPs and is
+deterministic, and that the memory-rate kernel writes what it is asked to and
+reports plausible rates."""
 import ctypes
 import os
 import sys
@@ -32,7 +33,7 @@ def test_calibration_is_not_in_the_product_library():
     if not os.path.exists(dmm.LIB_PATH):
         pytest.skip("libdmm.so not built")
     lib = ctypes.CDLL(dmm.LIB_PATH)
-    for name in ("calib_mfma_ceiling_fp8", "dmm_mfma_ceiling_fp8"):
+    for name in ("calib_mfma_ceiling_fp8", "dmm_mfma_ceiling_fp8", "calib_memory_rate"):
         assert not hasattr(lib, name), name
 
 
@@ -75,3 +76,42 @@ def test_calibration_kernel_runs_and_is_deterministic(L, wps, variant):
     assert torch.equal(out1[:used], out2[:used])
     assert torch.equal(out1[:used], ref[:used])
     assert (out1[:used] != 0).any()
+
+
+@pytest.mark.parametrize("buf,buf_bytes,region,iters,kind,grid,why", [
+    (None, 1 << 30, 1 << 16, 1, 0, 1, "buf: pointer"), (ctypes.c_void_p((1 << 20) + 8), 1 << 30, 1 << 16, 1, 0, 1, "buf: pointer"),
+    (ALIGNED, 1 << 30, 1 << 16, 1, 4, 1, "kind"), (ALIGNED, 1 << 30, 1 << 16, 1, -1, 1, "kind"),
+    (ALIGNED, 1 << 30, 1 << 15, 1, 0, 1, "region"), (ALIGNED, 1 << 30, 3 << 16, 1, 0, 1, "region"),
+    (ALIGNED, 1 << 30, 1 << 20, 1, 3, 1, "region"), (ALIGNED, 1 << 30, (1 << 30) * 2, 1, 0, 1, "region"),
+    (ALIGNED, 1 << 30, 1 << 16, 0, 0, 1, "iters"), (ALIGNED, 1 << 30, 1 << 16, (1 << 16) + 1, 0, 1, "iters"),
+])
+def test_memory_rate_rules(L, buf, buf_bytes, region, iters, kind, grid, why):
+    """The memory-rate entry point checks its arguments before any HIP call."""
+    st = L.calib_memory_rate(buf, buf_bytes, region, iters, kind, 0, grid, ALIGNED, None)
+    assert st == 1, st
+    assert why in L.calib_last_error().decode()
+
+
+@pytest.mark.gpu
+def test_memory_rate_kernel_writes_its_region_and_reports_rates(L):
+    """The store kinds write exactly their workgroups' regions (a poisoned
+    buffer keeps its poison past grid * region), the epilogue pattern covers
+    the rows it claims, and every kind reports a positive, finite rate below
+    the L1's 64 bytes per cycle per CU for HBM-bound regions."""
+    import torch
+
+    print("[case] memory-rate kernel", flush=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    region = 4 << 20
+    buf = torch.full((cus * region + (1 << 20),), 0xEE, dtype=torch.uint8, device="cuda:0")
+    bench.memory_rate(torch, buf, region, "stores_lines", grid=8, iters=4, launches=1)
+    torch.cuda.synchronize()
+    b = buf.view(torch.int32)
+    lines = b[: 8 * region // 4].view(8, region // 4)
+    # kind 2 writes {lane, wave, workgroup, 7} per 16 bytes over the region's first 4 waves x 16 x 4 KiB
+    assert (lines[:, 3::4][:, : 4 * 4 * 16 * 1024 // 16] == 7).all()
+    assert (buf[8 * region:] == 0xEE).all()
+    for kind in bench.MEMORY_KINDS:
+        per_cu, tbs = bench.memory_rate(torch, buf[: cus * region], region, kind, iters=16, launches=2)
+        print("[stats]", kind, per_cu, tbs, flush=True)
+        assert 0.5 < per_cu < 64.0 and 0.05 < tbs < 40.0, (kind, per_cu, tbs)

@@ -101,10 +101,9 @@ __device__ __forceinline__ v4f load4(const uint16_t* xr, int c) {
                  __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xFFFF0000u)};
 }
 
-// Rows of up to 256 NC columns stay in registers (NC 16-byte chunks per
-// lane), so each value is read from HBM once and every load of the row is
-// in flight before the first wait; longer rows take the two-pass kernel
-// below, whose second pass re-reads the row from L2.
+// One wave per row: rows of up to 256 NC columns stay in registers (NC
+// 16-byte chunks per lane), so each value is read from HBM once and every
+// load of the row is in flight before the first wait.
 template <typename In, int NC>
 __global__ void __launch_bounds__(256) quantize_rows_reg_kernel(const In* __restrict__ x, uint8_t* __restrict__ q,
                                                                 float* __restrict__ scale, int rows, int cols) {
@@ -132,7 +131,7 @@ __global__ void __launch_bounds__(256) quantize_rows_reg_kernel(const In* __rest
     if (lane == 0) scale[row] = s;
 }
 
-// Rows of 2049 .. 7168 columns: W (2 or 4) waves per row, wave h holding
+// Rows of 513 .. 7168 columns: W (2 or 4) waves per row, wave h holding
 // the 64-chunk slices h, h + W, h + 2W, ... of it (NC chunks per lane), their
 // maxima combined through LDS; 1/W of the registers of one wave per row, so
 // W times the rows in flight.
@@ -173,6 +172,8 @@ __global__ void __launch_bounds__(256) quantize_rows_split_kernel(const In* __re
     if (lane == 0 && h == 0) scale[row] = s;
 }
 
+// Rows beyond 7168 columns: one wave per row in two passes, the second
+// re-reading the row (from L2) to quantise it.
 template <typename In>
 __global__ void __launch_bounds__(256) quantize_rows_kernel(const In* __restrict__ x, uint8_t* __restrict__ q,
                                                             float* __restrict__ scale, int rows, int cols) {
@@ -333,13 +334,17 @@ __global__ void __launch_bounds__(256) preshuffle_b_kernel(const uint8_t* __rest
 
 // -------------------------------------------------------------- launch
 // Per-token quantisation, rows held in registers up to 7168 columns: one
-// wave per row up to 2048 columns, two up to 4096 (8 chunks per lane each),
-// four up to 7168 (7 each); the two-pass kernel beyond.
+// wave per row up to 512 columns, two up to 2048 (4 chunks per lane each)
+// and up to 4096 (8 each), four up to 7168 (7 each); the two-pass kernel
+// beyond.  (Two waves per row against one, same-box A/B: 32768 x 1792
+// 44.2 -> 43.2 us, 65536 x 1024 59.2 -> 56.5 us, but 16384 x 512 9.7 ->
+// 11.6 us.)
 template <typename In>
 static hipError_t launch_rows(const In* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st) {
     const dim3 g4((rows + 3) / 4), g2((rows + 1) / 2), g1(rows), b(256);
     const int chunks = (cols / 4 + 63) / 64;  // 64-lane slices of 16-byte chunks in a row
-    if (chunks <= 8) hipLaunchKernelGGL((quantize_rows_reg_kernel<In, 8>), g4, b, 0, st, x, q, s, rows, cols);
+    if (chunks <= 2) hipLaunchKernelGGL((quantize_rows_reg_kernel<In, 2>), g4, b, 0, st, x, q, s, rows, cols);
+    else if (chunks <= 8) hipLaunchKernelGGL((quantize_rows_split_kernel<In, 4, 2>), g2, b, 0, st, x, q, s, rows, cols);
     else if (chunks <= 16) hipLaunchKernelGGL((quantize_rows_split_kernel<In, 8, 2>), g2, b, 0, st, x, q, s, rows, cols);
     else if (chunks <= 28) hipLaunchKernelGGL((quantize_rows_split_kernel<In, 7, 4>), g1, b, 0, st, x, q, s, rows, cols);
     else hipLaunchKernelGGL(quantize_rows_kernel<In>, g4, b, 0, st, x, q, s, rows, cols);

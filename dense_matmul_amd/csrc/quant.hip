@@ -90,7 +90,7 @@ struct DivQuant {
 };
 
 // ------------------------------------------------------------- per token
-// One wave per row; 4 rows per workgroup.  cols % 16 == 0.
+// One, two or four waves per row (launch_rows below); cols % 16 == 0.
 // Four consecutive values of a row as fp32: fp32 rows load 16 bytes, bf16
 // rows 8 bytes, widened exactly (a bf16 value is the high half of an fp32).
 __device__ __forceinline__ v4f load4(const float* xr, int c) { return ((const v4f*)xr)[c]; }

@@ -70,7 +70,7 @@ def device_asm(src="gemm_a8w8.hip", out=None):
 
 
 def disassemble(src="gemm_a8w8.hip"):
-    """gfx950 disassembly of the kernels this build compiled from one source
+    """gfx950 disassembly of the kernels build() compiled from one source
     file (the device code object inside _build/<src>.o, which build() leaves
     there), for audits of the emitted waits, barriers and loads."""
     obj = os.path.join(ROOT, "_build", src + ".o")

@@ -62,8 +62,13 @@ def to_dev(a):
 
 
 # ------------------------------------------------------------ quantisers
+# row lengths on both sides of each kernel boundary (one wave per row up to
+# 512 columns, two up to 2048 and 4096, four up to 7168, two passes beyond),
+# with ragged last 64-chunk slices
 @pytest.mark.parametrize("rows,cols,seed", [(512, 256, 1), (300, 1792, 2), (7, 7168, 3), (64, 16, 4),
-                                           (33, 4096, 14), (3, 2064, 16), (5, 9216, 15)])
+                                           (33, 4096, 14), (3, 2064, 16), (5, 9216, 15), (9, 512, 17),
+                                           (9, 528, 18), (11, 1040, 19), (6, 2048, 20), (6, 4112, 26),
+                                           (5, 6160, 27), (4, 7184, 28)])
 def test_quantize_per_token_bitexact(dmm, rows, cols, seed):
     announce("quantize_per_token", rows, cols, seed)
     x = inputs.normal((rows, cols), seed)
@@ -79,7 +84,7 @@ def test_quantize_per_token_bitexact(dmm, rows, cols, seed):
 
 
 @pytest.mark.parametrize("rows,cols,seed", [(512, 256, 21), (300, 1792, 22), (5, 7168, 23), (33, 4096, 24),
-                                           (5, 9216, 25)])
+                                           (5, 9216, 25), (7, 528, 29), (6, 4112, 30)])
 def test_quantize_per_token_bf16_input_bitexact(dmm, rows, cols, seed):
     """bf16 activations: the oracle quantises the same values widened to fp32
     (bf16 -> fp32 is exact), so codes and scales must match bitwise."""

@@ -197,12 +197,12 @@ def _gemm_args(a, b_shuf, out):
     return _codes(a, "a"), _codes(b_shuf, "b_shuf"), out, m, n, k
 
 
-PTPC_TILES = {"256x256": 1, "128x256": 2}
+PTPC_TILES = {"256x256": 1, "128x256": 2, "128x128": 3}
 
 
 def gemm_a8w8_ptpc(a, b_shuf, a_scale, b_scale, out=None, tile="auto"):
     """C = bf16(a_scale[m] * b_scale[n] * sum_k A[m,k] B[n,k]).  tile: "auto"
-    (the library's choice), "256x256" or "128x256" (same result)."""
+    (the library's choice), "256x256", "128x256" or "128x128" (same result)."""
     au, bu, out, m, n, k = _gemm_args(a, b_shuf, out)
     _require(a_scale, "a_scale", torch.float32, 1)
     _require(b_scale, "b_scale", torch.float32, 1)

@@ -193,7 +193,7 @@ dmm_status gemm_a8w8_ptpc(const uint8_t* a, const uint8_t* b_shuf, const float* 
 
 dmm_status gemm_a8w8_ptpc_tile(const uint8_t* a, const uint8_t* b_shuf, const float* a_scale, const float* b_scale,
                                uint16_t* c, int64_t m, int64_t n, int64_t k, int tile, void* stream) {
-    REQUIRE(tile >= 0 && tile <= 2, "tile must be 0 (auto), 1 (256x256) or 2 (128x256) (got %d)", tile);
+    REQUIRE(tile >= 0 && tile <= 3, "tile must be 0 (auto), 1 (256x256), 2 (128x256) or 3 (128x128) (got %d)", tile);
     return gemm_common(0, tile, a, b_shuf, a_scale, b_scale, c, m, n, k, stream);
 }
 

@@ -55,7 +55,8 @@ namespace dmm {
 // MODE_PTPC_N: ptpc on the 128 x 256 tile of eight waves (see Cfg);
 // MODE_PTPC_G: ptpc over a gathered A (Gather), 256 x 256 tiles;
 // MODE_MXFP8_N: mxfp8 on the 256 x 128 tile of four waves;
-// MODE_BLOCKSCALE_N: blockscale on a 128 x 128 tile of four waves.
+// MODE_BLOCKSCALE_N: blockscale on a 128 x 128 tile of four waves;
+// MODE_PTPC_Q: ptpc on a 128 x 128 tile of four waves.
 enum {
     MODE_PTPC = 0,
     MODE_BLOCKSCALE = 1,
@@ -63,13 +64,17 @@ enum {
     MODE_PTPC_N = 3,
     MODE_PTPC_G = 4,
     MODE_MXFP8_N = 5,
-    MODE_BLOCKSCALE_N = 6
+    MODE_BLOCKSCALE_N = 6,
+    MODE_PTPC_Q = 7
 };
 
 template <int MODE>
 constexpr bool kWidePtpc = MODE == MODE_PTPC || MODE == MODE_PTPC_G;
+// ptpc on 32-column waves with VGPR accumulators (128 x 256 and 128 x 128)
 template <int MODE>
-constexpr bool kPtpc = kWidePtpc<MODE> || MODE == MODE_PTPC_N;
+constexpr bool kNarrowPtpc = MODE == MODE_PTPC_N || MODE == MODE_PTPC_Q;
+template <int MODE>
+constexpr bool kPtpc = kWidePtpc<MODE> || kNarrowPtpc<MODE>;
 template <int MODE>
 constexpr bool kMx = MODE == MODE_MXFP8 || MODE == MODE_MXFP8_N;
 template <int MODE>
@@ -156,7 +161,7 @@ constexpr bool store_nt_only(int k) { return k >= kLongK; }
 // twice the size of B in each K tile.
 // MODE_BLOCKSCALE_N runs the blockscale waves four to a 128 x 128 tile (one
 // per SIMD), which doubles the tile count of grids that would leave CUs
-// idle.
+// idle; MODE_PTPC_Q does the same for the narrow ptpc waves.
 template <int MODE>
 struct Cfg {
     static constexpr sched::Shape S = sched::shape_of(MODE);  // kpipe.h
@@ -438,7 +443,7 @@ __device__ __forceinline__ void mfma_acc(v4f& acc, const v8i& b, const v8i& a) {
     else asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
 }
 
-// The same with the accumulator in VGPRs (MODE_PTPC_N).
+// The same with the accumulator in VGPRs (MODE_PTPC_N, MODE_PTPC_Q).
 template <bool ZERO>
 __device__ __forceinline__ void mfma_vacc(v4f& acc, const v8i& b, const v8i& a) {
     if constexpr (ZERO) asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(b), "v"(a));
@@ -507,7 +512,7 @@ template <int MODE, int T, int mb, bool FIRST>
 __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
     if constexpr (kWidePtpc<MODE> || kMx<MODE>) {
         static_for<0, Cfg<MODE>::NBW>([&](auto NBc) { mfma_block<MODE, T, mb, decltype(NBc)::value, FIRST>(x, a); });
-    } else if constexpr (MODE == MODE_PTPC_N) {
+    } else if constexpr (kNarrowPtpc<MODE>) {
         // each accumulator is rewritten once per K tile, 2 MB - 1 matrix ops
         // after its last write: far past the result latency
         mfma_vacc<FIRST>(x.acc[mb][0], x.bq[T][0], a);
@@ -649,7 +654,7 @@ __device__ __forceinline__ Epi epi_begin(Ctx<MODE>& x, int m0, int n0) {
         e.lone = first + 1 == p;
         e.o8 = base + 8 * x.g + (first + 1 == p ? 0u : kDrop);
     }
-    if constexpr (MODE == MODE_PTPC_N) {
+    if constexpr (kNarrowPtpc<MODE>) {
         // rows MB i .. MB i + 7; columns 8g + 4j + v of the wave's 32 (a lone
         // block: 4g + v)
         static_assert(C::MB == 8 && C::NBW == 2, "two A- and two B-scale vectors");
@@ -774,7 +779,7 @@ __device__ __forceinline__ void epi_row(Ctx<MODE>& x, const Epi& e) {
         static_assert(C::NBW == 2, "one block pair per wave");
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(x.c, (uint32_t)x.M * (uint32_t)x.N * 2u);
         v4f u = x.acc[mb][0], v = x.acc[mb][1];
-        if constexpr (MODE == MODE_PTPC_N) {
+        if constexpr (kNarrowPtpc<MODE>) {
             const float sa = e.eas[mb / 4][mb % 4];
             u = u * sa * e.ebs[0];
             v = v * sa * e.ebs[1];
@@ -1011,7 +1016,7 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRe
     if constexpr (EPM == 1) x.ep = epi_begin<MODE>(x, prev.m0, prev.n0);
     // the tile's scales leave LDS before this step's wait lets the next
     // tile's scale DMAs in (the narrow tile stores at the end of the step)
-    if constexpr (EPM == 3 || (MODE == MODE_PTPC_N && LAST && !FIRST)) x.ep = epi_begin<MODE>(x, g.t0.m0, g.t0.n0);
+    if constexpr (EPM == 3 || (kNarrowPtpc<MODE> && LAST && !FIRST)) x.ep = epi_begin<MODE>(x, g.t0.m0, g.t0.n0);
     realign_mx<MODE, T>(x);
     v8i f0 = x.pre[0], f1 = x.pre[1], f2;
     EpiRow q;
@@ -1047,7 +1052,7 @@ __device__ __forceinline__ void tile_body(Ctx<MODE>& x, int s0, Ring g, TileRef 
     }
     if constexpr (!kDeferEpilogue<MODE>) {
         mfma_drain<MODE>(x);
-        if constexpr (MODE == MODE_PTPC_N && CASE != 4) epi_rows<MODE>(x, x.ep);
+        if constexpr (kNarrowPtpc<MODE> && CASE != 4) epi_rows<MODE>(x, x.ep);
         else store_tile<MODE>(x, g.t0.m0, g.t0.n0);
     }
 }
@@ -1205,7 +1210,8 @@ static hipError_t launch_gemm(const GemmArgs& base, hipStream_t stream) {
 // most, so a launch takes about ceil(T / CUs) tile times.  The 256 x 256 tile
 // moves the fewest bytes per matrix op; a half-size tile (128 x 256 for
 // ptpc, 256 x 128 for mxfp8) takes `half_cost` of a wide tile's time (more
-// than one half: it reads the same LDS fragments for half the matrix ops).
+// than one half: it reads the same LDS fragments for half the matrix ops;
+// ptpc also has a quarter-size tile, below).
 // The half tile is chosen when its waves cost less, which happens where the
 // wide grid leaves many CUs idle in its last wave (at most half the CUs
 // busy, or a last wave well short of full).
@@ -1215,12 +1221,21 @@ static bool half_tile_wins(long wide_tiles, long half_tiles, double half_cost) {
     return (double)half_waves * half_cost < (double)wide_waves;
 }
 
-// ptpc: the 128 x 256 tile of eight waves runs at about 0.8 of the wide
-// tile's rate per matrix op (measured), so it costs 0.625 of a wide tile.
+// ptpc, three tiles: 256 x 256 (1), 128 x 256 of eight waves (2) and
+// 128 x 128 of four waves (3), each costing a measured fraction of a wide
+// tile's time (the 128 x 128 tile: 28 waves 206 us against 7 waves of wide
+// tiles 162 us at 16384 x 7168 x 1792, 56 against 14 waves 434 against
+// 319 us at 32768 x 7168 x 1792).  The launch takes the tile whose waves
+// over the CUs cost least; the smaller tiles pay off only where the wide
+// grid leaves CUs idle.
+constexpr double kPtpcHalfCost = 0.625, kPtpcQuarterCost = 0.34;
 int ptpc_tile_for(int m, int n) {
-    const long wide = (long)((m + 255) / 256) * ((n + 255) / 256);
-    const long half = (long)((m + 127) / 128) * ((n + 255) / 256);
-    return half_tile_wins(wide, half, 0.625) ? 2 : 1;
+    const long cus = device_cus();
+    auto waves = [cus](long tiles) { return (double)((tiles + cus - 1) / cus); };
+    const double wide = waves((long)((m + 255) / 256) * ((n + 255) / 256));
+    const double half = kPtpcHalfCost * waves((long)((m + 127) / 128) * ((n + 255) / 256));
+    const double quarter = kPtpcQuarterCost * waves((long)((m + 127) / 128) * ((n + 127) / 128));
+    return quarter < half && quarter < wide ? 3 : half < wide ? 2 : 1;
 }
 
 // mxfp8: the 256 x 128 tile of four waves.
@@ -1245,9 +1260,12 @@ int blockscale_tile_for(int m, int n) {
 hipError_t launch_gemm_a8w8(int mode, int tile, const uint8_t* a, const uint8_t* b, const void* sa, const void* sb,
                             uint16_t* c, int m, int n, int k, hipStream_t stream) {
     GemmArgs p{a, b, sa, sb, c, m, n, k, 0, 0};
-    if (mode == MODE_PTPC && (tile == 0 ? ptpc_tile_for(m, n) : tile) == 2) mode = MODE_PTPC_N;
-    if (mode == MODE_PTPC) return launch_gemm<MODE_PTPC>(p, stream);
-    if (mode == MODE_PTPC_N) return launch_gemm<MODE_PTPC_N>(p, stream);
+    if (mode == MODE_PTPC) {
+        const int t = tile == 0 ? ptpc_tile_for(m, n) : tile;
+        if (t == 2) return launch_gemm<MODE_PTPC_N>(p, stream);
+        if (t == 3) return launch_gemm<MODE_PTPC_Q>(p, stream);
+        return launch_gemm<MODE_PTPC>(p, stream);
+    }
     if (mode == MODE_MXFP8 && (tile == 0 ? mxfp8_tile_for(m, n) : tile) == 2) mode = MODE_MXFP8_N;
     if (mode == MODE_MXFP8) return launch_gemm<MODE_MXFP8>(p, stream);
     if (mode == MODE_MXFP8_N) return launch_gemm<MODE_MXFP8_N>(p, stream);

@@ -54,7 +54,7 @@ constexpr int kStages = 4;  // LDS stages of the A tile
 //   0 ptpc, 256 x 256, 4 waves         3 ptpc, 128 x 256, 8 waves
 //   1 blockscale, 128 x 256, 8 waves   4 ptpc over a gathered A, 256 x 256
 //   2 mxfp8, 256 x 256, 4 waves        5 mxfp8, 256 x 128, 4 waves
-//   6 blockscale, 128 x 128, 4 waves
+//   6 blockscale, 128 x 128, 4 waves   7 ptpc, 128 x 128, 4 waves
 // Each wave owns MB 16-row blocks (all rows of the tile) and NBW 16-column
 // blocks.  Per K tile a wave issues NA A-tile DMAs (1 KiB each: the 16 MB x
 // 128-byte tile split over the waves) and NB vector loads of its B event
@@ -66,8 +66,8 @@ struct Shape {
     int MB, NBW, WAVES, NA, NB, NSC;
 };
 constexpr Shape shape_of(int mode) {
-    const bool narrow = mode == 1 || mode == 3, slim = mode == 5, square = mode == 6;
-    const bool ptpc = mode == 0 || mode == 3 || mode == 4;
+    const bool narrow = mode == 1 || mode == 3, slim = mode == 5, square = mode == 6 || mode == 7;
+    const bool ptpc = mode == 0 || mode == 3 || mode == 4 || mode == 7;
     const int MB = narrow || square ? 8 : 16, NBW = narrow || slim || square ? 2 : 4, WAVES = narrow ? 8 : 4;
     return Shape{MB, NBW, WAVES, 2 * MB / WAVES, ptpc ? 2 * NBW : 2 * NBW + 3, ptpc ? 2 : 0};
 }

@@ -125,10 +125,11 @@ dmm_status gemm_a8w8_ptpc(const uint8_t* a, const uint8_t* b_shuf, const float* 
 
 /* ptpc with an explicit output-tile shape, the same result as
  * gemm_a8w8_ptpc: tile 1 = 256 x 256 (four waves), 2 = 128 x 256 (eight
- * waves), 0 = the choice gemm_a8w8_ptpc makes (128 x 256 when its waves
- * over the compute units cost less than the 256 x 256 tile's: each costs
- * 0.625 of a wide tile, so e.g. when the wide grid would leave at least
- * half the compute units idle).  The pages size the
+ * waves), 3 = 128 x 128 (four waves), 0 = the choice gemm_a8w8_ptpc makes:
+ * the tile whose waves over the compute units cost least, a 128 x 256 tile
+ * costing 0.625 and a 128 x 128 tile 0.34 of a wide tile's time (so the
+ * smaller tiles win only where the wide grid would leave many compute units
+ * idle).  The pages size the
  * tile to the problem in the same spirit (mori PR 785, Cost: the table's
  * shapes; aiter PR 6539, Motivation and its review thread: the tuned rows,
  * one kernel configuration per shape).  Other values of tile return

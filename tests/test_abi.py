@@ -77,11 +77,12 @@ def test_gemm_shape_rules(L, m, n, k, why):
 
 @pytest.mark.parametrize("name", ["gemm_a8w8_ptpc_tile", "gemm_a8w8_blockscale_tile", "gemm_a8w8_mxfp8_tile"])
 def test_tile_rule(L, name):
-    """tile is 0 (auto), 1 (the wide tile) or 2 (the half-size one);
-    anything else is an argument error, reported before any HIP call."""
+    """tile is 0 (auto), 1 (the wide tile) or 2 (the half-size one), and 3
+    (128 x 128) for ptpc; anything else is an argument error, reported
+    before any HIP call."""
     f = getattr(L, name)
     f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_void_p]
-    for tile in (-1, 3, 256):
+    for tile in (-1, 4 if name == "gemm_a8w8_ptpc_tile" else 3, 256):
         assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 64, 256, 256, tile, None) == 1
         assert b"tile must be" in L.dmm_last_error()
     # shape rules apply as for the call without a tile

@@ -40,7 +40,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 ONE = 0x38  # E4M3 code of 1.0
-MODES = ["ptpc_w", "ptpc_n", "blockscale", "blockscale_n", "mxfp8", "mxfp8_n"]
+MODES = ["ptpc_w", "ptpc_n", "ptpc_q", "blockscale", "blockscale_n", "mxfp8", "mxfp8_n"]
 
 
 @pytest.fixture(scope="module")
@@ -75,8 +75,8 @@ def run(dmm, mode, qa, qb, sa, sb):
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     b_shuf = dmm.preshuffle_b(dev(qb))
     a, s_a, s_b = dev(qa), dev(sa), dev(sb)
-    if mode in ("ptpc_w", "ptpc_n"):
-        c = dmm.gemm_a8w8_ptpc(a, b_shuf, s_a, s_b, tile={"ptpc_w": "256x256", "ptpc_n": "128x256"}[mode])
+    if mode in ("ptpc_w", "ptpc_n", "ptpc_q"):
+        c = dmm.gemm_a8w8_ptpc(a, b_shuf, s_a, s_b, tile={"ptpc_w": "256x256", "ptpc_n": "128x256", "ptpc_q": "128x128"}[mode])
     elif mode.startswith("blockscale"):
         c = dmm.gemm_a8w8_blockscale(a, b_shuf, s_a, s_b, tile={"blockscale": "128x256", "blockscale_n": "128x128"}[mode])
     else:
@@ -205,8 +205,10 @@ def test_modes_agree_under_unit_scales(dmm):
     qb = a_codes(n, k, 941)
     ptpc_w = run(dmm, "ptpc_w", qa, qb, np.ones(m, np.float32), np.ones(n, np.float32))
     ptpc_n = run(dmm, "ptpc_n", qa, qb, np.ones(m, np.float32), np.ones(n, np.float32))
+    ptpc_q = run(dmm, "ptpc_q", qa, qb, np.ones(m, np.float32), np.ones(n, np.float32))
     mx = run(dmm, "mxfp8", qa, qb, np.full((k // 32, m), 127, np.uint8), np.full((k // 32, n), 127, np.uint8))
     assert np.array_equal(ptpc_w, ptpc_n), f"ptpc tiles differ at {np.argwhere(ptpc_w != ptpc_n)[:4].tolist()}"
+    assert np.array_equal(ptpc_w, ptpc_q), f"ptpc tiles differ at {np.argwhere(ptpc_w != ptpc_q)[:4].tolist()}"
     assert np.array_equal(ptpc_w, mx), f"ptpc and mxfp8 differ at {np.argwhere(ptpc_w != mx)[:4].tolist()}"
 
 

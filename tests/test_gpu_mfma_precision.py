@@ -33,7 +33,7 @@ from oracle import tolerance
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 LAUNCHES = 64
-MODES = ["ptpc", "ptpc_w", "blockscale", "blockscale_n", "mxfp8", "mxfp8_n"]
+MODES = ["ptpc", "ptpc_w", "ptpc_q", "blockscale", "blockscale_n", "mxfp8", "mxfp8_n"]
 
 
 @pytest.fixture(scope="module")
@@ -69,7 +69,7 @@ def cancelling_operands(seed):
 
 
 def base(mode):
-    return {"ptpc_w": "ptpc", "mxfp8_n": "mxfp8", "blockscale_n": "blockscale"}.get(mode, mode)
+    return {"ptpc_w": "ptpc", "ptpc_q": "ptpc", "mxfp8_n": "mxfp8", "blockscale_n": "blockscale"}.get(mode, mode)
 
 
 def unit_scales(mode, m, n):
@@ -88,6 +88,8 @@ def run(dmm, mode, qa, qb, sa, sb):
         c = dmm.gemm_a8w8_ptpc(t(qa), bs, t(sa), t(sb))
     elif mode == "ptpc_w":
         c = dmm.gemm_a8w8_ptpc(t(qa), bs, t(sa), t(sb), tile="256x256")
+    elif mode == "ptpc_q":
+        c = dmm.gemm_a8w8_ptpc(t(qa), bs, t(sa), t(sb), tile="128x128")
     elif mode == "blockscale":
         c = dmm.gemm_a8w8_blockscale(t(qa), bs, t(sa), t(sb), tile="128x256")
     elif mode == "blockscale_n":

@@ -251,13 +251,13 @@ def test_preshuffle_is_the_documented_permutation(dmm, n, k):
 # ------------------------------------------------------------------ GEMM
 # ptpc runs on two tile shapes; "ptpc" is the library's own choice, the
 # other two force one shape (same data, same oracle).
-PTPC_TILE = {"ptpc": "auto", "ptpc_w": "256x256", "ptpc_n": "128x256"}
+PTPC_TILE = {"ptpc": "auto", "ptpc_w": "256x256", "ptpc_n": "128x256", "ptpc_q": "128x128"}
 # mxfp8 likewise: "mxfp8" forces the 256x256 tile, "mxfp8_n" the 256x128 one
 MXFP8_TILE = {"mxfp8": "256x256", "mxfp8_n": "256x128", "mxfp8_auto": "auto"}
 # blockscale: "blockscale" forces the 128x256 tile, "blockscale_n" the 128x128 one
 BLOCKSCALE_TILE = {"blockscale": "128x256", "blockscale_n": "128x128", "blockscale_auto": "auto"}
 MODE_ID = {"ptpc": 0, "blockscale": 1, "mxfp8": 2}
-GEMM_MODES = ["ptpc_w", "ptpc_n", "blockscale", "blockscale_n", "mxfp8", "mxfp8_n"]
+GEMM_MODES = ["ptpc_w", "ptpc_n", "ptpc_q", "blockscale", "blockscale_n", "mxfp8", "mxfp8_n"]
 
 
 def base_mode(mode):
@@ -273,7 +273,7 @@ def gemm_fn(dmm, mode):
 
 
 def tile_rows(mode):
-    return 128 if mode in ("blockscale", "blockscale_n", "ptpc_n") else 256
+    return 128 if mode in ("blockscale", "blockscale_n", "ptpc_n", "ptpc_q") else 256
 
 
 def quantised_operands(mode, m, n, k, seed_a, seed_b):
@@ -376,7 +376,7 @@ def run_poisoned(dmm, mode, qa, qb, sa, sb, launches, hog=False):
     return outs
 
 
-@pytest.mark.parametrize("mode", ["ptpc", "ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale", "blockscale_n"])
+@pytest.mark.parametrize("mode", ["ptpc", "ptpc_w", "ptpc_n", "ptpc_q", "mxfp8", "mxfp8_n", "blockscale", "blockscale_n"])
 @pytest.mark.parametrize("m,n,k,seed_a,seed_b", [(4096, 7168, 256, 11, 12), (16384, 7168, 512, 21, 22)])
 def test_race_shapes_bit_stable_and_correct(dmm, mode, m, n, k, seed_a, seed_b):
     """The pages' race shapes (mori PR 785, Test table), in every mode and
@@ -395,7 +395,7 @@ def test_race_shapes_bit_stable_and_correct(dmm, mode, m, n, k, seed_a, seed_b):
     check_close(outs[0][rows], ref, f"{mode} {m}x{n}x{k} sampled rows", base_mode(mode), (qa, qb, sa, sb), rows)
 
 
-@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale", "blockscale_n"])
+@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "ptpc_q", "mxfp8", "mxfp8_n", "blockscale", "blockscale_n"])
 def test_bit_stable_under_concurrent_copy(dmm, mode):
     """Same 20-launch identity with an HBM copy loop on a second stream."""
     m, n, k = 4096, 7168, 256
@@ -462,7 +462,7 @@ def test_invalid_arguments_raise_value_error(dmm):
                            torch.ones(16, dtype=torch.float32, device=DEV))
 
 
-@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "mxfp8", "mxfp8_n", "blockscale", "blockscale_n"])
+@pytest.mark.parametrize("mode", ["ptpc_w", "ptpc_n", "ptpc_q", "mxfp8", "mxfp8_n", "blockscale", "blockscale_n"])
 @pytest.mark.parametrize("k", [128, 256, 384, 512, 640])
 def test_many_tiles_per_workgroup_every_k_phase(dmm, mode, k):
     """More tiles than CUs, so every workgroup runs 2-3 tiles back to back,

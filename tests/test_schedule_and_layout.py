@@ -87,7 +87,7 @@ def shim(tmp_path_factory):
 # ---------------------------------------------------------------- schedule
 # the kernel's modes (kpipe.h, shape_of): name -> mode id
 MODE_IDS = {"ptpc": 0, "blockscale": 1, "mxfp8": 2, "ptpc_128x256": 3, "ptpc_gathered": 4, "mxfp8_256x128": 5,
-            "blockscale_128x128": 6}
+            "blockscale_128x128": 6, "ptpc_128x128": 7}
 
 
 def _shapes():
@@ -107,7 +107,8 @@ def test_mode_shapes_are_the_documented_loads():
     = 2 MB / waves A DMAs and NB = 2 NBW B fragment halves (+ 3 scale loads
     for mxfp8 and blockscale); the ptpc tiles add 2 epilogue-scale DMAs."""
     assert MODES == {"ptpc": (8, 8, 2), "blockscale": (2, 7, 0), "mxfp8": (8, 11, 0), "ptpc_128x256": (2, 4, 2),
-                     "ptpc_gathered": (8, 8, 2), "mxfp8_256x128": (8, 7, 0), "blockscale_128x128": (4, 7, 0)}
+                     "ptpc_gathered": (8, 8, 2), "mxfp8_256x128": (8, 7, 0), "blockscale_128x128": (4, 7, 0),
+                     "ptpc_128x128": (4, 4, 2)}
 
 
 def program(L, KI, ntiles, NA, NB, NSC, wait_fn=None):

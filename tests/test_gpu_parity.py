@@ -198,6 +198,36 @@ def test_quantizers_near_rounding_midpoints_bitexact(dmm):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
 
 
+def test_quantize_direct_range_exhaustive(dmm):
+    """Every fp32 value of magnitude in [2^-6, 448], both signs (247.5 M
+    values), quantised per token under a scale of exactly 1 (each row starts
+    with 448): the quotient is the value itself, so this runs the GPU
+    encoder's direct path (the hardware E4M3 conversion) over its whole input
+    range, and the division path at every midpoint window, against the
+    oracle's encoder, bitwise."""
+    lo, hi = 0x3C800000, 0x43E00000  # 2^-6 and 448
+    mags = np.arange(lo, hi + 1, dtype=np.uint32)
+    vals = np.concatenate([mags, mags | np.uint32(0x80000000)]).view(np.float32)
+    cols = (1 << 20) + 16
+    per_row = cols - 1
+    rows = -(-vals.size // per_row)
+    body = np.full(rows * per_row, np.float32(1.0))
+    body[: vals.size] = vals
+    x = np.empty((rows, cols), np.float32)
+    x[:, 0] = np.float32(448.0)
+    x[:, 1:] = body.reshape(rows, per_row)
+    assert np.array_equal(x[:, 1:].reshape(-1)[: vals.size].view(np.uint32), vals.view(np.uint32))
+    announce("quantize_per_token exhaustive direct range", x.shape)
+    del mags, vals, body
+    q, s = dmm.quantize_per_token(to_dev(x))
+    assert (s.cpu().numpy() == 1.0).all()
+    got = q.view(torch.uint8).cpu().numpy()
+    oq, os_ = oracle.quantize_per_token(x)
+    assert (os_ == 1.0).all()
+    bad = np.argwhere(got != oq)
+    assert bad.size == 0, (len(bad), [(float(x[r, c]), int(got[r, c]), int(oq[r, c])) for r, c in bad[:5]])
+
+
 def test_quantize_mxfp8_near_rounding_midpoints_bitexact(dmm):
     """mxfp8 scales by a power of two exactly, so values at E4M3 midpoints
     times the group's power of two are exact ties (round to even) and their

@@ -228,6 +228,36 @@ def test_quantize_direct_range_exhaustive(dmm):
     assert bad.size == 0, (len(bad), [(float(x[r, c]), int(got[r, c]), int(oq[r, c])) for r, c in bad[:5]])
 
 
+def test_quantize_mxfp8_direct_range_exhaustive(dmm):
+    """mxfp8 scales by 2^0 when a group's maximum is 448, so every other
+    value of the group reaches the hardware E4M3 conversion unchanged: every
+    fp32 value of magnitude in [2^-10, 448] (the E4M3 subnormal steps
+    included), both signs, plus every 4096th pattern below 2^-10 (fp32
+    subnormals included), against the oracle's encoder, bitwise."""
+    lo, hi = 0x3A800000, 0x43E00000  # 2^-10 and 448
+    mags = np.concatenate([np.arange(0, lo, 4096, dtype=np.uint32), np.arange(lo, hi + 1, dtype=np.uint32)])
+    vals = np.concatenate([mags, mags | np.uint32(0x80000000)]).view(np.float32)
+    k = 1 << 20
+    groups = -(-vals.size // 31)
+    body = np.full(groups * 31, np.float32(1.0))
+    body[: vals.size] = vals
+    g = np.empty((groups, 32), np.float32)
+    g[:, 0] = np.float32(448.0)
+    g[:, 1:] = body.reshape(groups, 31)
+    rows = -(-groups // (k // 32))
+    x = np.full((rows * (k // 32), 32), np.float32(448.0))
+    x[:groups] = g
+    x = x.reshape(rows, k)
+    announce("quantize_mxfp8 exhaustive direct range", x.shape)
+    del mags, vals, body, g
+    q, e = dmm.quantize_mxfp8(to_dev(x))
+    oq, oe = oracle.quantize_mxfp8(x)
+    assert (oe == 127).all() and np.array_equal(e.cpu().numpy(), oe)
+    got = q.view(torch.uint8).cpu().numpy()
+    bad = np.argwhere(got != oq)
+    assert bad.size == 0, (len(bad), [(float(x[r, c]), int(got[r, c]), int(oq[r, c])) for r, c in bad[:5]])
+
+
 def test_quantize_mxfp8_near_rounding_midpoints_bitexact(dmm):
     """mxfp8 scales by a power of two exactly, so values at E4M3 midpoints
     times the group's power of two are exact ties (round to even) and their

@@ -167,11 +167,15 @@ void orc_quantize_blockscale_b(const float* x, int64_t n, int64_t k, uint8_t* q,
 }
 
 /* Smallest power-of-two exponent e with amax / 2^e <= 448, i.e.
- * e = ceil(log2(amax / 448)), taken exactly from frexpf. */
+ * e = ceil(log2(amax / 448)), taken exactly from frexpf.  An infinite
+ * maximum has no such e: ceil(log2(inf)) is +inf, clamped like every other
+ * exponent to the format's largest, 127 (frexpf's exponent is unspecified
+ * for an infinite argument, so it is not consulted). */
 static int mx_exponent(float amax) {
     int ex, e;
     float r, fr;
     if (amax == 0.0f) return 0;
+    if (isinf(amax)) return 127;
     r = amax / 448.0f;
     fr = frexpf(r, &ex); /* r = fr * 2^ex, fr in [0.5, 1) */
     e = (fr == 0.5f) ? ex - 1 : ex;

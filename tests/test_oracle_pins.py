@@ -197,6 +197,25 @@ def test_quantize_blockscale_b_block_amax(orc, n):
             assert np.array_equal(q[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128], t_enc_e4m3((blk / sc).numpy()))
 
 
+def test_quantize_mxfp8_infinite_group_maximum(orc):
+    """An infinite group maximum has no exponent with amax / 2^e <= 448:
+    ceil(log2(inf)) clamps to 127; the infinity encodes as the largest
+    E4M3 magnitude (saturation), finite values under 2^-127 as zero, NaN as
+    0x7F; a group whose only non-zero is NaN has maximum 0 (fmax ignores
+    NaN) and exponent 0."""
+    x = np.ones((2, 64), np.float32)
+    x[0, 3] = np.inf
+    x[0, 4] = -2.0
+    x[1, 0:32] = 0.0
+    x[1, 7] = np.nan
+    q, e = orc.quantize_mxfp8(x)  # e[group, row]
+    assert e[0, 0] == 127 + 127  # row 0, group 0: the infinity
+    assert e[1, 0] == 127 - 8  # row 0, group 1: maximum 1
+    assert e[0, 1] == 127  # row 1, group 0: maximum 0 (only NaN)
+    assert q[0, 3] == 0x7E and q[0, 4] == 0x80 and q[0, 0] == 0x00
+    assert q[1, 7] == 0x7F and q[1, 0] == 0x00
+
+
 def test_quantize_mxfp8_exponent_and_codes(orc):
     x = inputs.normal((24, 512), 11)
     x[3, 32:64] = 0.0

@@ -209,7 +209,9 @@ __global__ void __launch_bounds__(256) quantize_blockscale_a_kernel(const float*
         const int c = base + lane;
         const bool valid = c < n4;  // false only for lanes 32-63 of a last half pass
         v4f v = valid ? xr[c] : (v4f){0.f, 0.f, 0.f, 0.f};
-        float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        // the maximum starts from 0 like the row and block maxima: fmax
+        // ignores NaN, so a group of NaN has maximum 0 (scale 1 / exponent 0)
+        float a = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))), 0.0f);
         const float s = amax_to_scale(group_max(a, 32));
         if (valid) {
             qr[c] = DivQuant(s).pack(v);
@@ -289,7 +291,9 @@ __global__ void __launch_bounds__(256) quantize_mxfp8_kernel(const float* __rest
         const int c = base + lane;
         const bool valid = c < n4;
         v4f v = valid ? xr[c] : (v4f){0.f, 0.f, 0.f, 0.f};
-        float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        // the maximum starts from 0 like the row and block maxima: fmax
+        // ignores NaN, so a group of NaN has maximum 0 (scale 1 / exponent 0)
+        float a = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))), 0.0f);
         const int e = mx_exp(group_max(a, 8));
         if (valid) {
             // scaling by 2^-e is exact (or one rounding into the subnormals)

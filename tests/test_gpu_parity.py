@@ -258,6 +258,34 @@ def test_quantize_mxfp8_direct_range_exhaustive(dmm):
     assert bad.size == 0, (len(bad), [(float(x[r, c]), int(got[r, c]), int(oq[r, c])) for r, c in bad[:5]])
 
 
+def test_quantizers_non_finite_inputs_bitexact(dmm):
+    """NaN and infinities in the input: every quantiser's maximum ignores
+    NaN (fmax), an infinite maximum gives an infinite fp32 scale (finite
+    values quantise to zero, infinities to NaN) or the largest E8M0
+    exponent; codes and scales match the oracle bitwise."""
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((256, 512)).astype(np.float32)
+    for r in range(0, 256, 3):
+        x[r, rng.integers(0, 512)] = np.nan
+    for r in range(1, 256, 5):
+        x[r, rng.integers(0, 512)] = np.inf
+    for r in range(2, 256, 7):
+        x[r, rng.integers(0, 512)] = -np.inf
+    x[4, 0:128] = np.nan  # a whole row block of NaN in one 128-wide block
+    x[5, 32:64] = 0.0
+    x[5, 40] = np.nan  # a group whose maximum is 0
+    announce("quantizers non-finite inputs", x.shape)
+    for name in ("quantize_per_token", "quantize_blockscale_a", "quantize_blockscale_b"):
+        q, s = getattr(dmm, name)(to_dev(x))
+        oq, os_ = getattr(oracle, name)(x)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32)), name
+        assert np.array_equal(q.view(torch.uint8).cpu().numpy(), oq), name
+    q, e = dmm.quantize_mxfp8(to_dev(x))
+    oq, oe = oracle.quantize_mxfp8(x)
+    assert np.array_equal(e.cpu().numpy(), oe)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), oq)
+
+
 def test_quantize_mxfp8_near_rounding_midpoints_bitexact(dmm):
     """mxfp8 scales by a power of two exactly, so values at E4M3 midpoints
     times the group's power of two are exact ties (round to even) and their

@@ -462,35 +462,38 @@ __device__ __forceinline__ void mfma_scaled_acc(v4f& acc, const v8i& b, const v8
                      : "v"(b), "v"(a), "v"(sb), "v"(sa), "n"(OA & 1), "n"(OB & 1), "n"(OA >> 1), "n"(OB >> 1));
 }
 
-// blockscale: acc[r] (+)= bp[r % 2] * sa(row, kt) * sb(block, kt).  The fp8
-// 16x16x128 matrix op has 8 passes, so a VALU read of its result needs 11
-// wait states, which the compiler cannot see across the asm statements.
-// Row block r's products are folded after row block r + 1's two matrix ops
-// and the 10 wait states of the s_nop pair: 12 whatever the compiler
-// schedules in between.  The last row block's come after the previous
-// fold (10 nops, 8 VALU) and its own 10 nops.
-template <int MODE, int T, int r, bool FIRST>
-__device__ __forceinline__ void fold_products(Ctx<MODE>& x) {
-    const float s = x.sfa[T][r / 4][r % 4] * x.sfb[T];
-    v4f& c0 = x.acc[r][0];
-    v4f& c1 = x.acc[r][1];
-    const v4f p0 = x.bp[r & 1][0], p1 = x.bp[r & 1][1];
-    if constexpr (FIRST) {
-        asm volatile(
-            "s_nop 7\n\ts_nop 1\n\t"
-            "v_mul_f32 %0, %8, %16\n\tv_mul_f32 %1, %9, %16\n\tv_mul_f32 %2, %10, %16\n\tv_mul_f32 %3, %11, %16\n\t"
-            "v_mul_f32 %4, %12, %16\n\tv_mul_f32 %5, %13, %16\n\tv_mul_f32 %6, %14, %16\n\tv_mul_f32 %7, %15, %16"
-            : "=&v"(c0[0]), "=&v"(c0[1]), "=&v"(c0[2]), "=&v"(c0[3]), "=&v"(c1[0]), "=&v"(c1[1]), "=&v"(c1[2]),
-              "=&v"(c1[3])
-            : "v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(p1[0]), "v"(p1[1]), "v"(p1[2]), "v"(p1[3]), "v"(s));
-    } else {
-        asm volatile(
-            "s_nop 7\n\ts_nop 1\n\t"
-            "v_fmac_f32 %0, %8, %16\n\tv_fmac_f32 %1, %9, %16\n\tv_fmac_f32 %2, %10, %16\n\tv_fmac_f32 %3, %11, %16\n\t"
-            "v_fmac_f32 %4, %12, %16\n\tv_fmac_f32 %5, %13, %16\n\tv_fmac_f32 %6, %14, %16\n\tv_fmac_f32 %7, %15, %16"
-            : "+v"(c0[0]), "+v"(c0[1]), "+v"(c0[2]), "+v"(c0[3]), "+v"(c1[0]), "+v"(c1[1]), "+v"(c1[2]), "+v"(c1[3])
-            : "v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(p1[0]), "v"(p1[1]), "v"(p1[2]), "v"(p1[3]), "v"(s));
-    }
+// blockscale: acc[r][nb] (+)= bp[r % 2][nb] * s, s = sa(row, kt) * sb(block,
+// kt).  The fp8 16x16x128 matrix op has 8 passes, so a VALU access to its
+// result needs 11 wait states, which the compiler cannot see across the asm
+// statements.  Column block nb of row block r is folded right after the
+// matrix op (r + 1, nb), so that the four additions sit between matrix ops;
+// PAD wait states of s_nop go in front, where the instructions counted
+// since the matrix op that wrote the products fall short of 11 (mfma_row).
+template <int PAD>
+__device__ __forceinline__ void pad_wait_states() {
+    static_assert(PAD >= 0 && PAD <= 16, "one or two s_nop");
+    if constexpr (PAD > 8) asm volatile("s_nop 7\n\ts_nop %0" ::"n"(PAD - 9));
+    else if constexpr (PAD > 0) asm volatile("s_nop %0" ::"n"(PAD - 1));
+}
+
+template <int MODE, int T, int r>
+__device__ __forceinline__ float fold_scale(const Ctx<MODE>& x) {
+    return x.sfa[T][r / 4][r % 4] * x.sfb[T];
+}
+
+template <int MODE, int r, int nb, bool FIRST, int PAD>
+__device__ __forceinline__ void fold_block(Ctx<MODE>& x, float s) {
+    v4f& c = x.acc[r][nb];
+    const v4f p = x.bp[r & 1][nb];
+    pad_wait_states<PAD>();
+    if constexpr (FIRST)
+        asm volatile("v_mul_f32 %0, %4, %8\n\tv_mul_f32 %1, %5, %8\n\tv_mul_f32 %2, %6, %8\n\tv_mul_f32 %3, %7, %8"
+                     : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3])
+                     : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(s));
+    else
+        asm volatile("v_fmac_f32 %0, %4, %8\n\tv_fmac_f32 %1, %5, %8\n\tv_fmac_f32 %2, %6, %8\n\tv_fmac_f32 %3, %7, %8"
+                     : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3])
+                     : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(s));
 }
 
 // Block (mb, nb) of a K tile, ptpc / mxfp8 (AGPR accumulators).
@@ -521,16 +524,30 @@ __device__ __forceinline__ void mfma_row(Ctx<MODE>& x, const v8i& a) {
         // blockscale: one fp32 scale per (row, 128-wide K tile) times the
         // B block's scale multiplies each K tile's products before they are
         // added to the VGPR accumulators.  The products of row block mb go
-        // to bp[mb % 2]; row block mb - 1's are scaled in behind them, so
-        // the matrix ops of one row block overlap the additions of the last.
+        // to bp[mb % 2]; column block nb of row block mb - 1 is scaled in
+        // right behind the matrix op (mb, nb), the last row block's after
+        // its own.  Wait states from the matrix op (r, nb) to the fold (r,
+        // nb), one per instruction in between plus the fold's own padding:
+        //   fold (0, 0): two matrix ops + 9 = 11;
+        //   fold (r, 0), r >= 1: fold (r-1, 0) (padding >= 1, four
+        //     additions), a matrix op, fold (r-1, 1) (4), a matrix op, + 1
+        //     = 12 or more;
+        //   fold (r, 1): fold (r-1, 1) (4; none for r = 0), a matrix op,
+        //     fold (r, 0) (1 + 4 or 9 + 4), a matrix op = 11 or more;
+        //   last row block: fold (7, 0) 5 + 1 + 4 + 1 = 11, fold (7, 1)
+        //     4 + 5 + 2 = 11.
+        // Anything the compiler puts in between only adds to these
+        // (tests/test_isa_hazards.py audits the emitted code).
         static_assert(Cfg<MODE>::NBW == 2, "two column blocks per wave");
-        asm volatile(
-            "v_mfma_f32_16x16x128_f8f6f4 %0, %2, %4, 0\n\t"
-            "v_mfma_f32_16x16x128_f8f6f4 %1, %3, %4, 0"
-            : "=&v"(x.bp[mb & 1][0]), "=&v"(x.bp[mb & 1][1])
-            : "v"(x.bq[T][0]), "v"(x.bq[T][1]), "v"(a));
-        if constexpr (mb > 0) fold_products<MODE, T, mb - 1, FIRST>(x);
-        if constexpr (mb == Cfg<MODE>::MB - 1) fold_products<MODE, T, mb, FIRST>(x);
+        constexpr int MB = Cfg<MODE>::MB;
+        asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=&v"(x.bp[mb & 1][0]) : "v"(x.bq[T][0]), "v"(a));
+        if constexpr (mb > 0) fold_block<MODE, mb - 1, 0, FIRST, mb == 1 ? 9 : 1>(x, fold_scale<MODE, T, mb - 1>(x));
+        asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=&v"(x.bp[mb & 1][1]) : "v"(x.bq[T][1]), "v"(a));
+        if constexpr (mb > 0) fold_block<MODE, mb - 1, 1, FIRST, 0>(x, fold_scale<MODE, T, mb - 1>(x));
+        if constexpr (mb == MB - 1) {
+            fold_block<MODE, mb, 0, FIRST, 1>(x, fold_scale<MODE, T, mb>(x));
+            fold_block<MODE, mb, 1, FIRST, 2>(x, fold_scale<MODE, T, mb>(x));
+        }
     }
 }
 
@@ -1247,10 +1264,10 @@ int mxfp8_tile_for(int m, int n) {
 }
 
 // blockscale: the 128 x 128 tile of four waves (one per SIMD, so no second
-// wave hides the fold's result latency) costs 0.64 of a 128 x 256 tile
-// (measured at 16384 x 7168 x 2048: 28 waves of the small tile 328 us, 14
-// waves of the wide one 256 us).
-constexpr double kBlockscaleHalfCost = 0.64;
+// wave fills the gaps of its instruction stream) costs 0.59 of a 128 x 256
+// tile (measured at 16384 x 7168 x 2048: 28 waves of the small tile 282 us,
+// 14 waves of the wide one 239 us).
+constexpr double kBlockscaleHalfCost = 0.59;
 int blockscale_tile_for(int m, int n) {
     const long wide = (long)((m + 127) / 128) * ((n + 255) / 256);
     const long half = (long)((m + 127) / 128) * ((n + 127) / 128);

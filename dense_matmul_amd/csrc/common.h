@@ -30,17 +30,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // Direct global -> LDS load of 16 bytes per lane through a buffer
-// descriptor: lane l writes lds + 16 l (lds must be wave-uniform).  The host
+// descriptor: lane l writes lds + 16 l (lds must be wave-uniform); the
+// address is the descriptor's base + voffset + soffset (soffset uniform).  The host
 // compilation pass cannot type-check this builtin inside device function
 // templates, so the call exists in the device pass only; the host pass never
 // executes device code.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_char* lds, int voffset) {
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_char* lds, int voffset, int soffset = 0) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voffset, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voffset, soffset, 0, 0);
 #else
     (void)r;
     (void)lds;
     (void)voffset;
+    (void)soffset;
 #endif
 }
 

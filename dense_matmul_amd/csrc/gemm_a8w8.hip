@@ -300,14 +300,30 @@ __device__ __forceinline__ TileRef Ctx<MODE>::ref(int j) {
     return TileRef{m0, n0, m0 * K, (n0 / 16) * KI * 2048};
 }
 
-// Descriptors over all of A or B, or empty for a tile past the list.
+// Descriptors over A (B) from a tile's first row (first column block) to the
+// end of the operand, or empty for a tile past the list.  Within the tile a
+// lane's offset (its row or fragment, loop-invariant) is the instruction's
+// VGPR offset and the K tile's the scalar offset, so no step spends vector
+// instructions on addresses.  The range check, on the VGPR part (the scalar
+// offset stays below K either way), still drops rows past M and column
+// blocks past N: their offsets reach past the shortened extent.
+// Blockscale keeps descriptors over the whole operand and adds the tile's
+// offset to the VGPR offset instead: its two waves per SIMD share the scalar
+// unit, where the per-step descriptor arithmetic cost it more than the
+// vector additions it saves (16384 x 7168 x 2048: 241.5 against 237.5 us;
+// ptpc and mxfp8 gain 1.3-2.4 %).
 template <int MODE>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t a_rsrc(const Ctx<MODE>& x, bool valid) {
-    return make_rsrc(x.a, valid ? (uint32_t)x.M * (uint32_t)x.K : 0u);
+constexpr bool kTileRsrc = !kBlock<MODE>;
+
+template <int MODE>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t a_rsrc(const Ctx<MODE>& x, int a_off, bool valid) {
+    const uint32_t o = kTileRsrc<MODE> ? (uint32_t)__builtin_amdgcn_readfirstlane(a_off) : 0u;
+    return make_rsrc(x.a + o, valid ? (uint32_t)x.M * (uint32_t)x.K - o : 0u);
 }
 template <int MODE>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t b_rsrc(const Ctx<MODE>& x, bool valid) {
-    return make_rsrc(x.b, valid ? (uint32_t)x.N * (uint32_t)x.K : 0u);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t b_rsrc(const Ctx<MODE>& x, int b_off, bool valid) {
+    const uint32_t o = kTileRsrc<MODE> ? (uint32_t)__builtin_amdgcn_readfirstlane(b_off) : 0u;
+    return make_rsrc(x.b + o, valid ? (uint32_t)x.N * (uint32_t)x.K - o : 0u);
 }
 
 // ---------------------------------------------------------------- issue
@@ -315,12 +331,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t b_rsrc(const Ctx<MODE>& x, boo
 // the per-K-tile scales of the mode.  A step spreads the fragment loads over
 // its first row blocks, one or two between consecutive groups of matrix ops.
 //
-// Fragment load Q (0..2 NBW-1): half Q % 2 of column block Q / 2; base = the
-// tile's B offset + 2048 kt for K tile kt.
+// Fragment load Q (0..2 NBW-1): half Q % 2 of column block Q / 2; b_off =
+// the tile's B offset (where rb starts, see b_rsrc), kbase = 2048 kt for K
+// tile kt.
 template <int MODE, int T, int Q>
-__device__ __forceinline__ void b_piece(Ctx<MODE>& x, __amdgpu_buffer_rsrc_t rb, int base) {
-    const int off = x.voff_b[Q / 2] + base + (Q % 2) * 1024;
-    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+__device__ __forceinline__ void b_piece(Ctx<MODE>& x, __amdgpu_buffer_rsrc_t rb, int b_off, int kbase) {
+    const int voff = x.voff_b[Q / 2] + (Q % 2) * 1024;
+    const v4i v = kTileRsrc<MODE>
+                      ? __builtin_amdgcn_raw_buffer_load_b128(rb, voff, __builtin_amdgcn_readfirstlane(kbase), 0)
+                      : __builtin_amdgcn_raw_buffer_load_b128(rb, voff + b_off + kbase, 0, 0);
     v8i& d = x.bq[T][Q / 2];
     constexpr int h = 4 * (Q % 2);
     d[h + 0] = v[0];
@@ -382,9 +401,8 @@ __device__ __forceinline__ void b_scales(Ctx<MODE>& x, TileRef r, int kt) {
 // A whole B event at once (the prologue's).
 template <int MODE, int T>
 __device__ __forceinline__ void issue_b(Ctx<MODE>& x, TileRef r, int kt) {
-    const __amdgpu_buffer_rsrc_t rb = b_rsrc(x, r.m0 >= 0);
-    const int base = r.b_off + kt * 2048;
-    static_for<0, 2 * Cfg<MODE>::NBW>([&](auto Qc) { b_piece<MODE, T, decltype(Qc)::value>(x, rb, base); });
+    const __amdgpu_buffer_rsrc_t rb = b_rsrc(x, r.b_off, r.m0 >= 0);
+    static_for<0, 2 * Cfg<MODE>::NBW>([&](auto Qc) { b_piece<MODE, T, decltype(Qc)::value>(x, rb, r.b_off, kt * 2048); });
     b_scales<MODE, T>(x, r, kt);
 }
 
@@ -406,18 +424,23 @@ __device__ __forceinline__ void issue_epilogue_scales(Ctx<MODE>& x, TileRef t) {
 }
 
 // Global -> LDS DMA of one A K tile: NA instructions per wave; instruction
-// j moves 1 KiB (8 rows x 128 bytes).  base = the tile's A offset + 128 kt
-// for K tile kt; rows past M fall outside the descriptor and read as zero.
+// j moves 1 KiB (8 rows x 128 bytes).  a_off = the tile's A offset (where ra
+// starts, see a_rsrc), kbase = 128 kt for K tile kt; rows past M fall
+// outside the descriptor and read as zero.
 template <int MODE>
-__device__ __forceinline__ void a_piece(Ctx<MODE>& x, lds_char* stage, __amdgpu_buffer_rsrc_t ra, int base, int j) {
-    lds_dma16(ra, stage + x.dma_lds + j * 1024, x.voff_a[j] + base);
+__device__ __forceinline__ void a_piece(Ctx<MODE>& x, lds_char* stage, __amdgpu_buffer_rsrc_t ra, int a_off, int kbase,
+                                        int j) {
+    if constexpr (kTileRsrc<MODE>)
+        lds_dma16(ra, stage + x.dma_lds + j * 1024, x.voff_a[j], __builtin_amdgcn_readfirstlane(kbase));
+    else
+        lds_dma16(ra, stage + x.dma_lds + j * 1024, x.voff_a[j] + a_off + kbase);
 }
 
 template <int MODE>
 __device__ __forceinline__ void issue_a(Ctx<MODE>& x, lds_char* stage, TileRef r, int kt) {
-    const __amdgpu_buffer_rsrc_t ra = a_rsrc(x, r.m0 >= 0);
+    const __amdgpu_buffer_rsrc_t ra = a_rsrc(x, r.a_off, r.m0 >= 0);
 #pragma unroll
-    for (int j = 0; j < Cfg<MODE>::NA; ++j) a_piece<MODE>(x, stage, ra, r.a_off + kt * BK, j);
+    for (int j = 0; j < Cfg<MODE>::NA; ++j) a_piece<MODE>(x, stage, ra, r.a_off, kt * BK, j);
 }
 
 template <int MODE, int S>
@@ -841,7 +864,8 @@ struct Ring {
 // step s+3 (K tile k+3 of this tile or of one of the next two).
 struct StepLoads {
     __amdgpu_buffer_rsrc_t rb, ra;
-    int bbase, abase;  // byte offsets of the B event's and the A DMA's K tile
+    int bbase, abase;  // K-tile byte offsets of the B event and the A DMA within their tiles
+    int boff, aoff;    // their tiles' B and A offsets
     int bkt;           // K tile of the B event (for the mode's scales)
     TileRef bref;
     TileRef enext;     // the next tile, whose epilogue scales a tile's last step loads
@@ -921,8 +945,8 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, TileRef cur, StepLoads L
         constexpr int nxt = mb + 2;
         if constexpr (mb < HALF) {
             if constexpr (mb % BSTRIDE == 0) {
-                b_piece<MODE, T ^ 1, mb / BSTRIDE * BPR>(x, L.rb, L.bbase);
-                if constexpr (BPR == 2) b_piece<MODE, T ^ 1, mb * BPR + 1>(x, L.rb, L.bbase);
+                b_piece<MODE, T ^ 1, mb / BSTRIDE * BPR>(x, L.rb, L.boff, L.bbase);
+                if constexpr (BPR == 2) b_piece<MODE, T ^ 1, mb * BPR + 1>(x, L.rb, L.boff, L.bbase);
             }
             if constexpr (mb == HALF - 1) {
                 b_scales<MODE, T ^ 1>(x, L.bref, L.bkt);
@@ -941,7 +965,7 @@ __device__ __forceinline__ void step_rows(Ctx<MODE>& x, TileRef cur, StepLoads L
         static_assert(C::NA <= HALF && HALF % C::NA == 0, "A DMAs spread evenly over the second half");
         constexpr int DSTRIDE = HALF / C::NA;
         if constexpr (mb >= HALF && (mb - HALF) % DSTRIDE == 0)
-            a_piece<MODE>(x, x.lds.p[SR], L.ra, L.abase, (mb - HALF) / DSTRIDE);
+            a_piece<MODE>(x, x.lds.p[SR], L.ra, L.aoff, L.abase, (mb - HALF) / DSTRIDE);
         if constexpr (nxt < C::MB) {
             v8i fr = read_a<MODE, S>(x, nxt);
             if constexpr (nxt % 3 == 0) f0 = fr;
@@ -1001,8 +1025,9 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRe
     // B event of stream step s+1: the next K tile, or the next tile's first
     L.bref = LAST ? g.t1 : g.t0;
     L.bkt = LAST ? 0 : k + 1;
-    L.rb = b_rsrc(x, L.bref.m0 >= 0);
-    L.bbase = L.bref.b_off + L.bkt * 2048;
+    L.rb = b_rsrc(x, L.bref.b_off, L.bref.m0 >= 0);
+    L.boff = L.bref.b_off;
+    L.bbase = L.bkt * 2048;
     L.enext = g.t1;
     // A DMA of stream step s+3: K tile k+3 of this tile or of one of the next
     // two (selected without branches) -- or, when K = 128 (every step both
@@ -1028,8 +1053,9 @@ __device__ __forceinline__ void kstep(Ctx<MODE>& x, int s, int k, Ring g, TileRe
         a_m0 = in0 ? g.t0.m0 : a_m0;
         akt = in0 ? kk : akt;
     }
-    L.ra = a_rsrc(x, a_m0 >= 0);
-    L.abase = a_off + akt * BK;
+    L.ra = a_rsrc(x, a_off, a_m0 >= 0);
+    L.aoff = a_off;
+    L.abase = akt * BK;
     if constexpr (EPM == 1) x.ep = epi_begin<MODE>(x, prev.m0, prev.n0);
     // the tile's scales leave LDS before this step's wait lets the next
     // tile's scale DMAs in (the narrow tile stores at the end of the step)

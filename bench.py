@@ -260,15 +260,26 @@ def copy_calibration(torch):
 KERNEL_SOURCES = ("gemm_a8w8.hip", "common.h", "kpipe.h", "lds_layout.h", "tile_order.h", "b_layout.h")
 
 
+def code_text(src):
+    """C++ source text without its comments and blank space: what a compiler
+    sees, so that editing a comment does not make a profile stale."""
+    import re
+
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash():
-    """sha256 over the fp8 GEMM kernel's source files, to tell whether a
-    counter summary was taken for the kernel as it is now."""
+    """sha256 over the fp8 GEMM kernel's source files (code_text of each),
+    to tell whether a counter summary was taken for the kernel as it is
+    now."""
     import hashlib
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "dense_matmul_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "dense_matmul_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -197,10 +197,11 @@ constexpr bool kAgprAcc = kDeferEpilogue<MODE> || MODE == MODE_MXFP8_N;
 // order::round_list with the gathered order).
 
 // One output tile of a workgroup's list: its origin and the byte offsets of
-// its A rows and preshuffled B blocks.  Loads go through descriptors over the
-// whole of A or B, so rows past M and column blocks past N fall outside them
-// and read as zero.  Past the end of the list m0 = -1: the descriptors of
-// such loads are empty, so they move no data but still count in vmcnt.
+// its A rows and preshuffled B blocks.  Loads go through descriptors that
+// end where A or B ends (a_rsrc, b_rsrc), so rows past M and column blocks
+// past N fall outside them and read as zero.  Past the end of the list m0 =
+// -1: the descriptors of such loads are empty, so they move no data but
+// still count in vmcnt.
 struct TileRef {
     int m0, n0;
     int a_off, b_off;

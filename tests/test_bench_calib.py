@@ -115,3 +115,17 @@ def test_memory_rate_kernel_writes_its_region_and_reports_rates(L):
         per_cu, tbs = bench.memory_rate(torch, buf[: cus * region], region, kind, iters=16, launches=2)
         print("[stats]", kind, per_cu, tbs, flush=True)
         assert 0.5 < per_cu < 64.0 and 0.05 < tbs < 40.0, (kind, per_cu, tbs)
+
+
+def test_code_text_drops_comments_and_blank_space_only():
+    src = "int a = 1; // the count\n/* a block\n   comment */\tint  b = a /2;\n"
+    assert bench.code_text(src) == "int a = 1; int b = a /2;"
+    assert bench.code_text("x = y;") != bench.code_text("x = z;")
+
+
+def test_committed_traffic_profile_is_for_the_current_kernel():
+    # the bench reports roofline.traffic only from a counter summary taken on
+    # the GEMM sources as they are; a kernel change needs new counter runs
+    traffic = bench.traffic_from_profiles("gemm_a8w8_ptpc")
+    assert traffic is not None, "profiles/gemm_a8w8_ptpc_traffic.json was taken on other kernel sources"
+    assert 5e8 < traffic < 5e9

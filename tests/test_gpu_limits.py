@@ -1,4 +1,4 @@
-"""The fp8 GEMMs at the operand-size limits of the C ABI.
+"""The GEMMs at the operand-size limits of the C ABI.
 
 Operands are addressed with 32-bit buffer offsets, so the C ABI takes A, B
 and C up to 2^31 bytes each, with a margin of 256 rows (the rows a last tile
@@ -7,9 +7,11 @@ may reach past M or N).  Each test drives one operand to that limit:
 * A: M = 299337, N = 16, K = 7168 (A 2.146 GB), every tile of every mode;
 * B: M = 1, N = 4177968, K = 512 (B 2.139 GB, and its preshuffled copy),
   ptpc on its three tiles and mxfp8 on its two;
-* C: M = 149540, N = 7168, K = 128 (C 2.144 GB), every tile of every mode.
+* C: M = 149540, N = 7168, K = 128 (C 2.144 GB), every tile of every mode;
+* and the bf16 GEMM's three limits (A 1048319 x 1024, B 1048304 x 1024, C
+  149540 x 7168), both tiles.
 
-The data sit in the exact regime (codes of 0, +-0.5, +-1, +-2 and power-of-two
+The data sit in the exact regime (values 0, +-0.5, +-1, +-2 and power-of-two
 scales), where every sum is exact in fp32, so the GPU must equal the oracle
 bit for bit.  The large operand is drawn on the device by torch's seeded
 generator; the oracle gets the sampled rows (or 128-column blocks) copied
@@ -169,4 +171,67 @@ def test_c_at_the_limit(dmm, mode):
         c = run_poisoned(dmm, mode, tile, a, b_shuf, s_a, s_b, m, n)
         assert_bitwise(bits(c[torch.from_numpy(rows).to(DEV)]), ref, f"C limit {mode} {tile}")
         del c
+    torch.cuda.empty_cache()
+
+
+# bf16 bit patterns of 0.5, 1 and 2 (0x3F00, 0x3F80, 0x4000), sign in bit 15
+def test_bf16_patterns_are_the_exact_values():
+    h = np.array([0x3F00, 0x3F80, 0x4000, 0xBF00, 0xBF80, 0xC000, 0], np.uint16)
+    assert oracle.bf16_to_f32(h).tolist() == [0.5, 1.0, 2.0, -0.5, -1.0, -2.0, 0.0]
+
+
+def exact_bf16_device(shape, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    r = torch.randint(0, 4, shape, generator=g, device=DEV, dtype=torch.int16)
+    s = torch.randint(0, 2, shape, generator=g, device=DEV, dtype=torch.int16)
+    h = torch.where(r > 0, r * 0x80 + 0x3E80, torch.zeros_like(r))
+    del r
+    return (h | (s << 15)).view(torch.bfloat16)
+
+
+def exact_bf16_host(shape, seed):
+    return inputs.choice(shape, np.array([0x3F00, 0x3F80, 0x4000, 0xBF00, 0xBF80, 0xC000, 0], np.uint16), seed)
+
+
+@pytest.mark.parametrize("which", ["A", "B", "C"])
+def test_bf16_at_the_limit(dmm, which):
+    m, n, k = {"A": (1048319, 16, 1024), "B": (1, 1048304, 1024), "C": (149540, 7168, 64)}[which]
+    assert n % 16 == 0 and k % 64 == 0
+    assert (m + 256) * k * 2 < LIMIT and (n + 256) * k * 2 < LIMIT and (m + 256) * n * 2 < LIMIT
+    print(f"[case] limits bf16 {which} {m}x{n}x{k}", flush=True)
+    dev = lambda h: torch.from_numpy(h.view(np.int16)).to(DEV).view(torch.bfloat16)
+    host = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if which == "A":
+        a, qb = exact_bf16_device((m, k), 731), exact_bf16_host((n, k), 732)
+        b = dev(qb)
+        rows = inputs.rows_sample(m, seed=733)
+        ref = oracle.gemm_bf16(host(a[torch.from_numpy(rows).to(DEV)]), qb)
+        pick = lambda c: c[torch.from_numpy(rows).to(DEV)]
+    elif which == "B":
+        qa, b = exact_bf16_host((m, k), 741), exact_bf16_device((n, k), 742)
+        a = dev(qa)
+        cols = np.unique(np.concatenate([np.arange(256), np.arange(n - 256, n),
+                                         np.random.default_rng(743).integers(0, n, 2048)]))
+        ref = oracle.gemm_bf16(qa, host(b[torch.from_numpy(cols).to(DEV)]))
+        pick = lambda c: c[:, torch.from_numpy(cols).to(DEV)]
+    else:
+        qa, qb = exact_bf16_host((m, k), 751), exact_bf16_host((n, k), 752)
+        a, b = dev(qa), dev(qb)
+        rows = inputs.rows_sample(m, seed=753)
+        ref = oracle.gemm_bf16(qa, qb, rows=rows)
+        pick = lambda c: c[torch.from_numpy(rows).to(DEV)]
+    for tile in ("128x128", "64x64"):
+        buf = torch.empty(m * n + 2048, dtype=torch.bfloat16, device=DEV)
+        c = buf[: m * n].view(m, n)
+        canary = buf[m * n:].view(torch.int16)
+        buf.fill_(float("nan"))
+        canary.fill_(0x5A5A)
+        dmm.gemm_bf16(a, b, out=c, tile=tile)
+        torch.cuda.synchronize()
+        assert not torch.isnan(c).any().item(), f"bf16 {which} {tile}: unwritten elements"
+        assert bool((canary == 0x5A5A).all().item()), f"bf16 {which} {tile}: write past the end of C"
+        assert_bitwise(host(pick(c).contiguous()), ref, f"bf16 {which} limit {tile}")
+        del buf, c, canary
+    del a, b
     torch.cuda.empty_cache()

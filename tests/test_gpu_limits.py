@@ -235,3 +235,49 @@ def test_bf16_at_the_limit(dmm, which):
         del buf, c, canary
     del a, b
     torch.cuda.empty_cache()
+
+
+# The quantisers index rows with 64-bit offsets: a per-token, blockscale or
+# mxfp8 input of 300000 x 7168 fp32 (2.15e9 values, 8.6 GB, past 2^31 values)
+# and a blockscale B of 4177968 x 512 (a partial last 128-row block), N(0,1)
+# from torch's seeded generator; sampled rows (whole 128-row blocks for B)
+# against the oracle's quantisers, codes and scales bitwise.
+@pytest.mark.parametrize("kind", ["per_token", "per_token_bf16", "blockscale_a", "mxfp8", "blockscale_b"])
+def test_quantisers_past_2_31_values(dmm, kind):
+    m, k = (4177968, 512) if kind == "blockscale_b" else (300000, 7168)
+    print(f"[case] limits quantiser {kind} {m}x{k}", flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(771)
+    x = torch.randn((m, k), generator=g, device=DEV, dtype=torch.float32)
+    if kind == "per_token_bf16":
+        x = x.to(torch.bfloat16)
+    fn = {"per_token": dmm.quantize_per_token, "per_token_bf16": dmm.quantize_per_token,
+          "blockscale_a": dmm.quantize_blockscale_a, "mxfp8": dmm.quantize_mxfp8,
+          "blockscale_b": dmm.quantize_blockscale_b}[kind]
+    q, s = fn(x)
+    torch.cuda.synchronize()
+    if kind == "blockscale_b":
+        nblk = (m + 127) // 128
+        blocks = sorted({0, nblk - 2, nblk - 1, *np.random.default_rng(772).integers(0, nblk, 8).tolist()})
+        rows = np.concatenate([np.arange(128 * j, min(m, 128 * j + 128)) for j in blocks])
+    else:
+        rows = inputs.rows_sample(m, seed=772)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    xr = x[rows_t].float().cpu().numpy()
+    got_q = q.view(torch.uint8)[rows_t].cpu().numpy()
+    if kind.startswith("per_token"):
+        ref_q, ref_s = oracle.quantize_per_token(xr)
+        got_s = s[rows_t].cpu().numpy()
+    elif kind == "blockscale_a":
+        ref_q, ref_s = oracle.quantize_blockscale_a(xr)
+        got_s = s[:, rows_t].cpu().numpy()
+    elif kind == "mxfp8":
+        ref_q, ref_s = oracle.quantize_mxfp8(xr)
+        got_s = s[:, rows_t].cpu().numpy()
+    else:
+        ref_q, ref_s = oracle.quantize_blockscale_b(xr)
+        got_s = s[torch.tensor(blocks, device=DEV)].cpu().numpy()
+    assert_bitwise(got_q, ref_q, f"quantiser {kind} codes")
+    assert np.array_equal(got_s.view(np.uint8), np.ascontiguousarray(ref_s).view(np.uint8)), f"{kind}: scales differ"
+    del x, q, s
+    torch.cuda.empty_cache()

@@ -718,7 +718,7 @@ def extra_shapes(dmm, torch, args):
     t = timed_arms({"bf16": lambda: dmm.gemm_bf16(a, b, out=out)}, 200, 20, warm_s)
     ms = t["bf16"]["median"]
     tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
-    res["bf16_4096x1024x896"] = {"us": round(ms * 1e3, 2), "min_us": round(t["bf16"]["min"] * 1e3, 2),
+    res["bf16_4096x896x1024"] = {"us": round(ms * 1e3, 2), "min_us": round(t["bf16"]["min"] * 1e3, 2),
                                  "TFLOP/s": round(tf, 1), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1),
                                  "alg_GB/s": round((2 * (m * k + n * k + m * n)) / (ms * 1e-3) / 1e9)}
     return res
